@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Benchmark of the W3G128 fused GEMV on one MI355X.
+
+Default workload: the gate_proj shape of a Llama-3.1-70B decoder layer,
+W [28672, 8192] stored as int32 [28672, 768] + bf16 scales [28672, 64], one bf16
+activation row (batch 1), fp32 output.  One step = one qgemv_w3g128 call, the
+whole batch-1 hot path (weight stream, scale fetch, activation staging,
+decode, multiply-accumulate, reduction, store) in a single kernel.
+
+Inputs are seeded synthetic tensors (`synth`), resident in device memory
+before timing starts.  Weight/scale copies are rotated so the bytes of all
+copies exceed twice the 256 MB Infinity Cache; each step reads a copy that
+is not cache resident.  Steps are timed with HIP events recorded on the stream
+the kernels are launched on.
+
+Prints ONE JSON line on stdout.  `--extra` also measures the other workloads
+(the full layer at batch 1, batched decode M = 4..32, prefill M = 512) and
+prints them as JSON lines on stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 matrix peak, published
+MALL_BYTES = 256 * 2 ** 20
+METRIC = "W3G128 GEMV effective HBM GB/s and % of peak (70B layer shapes, B=1)"
+KERNEL_SRC = os.path.join(ROOT, "dequant_gemv_qgemv_amd", "csrc", "qw3.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qgemv_gate_proj_traffic.json")
+
+
+def gemv_bytes(n: int, k: int, m: int = 1) -> int:
+    """Algorithmic bytes: packed words + scales + activations + fp32 outputs."""
+    return n * (3 * k // 32) * 4 + n * (k // 128) * 2 + m * k * 2 + m * n * 4
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or None
+    when the kernel source changed since those counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+class Rotation:
+    """Copies of one weight tensor pair, enough to exceed 2x the MALL."""
+
+    def __init__(self, torch, packed, scales, min_copies=2):
+        per = packed.numel() * 4 + scales.numel() * 2
+        copies = max(min_copies, -(-2 * MALL_BYTES // per) + 1)
+        self.items = [(packed.clone(), scales.clone()) for _ in range(copies)]
+        self.copies = copies
+
+    def __getitem__(self, i):
+        return self.items[i % self.copies]
+
+
+def time_steps(torch, fn, steps: int, warmup: int):
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        fn(i)
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps  # ms per step
+
+
+def make_weight(torch, q, name):
+    import synth
+    c, s = synth.layer_weights(name)
+    codes = torch.from_numpy(c).cuda()
+    packed = q.qpack_uint3(codes)
+    del codes
+    scales = torch.from_numpy(s.view(np.int16)).cuda()
+    return c, s, packed, scales
+
+
+def cpu_baseline(c, s, x, k, budget_s=2.5):
+    """The oracle as it stands, on the host cores, over a bounded row sample."""
+    import oracle
+    rows = np.arange(0, c.shape[0], 4, dtype=np.int64)
+    words = oracle.pack(c[rows])
+    sc = np.ascontiguousarray(s[rows])
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.gemm(x, words, sc, k)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= budget_s:
+            break
+    nbytes = gemv_bytes(rows.size, k, x.shape[0]) * reps
+    return {
+        "value": round(nbytes / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": "oracle fp64 GEMV over every 4th row of gate_proj (%d of %d rows, K=%d), "
+                  "%d repetitions in %.2f s" % (rows.size, c.shape[0], k, reps, dt),
+    }
+
+
+def bench_extra(torch, q, steps, warmup, x_cache):
+    """Full layer at B=1, batched decode, prefill: JSON lines on stderr."""
+    import synth
+    out = []
+    layer = {}
+    total_bytes, total_ms = 0, 0.0
+    for name in ("q_proj", "k_proj", "v_proj", "o_proj", "gate_proj", "up_proj", "down_proj"):
+        c, s, packed, scales = make_weight(torch, q, name)
+        n, k = c.shape
+        rot = Rotation(torch, packed, scales)
+        xd = torch.from_numpy(synth.layer_x(1, k).reshape(-1).view(np.int16)).cuda()
+        y = torch.empty(n, dtype=torch.float32, device="cuda")
+        ms = time_steps(torch, lambda i: q.qgemv_w3g128(xd, rot[i][0], rot[i][1], out=y), steps, warmup)
+        b = gemv_bytes(n, k)
+        layer[name] = {"us": round(ms * 1e3, 3), "GB/s": round(b / ms / 1e6, 1), "bytes": b}
+        total_bytes += b
+        total_ms += ms
+        if name in ("gate_proj", "down_proj"):
+            for m in (4, 8, 16, 32, 512):
+                xm = torch.from_numpy(synth.layer_x(m, k).view(np.int16)).cuda()
+                ym = torch.empty((m, n), dtype=torch.float32, device="cuda")
+                st = max(10, steps // (8 if m == 512 else 2))
+                ms_m = time_steps(torch, lambda i: q.qgemm_w3g128_smallM(xm, rot[i][0], rot[i][1], out=ym),
+                                  st, max(2, warmup // 4))
+                bm = gemv_bytes(n, k, m)
+                rec = {"workload": "%s M=%d" % (name, m), "us": round(ms_m * 1e3, 3),
+                       "GB/s": round(bm / ms_m / 1e6, 1), "HBM_frac": round(bm / ms_m / 1e6 / HBM_PEAK_GBS, 4),
+                       "TFLOP/s": round(2.0 * m * n * k / ms_m / 1e9, 2)}
+                rec["MFMA_frac"] = round(rec["TFLOP/s"] / BF16_MFMA_PEAK_TFLOPS, 4)
+                out.append(rec)
+        del rot, packed, scales
+        torch.cuda.empty_cache()
+    out.insert(0, {"workload": "70B decoder layer, 7 projections back to back, B=1",
+                   "per_projection": layer, "layer_us_sum": round(total_ms * 1e3, 3),
+                   "layer_GB/s": round(total_bytes / total_ms / 1e6, 1),
+                   "layer_HBM_frac": round(total_bytes / total_ms / 1e6 / HBM_PEAK_GBS, 4)})
+    for rec in out:
+        print(json.dumps(rec), file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--extra", action="store_true", help="also time layer / batched / prefill workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import dequant_gemv_qgemv_amd as q
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    n, k = synth.LAYER_70B["gate_proj"][:2]
+    c, s, packed, scales = make_weight(torch, q, "gate_proj")
+    x = synth.layer_x(1, k)
+    xd = torch.from_numpy(x.reshape(-1).view(np.int16)).cuda()
+    rot = Rotation(torch, packed, scales)
+    y = torch.empty(n, dtype=torch.float32, device="cuda")
+
+    ms = time_steps(torch, lambda i: q.qgemv_w3g128(xd, rot[i][0], rot[i][1], out=y), args.steps, args.warmup)
+    nbytes = gemv_bytes(n, k)
+    gbs = nbytes / ms / 1e6
+    line = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16xf16->f32",
+        "data": "synthetic",
+        "config": {"workload": "gate_proj W3G128 GEMV, W [28672, 8192] -> int32 [28672, 768] + bf16 "
+                               "[28672, 64], x bf16 [1, 8192], y fp32 [28672]",
+                   "N": n, "K": k, "M": 1, "bytes_per_step": nbytes,
+                   "weight_copies_rotated": rot.copies, "us_per_step": round(ms * 1e3, 3)},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic()},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(c, s, x, k)
+    if args.extra:
+        del rot, packed, scales
+        torch.cuda.empty_cache()
+        bench_extra(torch, q, max(50, args.steps // 4), max(10, args.warmup // 4), None)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,123 @@
+/*
+ * qw3.h -- C ABI of the W3G128 fused dequantize-and-multiply library (gfx950).
+ *
+ * W3G128 is the weight format of the GSQ model card
+ * "Llama-3.1-70B-Instruct-3Bit-GSQ" (sections "Quantization details" and
+ * "Storage layout"): a Linear layer with original weight [N = out_features,
+ * K = in_features] is stored as
+ *   packed  int32 [N, 3K/32]   exact-width 3-bit codes, no padding
+ *   scales  bf16  [N, K/128]   one scale per group of 128 inputs
+ * with a symmetric integer codebook times the group scale and no zero point.
+ * This library reads it as follows (readings of points the card leaves open):
+ *   - each row is one little-endian bitstream: code k of row n occupies stream
+ *     bits 3k (least significant) to 3k+2, and stream bit j is bit (j mod 32)
+ *     of word (j div 32) of that row; the int32 container is read as raw bits;
+ *   - code c in 0..7 stands for the integer q = c - 4, so the weight is
+ *     w[n][k] = scales[n][k / 128] * (c[n][k] - 4).
+ * The fused operation is Y = X * dequant(W)^T (GLQ README, section
+ * "Inference kernels"), computed without ever writing the dense weight.
+ *
+ * Conventions shared by every entry point:
+ *   - All array pointers are DEVICE pointers owned by the caller; the library
+ *     never frees them.  Arrays are row-major and contiguous.
+ *   - bf16 values are passed as their raw 16-bit patterns (uint16_t).
+ *   - Work is enqueued on `hip_stream` (a hipStream_t; NULL means the default
+ *     stream) and returns without waiting for it; outputs are overwritten,
+ *     never accumulated into.
+ *   - Arguments are validated on the host before anything is enqueued; an
+ *     error status means nothing was launched and no output was touched.
+ *     QW3_ERR_HIP means the HIP runtime refused a launch or an allocation
+ *     (the message of the last HIP error is kept by qw3_last_hip_error()).
+ *   - Shapes: 0 <= N, 0 <= M, 0 <= K <= QW3_MAX_K and K % 128 == 0.  A size
+ *     of zero is valid and enqueues no work (for K == 0 the outputs of the
+ *     products are filled with zeros, the value of an empty sum).
+ *   - Alignment: `codes`, `packed`, `x` and `w_out` must be 16-byte aligned,
+ *     `scales` 2-byte and `y` 4-byte aligned, else QW3_ERR_ALIGN.
+ *   - Each call is deterministic: the same inputs give bit-identical outputs
+ *     on every run (all reductions run in a fixed order, no atomics).
+ *   - Inputs must be finite; NaN or Inf in x or scales give unspecified y.
+ */
+#ifndef QW3_H
+#define QW3_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int qw3_status;
+
+enum {
+    QW3_OK = 0,
+    QW3_ERR_NULL = -1,  /* a required pointer is NULL                        */
+    QW3_ERR_SHAPE = -2, /* negative size, K % 128 != 0, or K > QW3_MAX_K      */
+    QW3_ERR_ALIGN = -3, /* a pointer is not aligned as stated above           */
+    QW3_ERR_HIP = -4    /* the HIP runtime reported an error                  */
+};
+
+/* Largest supported in_features (1024 groups of 128). */
+#define QW3_MAX_K 131072
+
+/*
+ * qpack_uint3 -- pack 3-bit codes into the exact-width int32 stream.
+ *   codes  [N, K] uint8, values 0..7 (only the low 3 bits of each byte are
+ *          used; larger values are a caller error)
+ *   packed [N, 3K/32] int32, written
+ * Storage layout of the GSQ model card ("exact-width packing -- no sub-byte
+ * values are padded", [28672, 8192] -> [28672, 768]).
+ */
+qw3_status qpack_uint3(const uint8_t *codes, int32_t *packed, int64_t N, int64_t K,
+                       void *hip_stream);
+
+/*
+ * qdequant_bf16 -- expand packed codes into a dense bf16 weight.
+ *   packed [N, 3K/32] int32, scales [N, K/128] bf16
+ *   w_out  [N, K] bf16, written: w_out[n][k] = RNE_bf16(scales[n][k/128] * (c - 4))
+ * The product is exact in fp32 and rounded once to bf16, nearest-even.  This
+ * is the dense "dequantize then matmul" branch of the GLQ README ("How it
+ * works": CPU and fallback paths dequantize instead of fusing).
+ */
+qw3_status qdequant_bf16(const int32_t *packed, const uint16_t *scales, uint16_t *w_out,
+                         int64_t N, int64_t K, void *hip_stream);
+
+/*
+ * qgemv_w3g128 -- fused batch-1 product y = dequant(W) x.
+ *   x [K] bf16, packed [N, 3K/32] int32, scales [N, K/128] bf16
+ *   y [N] float32, written: y[n] = sum_k x[k] * scales[n][k/128] * (c[n][k] - 4)
+ * The packed weights are streamed from memory once; the dense weight is never
+ * formed (GLQ README, "Inference kernels").  fp32 accumulation; the result is
+ * within 1e-4 * sum_k |x[k] w[n][k]| + 1e-6 of the exact sum.
+ */
+qw3_status qgemv_w3g128(const uint16_t *x, const int32_t *packed, const uint16_t *scales,
+                        float *y, int64_t N, int64_t K, void *hip_stream);
+
+/*
+ * qgemm_w3g128_smallM -- fused product for M activation rows, Y = X dequant(W)^T.
+ *   x [M, K] bf16 (row stride K), packed [N, 3K/32] int32, scales [N, K/128] bf16
+ *   y [M, N] float32, written: y[m][n] = sum_k x[m][k] * scales[n][k/128] * (c[n][k] - 4)
+ * Any M >= 0 is accepted.  M == 1 runs the batch-1 kernel; small M streams
+ * the weights once for the whole batch through bf16-exact fp16 matrix-core
+ * products; large M (prefill) runs a tiled matrix-core kernel.  For M > 1 the
+ * call borrows a temporary device buffer of about 2*M*K + M*K/128 bytes from
+ * the stream-ordered allocator of `hip_stream` and releases it on the same
+ * stream.  Same accuracy bound as qgemv_w3g128.
+ */
+qw3_status qgemm_w3g128_smallM(const uint16_t *x, const int32_t *packed,
+                               const uint16_t *scales, float *y, int64_t M, int64_t N,
+                               int64_t K, void *hip_stream);
+
+/* Text for a status code (static storage, never NULL). */
+const char *qstatus_str(qw3_status status);
+
+/* Text of the last HIP error seen by this library in the calling thread. */
+const char *qw3_last_hip_error(void);
+
+/* ABI version of this header (increments on incompatible change). */
+int qw3_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QW3_H */

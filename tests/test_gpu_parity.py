@@ -1,0 +1,320 @@
+"""GPU parity of the HIP library against the CPU oracle, through the C ABI.
+
+Packing and dequantization must match the oracle bit for bit.  Products must
+satisfy |y_gpu - y_ref| <= 1e-4 * a + 1e-6 per element, where y_ref is the
+oracle's fp64 sum with exact products and a = sum_k |x_k w_k| (the tolerance
+the workload statement fixes).  Inputs come from `synth` (seeded); the oracle
+packs its own copy of the codes, so the two sides share only the raw draws.
+"""
+import functools
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+RTOL = 1e-4
+ATOL = 1e-6
+
+
+def q():
+    import dequant_gemv_qgemv_amd as mod
+    return mod
+
+
+def say(*args):
+    print("[gpu-case]", *args, file=sys.stderr, flush=True)
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    if a.dtype == np.uint32:
+        a = a.view(np.int32)
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    torch.cuda.synchronize()
+    if t.dtype == torch.bfloat16:
+        t = t.view(torch.int16)
+    return t.cpu().numpy()
+
+
+def assert_close(y_gpu, y_ref, a, what=""):
+    y_gpu = np.asarray(y_gpu, dtype=np.float64)
+    assert y_gpu.shape == y_ref.shape, (y_gpu.shape, y_ref.shape)
+    err = np.abs(y_gpu - y_ref)
+    bound = RTOL * a + ATOL
+    bad = ~(err <= bound)
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError("%s: %d of %d outside |err| <= 1e-4*a + 1e-6; first %s: gpu %s ref %s a %s"
+                             % (what, int(bad.sum()), bad.size, idx.tolist(),
+                                [y_gpu[tuple(i)] for i in idx], [y_ref[tuple(i)] for i in idx],
+                                [a[tuple(i)] for i in idx]))
+
+
+def gpu_pack(codes: np.ndarray) -> torch.Tensor:
+    return q().qpack_uint3(dev(codes))
+
+
+# ------------------------------------------------------------ pack/dequant --
+
+PACK_SHAPES = [(256, 1024), (37, 384), (1, 128), (5, 28672), (300, 256), (3, 131072)]
+
+
+@pytest.mark.parametrize("n,k", PACK_SHAPES)
+def test_qpack_bit_exact(n, k):
+    say("qpack", n, k)
+    c = synth.codes_all8(1000 + n + k, n, k)
+    got = host(gpu_pack(c)).view(np.uint32)
+    assert np.array_equal(got, oracle.pack(c))
+
+
+def test_qpack_tiny_case_and_golden_rows():
+    c, _, _ = synth.tiny_case()
+    say("qpack tiny")
+    assert np.array_equal(host(gpu_pack(c)).view(np.uint32), oracle.pack(c))
+    rows = np.stack([np.full(128, 4, np.uint8), np.full(128, 7, np.uint8), np.zeros(128, np.uint8),
+                     (np.arange(128) % 8).astype(np.uint8)])
+    assert np.array_equal(host(gpu_pack(rows)).view(np.uint32), oracle.pack(rows))
+
+
+@pytest.mark.parametrize("n,k", [(256, 1024), (37, 384), (7, 28672), (2, 131072)])
+def test_qdequant_bit_exact(n, k):
+    say("qdequant", n, k)
+    c = synth.codes_all8(2000 + n, n, k)
+    s = synth.scales(2100 + n, n, k // 128, sigma=0.7, eps=1e-3)
+    packed = gpu_pack(c)
+    w = host(q().qdequant_bf16(packed, dev(s))).view(np.uint16)
+    assert np.array_equal(w, oracle.dequant_bf16(oracle.pack(c), s, k))
+
+
+def test_qdequant_negative_and_tiny_scales():
+    n, k = 16, 256
+    c = synth.codes_all8(7, n, k)
+    s = synth.f32_to_bf16_bits(np.random.default_rng(8).standard_normal((n, 2)).astype(np.float32) * 1e-30)
+    say("qdequant signed tiny scales")
+    w = host(q().qdequant_bf16(gpu_pack(c), dev(s))).view(np.uint16)
+    assert np.array_equal(w, oracle.dequant_bf16(oracle.pack(c), s, k))
+
+
+# ------------------------------------------------------------------ GEMV ---
+
+def run_gemv(c, s, x):
+    n, k = c.shape
+    packed = gpu_pack(c)
+    return host(q().qgemv_w3g128(dev(x.reshape(-1)), packed, dev(s)))
+
+
+def ref_gemv(c, s, x):
+    y, a = oracle.gemm(x.reshape(1, -1), oracle.pack(c), s, c.shape[1])
+    return y[0], a[0]
+
+
+def test_qgemv_tiny_case():
+    c, s, x = synth.tiny_case()
+    say("qgemv tiny 256x1024")
+    y = run_gemv(c, s, x)
+    yr, a = ref_gemv(c, s, x)
+    assert_close(y, yr, a, "tiny")
+
+
+# G = K/128 values that hit every team size of the GEMV kernel, ragged N
+GEMV_SHAPES = [(1, 128), (37, 256), (5, 384), (40, 640), (33, 1152), (17, 2176), (70, 4096),
+               (9, 8064), (300, 8192), (11, 8320), (6, 12800), (8, 28672), (3, 38400),
+               (4, 65536), (2, 131072)]
+
+
+@pytest.mark.parametrize("n,k", GEMV_SHAPES)
+def test_qgemv_parity_all_codes(n, k):
+    say("qgemv", n, k)
+    c = synth.codes_all8(3000 + k, n, k)
+    s = synth.scales(3100 + k, n, k // 128, sigma=0.02, eps=1e-3)
+    x = synth.activations(3200 + k, 1, k)
+    y = run_gemv(c, s, x)
+    yr, a = ref_gemv(c, s, x)
+    assert_close(y, yr, a, "qgemv %dx%d" % (n, k))
+
+
+def test_qgemv_zero_rows_and_one_hot():
+    n, k = 64, 1024
+    c = np.full((n, k), 4, dtype=np.uint8)
+    c[1::2, 5] = 7  # odd rows: one weight, q = +3
+    s = synth.scales(41, n, k // 128, sigma=0.1, eps=1e-3)
+    x = synth.activations(42, 1, k)
+    say("qgemv zero rows")
+    y = run_gemv(c, s, x)
+    assert np.all(y[0::2] == 0.0)
+    yr, a = ref_gemv(c, s, x)
+    assert_close(y, yr, a, "zero rows")
+    xh = np.zeros((1, k), dtype=np.uint16)
+    xh[0, 5] = 0x4040  # 3.0
+    y = run_gemv(c, s, xh)
+    sf = synth.bf16_bits_to_f32(s)
+    assert np.all(y[1::2] == 9.0 * sf[1::2, 0])  # exact: 3 * 3 * s
+
+
+def test_qgemv_wide_activation_range():
+    """Per-group exponent handling: huge, tiny and mixed magnitudes."""
+    n, k = 48, 1024
+    c = synth.codes_all8(51, n, k)
+    s = synth.scales(52, n, k // 128, sigma=0.05, eps=1e-3)
+    rng = np.random.default_rng(53)
+    xf = rng.standard_normal(k).astype(np.float32)
+    xf[:128] *= np.float32(2.0 ** 60)
+    xf[128:256] *= np.float32(2.0 ** -60)
+    xf[256:384] *= np.exp2(rng.integers(-12, 12, 128)).astype(np.float32)  # 24 binades in one group
+    xf[384:512] = 0.0
+    x = synth.f32_to_bf16_bits(xf)
+    say("qgemv wide range")
+    y = run_gemv(c, s, x)
+    yr, a = ref_gemv(c, s, x)
+    assert_close(y, yr, a, "wide range")
+
+
+def test_qgemv_k_zero_and_n_zero():
+    mod = q()
+    say("qgemv K=0 / N=0")
+    packed = torch.empty((5, 0), dtype=torch.int32, device="cuda")
+    scales = torch.empty((5, 0), dtype=torch.int16, device="cuda")
+    x = torch.empty((0,), dtype=torch.int16, device="cuda")
+    y = torch.full((5,), 7.0, device="cuda")
+    mod.qgemv_w3g128(x, packed, scales, out=y)
+    assert host(y).tolist() == [0.0] * 5
+    y0 = mod.qgemv_w3g128(torch.zeros(1024, dtype=torch.int16, device="cuda"),
+                          torch.empty((0, 96), dtype=torch.int32, device="cuda"),
+                          torch.empty((0, 8), dtype=torch.int16, device="cuda"))
+    assert y0.shape == (0,)
+
+
+def test_qgemv_deterministic():
+    n, k = 4096, 8192
+    c = synth.codes(61, n, k)
+    s = synth.scales(62, n, k // 128)
+    x = synth.activations(63, 1, k)
+    say("qgemv determinism")
+    packed, sd, xd = gpu_pack(c), dev(s), dev(x.reshape(-1))
+    y1 = host(q().qgemv_w3g128(xd, packed, sd))
+    y2 = host(q().qgemv_w3g128(xd, packed, sd))
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+
+
+def test_binding_rejects_misaligned_view():
+    mod = q()
+    k = 1024
+    big = torch.zeros(k + 8, dtype=torch.int16, device="cuda")
+    packed = torch.zeros((4, 96), dtype=torch.int32, device="cuda")
+    scales = torch.zeros((4, 8), dtype=torch.int16, device="cuda")
+    say("qgemv misaligned")
+    with pytest.raises(mod.Qw3Error) as ei:
+        mod.qgemv_w3g128(big[1:k + 1], packed, scales)
+    assert ei.value.status == mod.QW3_ERR_ALIGN
+
+
+# ------------------------------------------------------------- small M ----
+
+@pytest.mark.parametrize("m", [2, 3, 4, 8, 16, 17, 31, 32, 33, 64, 100])
+@pytest.mark.parametrize("n,k", [(200, 1024), (70, 8192), (24, 28672)])
+def test_qgemm_parity(m, n, k):
+    say("qgemm", m, n, k)
+    c = synth.codes_all8(4000 + n + k, n, k)
+    s = synth.scales(4100 + k, n, k // 128, sigma=0.02, eps=1e-3)
+    x = synth.activations(4200 + m, m, k)
+    y = host(q().qgemm_w3g128_smallM(dev(x), gpu_pack(c), dev(s)))
+    yr, a = oracle.gemm(x, oracle.pack(c), s, k)
+    assert_close(y, yr, a, "qgemm M=%d %dx%d" % (m, n, k))
+
+
+def test_qgemm_m1_is_gemv_and_rows_repeat():
+    n, k = 100, 2048
+    c = synth.codes(71, n, k)
+    s = synth.scales(72, n, k // 128)
+    x1 = synth.activations(73, 1, k)
+    packed, sd = gpu_pack(c), dev(s)
+    say("qgemm M=1 / repeated rows")
+    y1 = host(q().qgemm_w3g128_smallM(dev(x1), packed, sd))
+    yv = host(q().qgemv_w3g128(dev(x1.reshape(-1)), packed, sd))
+    assert np.array_equal(y1[0].view(np.uint32), yv.view(np.uint32))
+    xr = np.repeat(x1, 20, axis=0)
+    yr = host(q().qgemm_w3g128_smallM(dev(xr), packed, sd))
+    assert all(np.array_equal(yr[i].view(np.uint32), yr[0].view(np.uint32)) for i in range(20))
+    ref, a = oracle.gemm(x1, oracle.pack(c), s, k)
+    assert_close(yr[0], ref[0], a[0], "repeated row")
+
+
+def test_qgemm_deterministic():
+    n, k, m = 512, 8192, 16
+    c = synth.codes(81, n, k)
+    s = synth.scales(82, n, k // 128)
+    x = synth.activations(83, m, k)
+    packed, sd, xd = gpu_pack(c), dev(s), dev(x)
+    say("qgemm determinism")
+    y1 = host(q().qgemm_w3g128_smallM(xd, packed, sd))
+    y2 = host(q().qgemm_w3g128_smallM(xd, packed, sd))
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+
+
+# --------------------------------------------- full 70B-layer shapes -------
+
+@functools.lru_cache(maxsize=2)
+def layer(name):
+    return synth.layer_weights(name)
+
+
+def sample_rows(n, count=192, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([[0, 1, n // 2, n - 2, n - 1], rng.integers(0, n, count)]))
+    return rows.astype(np.int64)
+
+
+def check_layer_gemm(name, m):
+    c, s = layer(name)
+    n, k = c.shape
+    x = synth.layer_x(m, k)
+    say("layer", name, "M=%d" % m, n, k)
+    packed = gpu_pack(c)
+    rows = sample_rows(n, seed=m)
+    got_words = host(packed[torch.from_numpy(rows).cuda()]).view(np.uint32)
+    ref_words = oracle.pack(c[rows])
+    assert np.array_equal(got_words, ref_words), "packed words differ on sampled rows"
+    if m == 1:
+        y = host(q().qgemv_w3g128(dev(x.reshape(-1)), packed, dev(s)))[None, :]
+    else:
+        y = host(q().qgemm_w3g128_smallM(dev(x), packed, dev(s)))
+    yr, a = oracle.gemm(x, ref_words, s[rows], k)
+    assert_close(y[:, rows], yr, a, "%s M=%d" % (name, m))
+
+
+def test_gate_proj_b1_full_size():
+    check_layer_gemm("gate_proj", 1)
+
+
+@pytest.mark.parametrize("name", ["q_proj", "k_proj", "v_proj", "o_proj", "up_proj", "down_proj"])
+def test_layer_projection_b1_full_size(name):
+    check_layer_gemm(name, 1)
+
+
+@pytest.mark.parametrize("m", [4, 8, 16, 32])
+@pytest.mark.parametrize("name", ["gate_proj", "down_proj"])
+def test_batched_decode_full_size(name, m):
+    check_layer_gemm(name, m)
+
+
+@pytest.mark.parametrize("name", ["gate_proj", "down_proj"])
+def test_prefill_m512_full_size(name):
+    c, s = layer(name)
+    n, k = c.shape
+    m = 512
+    x = synth.layer_x(m, k)
+    say("prefill", name, m, n, k)
+    y = host(q().qgemm_w3g128_smallM(dev(x), gpu_pack(c), dev(s)))
+    rows = sample_rows(n, count=24, seed=5)
+    yr, a = oracle.gemm(x, oracle.pack(c[rows]), s[rows], k)
+    assert_close(y[:, rows], yr, a, "prefill %s" % name)
