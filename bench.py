@@ -15,7 +15,9 @@ the kernels are launched on.
 
 Prints ONE JSON line on stdout.  `--extra` also measures the other workloads
 (the full layer at batch 1, batched decode M = 4..32, prefill M = 512) and
-prints them as JSON lines on stderr.
+prints them as JSON lines on stderr; the batch-1 projections there are timed
+per call inside a replayed HIP graph, since a host launch costs more than the
+smaller ones take to run.
 """
 from __future__ import annotations
 
@@ -122,7 +124,24 @@ def cpu_baseline(c, s, x, k, budget_s=2.5):
     }
 
 
-def bench_extra(torch, q, steps, warmup, x_cache):
+def graph_time(torch, fn, reps: int, replays: int, warmup: int):
+    """Per-call device time of fn(i), i = 0..reps-1, captured once in a HIP graph
+    and replayed: host launch overhead (which exceeds the run time of the small
+    projections) stays out of the figure."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        fn(0)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            for i in range(reps):
+                fn(i)
+    torch.cuda.synchronize()
+    return time_steps(torch, lambda i: graph.replay(), replays, warmup) / reps
+
+
+def bench_extra(torch, q, steps, warmup):
     """Full layer at B=1, batched decode, prefill: JSON lines on stderr."""
     import synth
     out = []
@@ -134,9 +153,12 @@ def bench_extra(torch, q, steps, warmup, x_cache):
         rot = Rotation(torch, packed, scales)
         xd = torch.from_numpy(synth.layer_x(1, k).reshape(-1).view(np.int16)).cuda()
         y = torch.empty(n, dtype=torch.float32, device="cuda")
-        ms = time_steps(torch, lambda i: q.qgemv_w3g128(xd, rot[i][0], rot[i][1], out=y), steps, warmup)
+        ms_launch = time_steps(torch, lambda i: q.qgemv_w3g128(xd, rot[i][0], rot[i][1], out=y), steps, warmup)
+        ms = graph_time(torch, lambda i: q.qgemv_w3g128(xd, rot[i][0], rot[i][1], out=y), 20,
+                        max(10, steps // 20), 3)
         b = gemv_bytes(n, k)
-        layer[name] = {"us": round(ms * 1e3, 3), "GB/s": round(b / ms / 1e6, 1), "bytes": b}
+        layer[name] = {"us": round(ms * 1e3, 3), "GB/s": round(b / ms / 1e6, 1), "bytes": b,
+                       "us_stream_launches": round(ms_launch * 1e3, 3)}
         total_bytes += b
         total_ms += ms
         if name in ("gate_proj", "down_proj"):
@@ -154,12 +176,25 @@ def bench_extra(torch, q, steps, warmup, x_cache):
                 out.append(rec)
         del rot, packed, scales
         torch.cuda.empty_cache()
-    out.insert(0, {"workload": "70B decoder layer, 7 projections back to back, B=1",
+    out.insert(0, {"workload": "70B decoder layer, 7 projections back to back, B=1 (device time per call, "
+                               "graph replay of 20 calls)",
                    "per_projection": layer, "layer_us_sum": round(total_ms * 1e3, 3),
                    "layer_GB/s": round(total_bytes / total_ms / 1e6, 1),
                    "layer_HBM_frac": round(total_bytes / total_ms / 1e6 / HBM_PEAK_GBS, 4)})
     for rec in out:
         print(json.dumps(rec), file=sys.stderr, flush=True)
+
+
+def read_copy_ceiling(torch):
+    """A plain 1 GiB device copy (torch copy_): what HBM gives a streaming kernel here."""
+    src = torch.ones(256 * 2 ** 20, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    nbytes = src.numel() * 4
+    ms_copy = time_steps(torch, lambda i: dst.copy_(src), 20, 3)
+    rec = {"workload": "ceiling: 1 GiB device copy (read + write)",
+           "copy_GB/s(read+write)": round(2 * nbytes / ms_copy / 1e6, 1)}
+    print(json.dumps(rec), file=sys.stderr, flush=True)
+    del src, dst
 
 
 def main():
@@ -169,6 +204,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--extra", action="store_true", help="also time layer / batched / prefill workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="first run 5 plain 256 MiB device copies (torch copy_), the known-size "
+                         "reference for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE counters")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="also time a plain 1 GiB device copy and print its GB/s on stderr")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
@@ -182,6 +222,16 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+
+    if args.calibrate:
+        src = torch.ones(64 * 2 ** 20, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    if args.ceiling:
+        read_copy_ceiling(torch)
 
     n, k = synth.LAYER_70B["gate_proj"][:2]
     c, s, packed, scales = make_weight(torch, q, "gate_proj")
@@ -218,7 +268,7 @@ def main():
     if args.extra:
         del rot, packed, scales
         torch.cuda.empty_cache()
-        bench_extra(torch, q, max(50, args.steps // 4), max(10, args.warmup // 4), None)
+        bench_extra(torch, q, max(50, args.steps // 4), max(10, args.warmup // 4))
     print(json.dumps(line), flush=True)
 
 

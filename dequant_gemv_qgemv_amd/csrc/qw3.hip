@@ -11,22 +11,24 @@
 // Decode.  Two codes are turned into an exact fp16 pair with two VALU ops:
 //   v = (window & mask) | 0x64006400   puts code a at mantissa bits [p,p+3) of
 //                                      the low half and code b at [p',p'+3) of
-//                                      the high half of two fp16 values 1024+..
-//   q = fma(v, (2^-p, 2^-p'), -(1024*2^-p + 4, 1024*2^-p' + 4))
-// which yields (a - 4, b - 4) exactly.  `window` is a 32-bit funnel shift of
-// the 96-bit block.  The 16 pairs of a block come from 7 windows, three of
-// which are the raw words, so a block of 32 codes costs 4 shifts + 16 and-or +
-// 16 packed fma.  Which two codes share an fp16 pair does not matter for a dot
-// product as long as the activations are paired the same way, so activations
-// are converted once into the same pairing (kPairLo / kPairHi below).
+//                                      the high half: fp16 values 1024 + a*2^p
+//                                      and 1024 + b*2^p'
+//   q = v - (1024 + 4*2^p, 1024 + 4*2^p')   (one v_pk_add_f16)
+// which yields ((a - 4) * 2^p, (b - 4) * 2^p') exactly; the 2^-p factors are
+// folded into the activations.  `window` is a 32-bit funnel shift of the
+// 96-bit block.  The 16 pairs of a block come from 7 windows, three of which
+// are the raw words, so a block of 32 codes costs 4 shifts + 16 and-or + 16
+// packed adds.  Which two codes share a pair does not matter for a dot product
+// as long as the activations are paired the same way, so activations are
+// converted once into the same pairing (kPairs below).
 //
 // Activations.  x is bf16; the products use fp16 operands, so each group of
 // 128 activations is scaled by a power of two 2^-e that brings its largest
-// magnitude into [2^14, 2^15) and is then rounded to fp16.  bf16 has 8
-// significant bits and fp16 11, so this is exact for every element within
-// 2^31 of the group's largest; 2^e is multiplied back in fp32 together with
-// the weight scale.  Every product q * x' is then exact and only the fp32
-// accumulation rounds.
+// magnitude into [2^14, 2^15), and each element by its slot's 2^-p, and is
+// then rounded to fp16.  bf16 has 8 significant bits and fp16 11, so this is
+// exact for every element within 2^24 of the group's largest; 2^e is
+// multiplied back in fp32 together with the weight scale.  Every product is
+// then exact and only the fp32 accumulation rounds.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -47,10 +49,31 @@ constexpr int kGroup = 128;         // weights per scale
 constexpr int kWordsPerGroup = 12;  // 128 * 3 / 32
 
 // ----------------------------------------------------------- decode table --
-// Code pairs of one 32-code block, in the order decode_block() emits them.
-// Pair i holds code kPairLo[i] in its low fp16 half and kPairHi[i] in its high.
-__device__ constexpr int kPairLo[16] = {0, 1, 2, 3, 4, 5, 12, 13, 14, 15, 16, 22, 23, 24, 25, 26};
-__device__ constexpr int kPairHi[16] = {7, 6, 9, 8, 10, 11, 18, 17, 19, 21, 20, 28, 27, 29, 31, 30};
+// The 16 code pairs of a 32-code block: window index (0: w0, 1: bits [4,36),
+// 2: [12,44), 3: w1, 4: [41,73), 5: w2, 6: [71,96)), low code, high code, and
+// their bit offsets p, p' inside the window's two 16-bit halves.  Every code
+// 0..31 appears once; lo at 3*lo - start(win) = p, hi at 3*hi - start - 16 = p'.
+struct PairSpec {
+    int win, lo, hi, p, pp;
+};
+constexpr PairSpec kPairs[16] = {
+    {0, 0, 7, 0, 5},   {0, 1, 6, 3, 2},   {1, 2, 9, 2, 7},   {1, 3, 8, 5, 4},
+    {2, 4, 10, 0, 2},  {2, 5, 11, 3, 5},  {3, 12, 18, 4, 6}, {3, 13, 17, 7, 3},
+    {4, 14, 19, 1, 0}, {4, 15, 21, 4, 6}, {4, 16, 20, 7, 3}, {5, 22, 28, 2, 4},
+    {5, 23, 27, 5, 1}, {6, 24, 29, 1, 0}, {6, 25, 31, 4, 6}, {6, 26, 30, 7, 3}};
+constexpr int kWinStart[7] = {0, 4, 12, 32, 41, 64, 71};
+
+constexpr bool pairs_cover_block() {
+    int seen = 0;
+    for (int i = 0; i < 16; ++i) {
+        const PairSpec ps = kPairs[i];
+        if (3 * ps.lo - kWinStart[ps.win] != ps.p || 3 * ps.hi - kWinStart[ps.win] - 16 != ps.pp) return false;
+        if (ps.p < 0 || ps.p > 7 || ps.pp < 0 || ps.pp > 7) return false;
+        seen |= (1 << ps.lo) | (1 << ps.hi);
+    }
+    return seen == -1;
+}
+static_assert(pairs_cover_block(), "decode table must cover codes 0..31 once at valid offsets");
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
@@ -61,47 +84,65 @@ __device__ __forceinline__ uint32_t pack_h2(_Float16 lo, _Float16 hi) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
-// Exact (a-4, b-4) from a window holding code a at bits [P, P+3) and code b at
-// bits [16+PP, 16+PP+3).
+// Exact ((a-4)*2^P, (b-4)*2^PP) from a window holding code a at bits [P, P+3)
+// and code b at bits [16+PP, 16+PP+3).
+// `magic` is 0x64006400 held in a VGPR (see magic_vgpr()): with the mask in an
+// SGPR the and/or pair then issues as a single v_and_or_b32 (gfx9 VOP3 cannot
+// encode two literal constants).
 template <int P, int PP>
-__device__ __forceinline__ h2_t q_pair(uint32_t win) {
+__device__ __forceinline__ h2_t q_pair(uint32_t win, uint32_t magic) {
     constexpr uint32_t kMask = (7u << P) | (7u << (16 + PP));
-    constexpr h2_t kMul = {(_Float16)(1.0f / (1 << P)), (_Float16)(1.0f / (1 << PP))};
-    constexpr h2_t kAdd = {(_Float16)(-(1024.0f / (1 << P) + 4.0f)),
-                           (_Float16)(-(1024.0f / (1 << PP) + 4.0f))};
-    const uint32_t v = (win & kMask) | 0x64006400u;
-    return __builtin_elementwise_fma(as_h2(v), kMul, kAdd);
+    constexpr h2_t kSub = {(_Float16)(1024.0f + 4.0f * (1 << P)), (_Float16)(1024.0f + 4.0f * (1 << PP))};
+    const uint32_t v = (win & kMask) | magic;
+    return as_h2(v) - kSub;
 }
 
-// The 32 codes of words (w0, w1, w2) as 16 exact fp16 pairs, pair order above.
-__device__ __forceinline__ void decode_block(uint32_t w0, uint32_t w1, uint32_t w2, h2_t (&q)[16]) {
-    const uint32_t s4 = __builtin_amdgcn_alignbit(w1, w0, 4);    // stream bits [4, 36)
-    const uint32_t s12 = __builtin_amdgcn_alignbit(w1, w0, 12);  // [12, 44)
-    const uint32_t s41 = __builtin_amdgcn_alignbit(w2, w1, 9);   // [41, 73)
-    const uint32_t s71 = w2 >> 7;                                // [71, 96)
-    q[0] = q_pair<0, 5>(w0);
-    q[1] = q_pair<3, 2>(w0);
-    q[2] = q_pair<2, 7>(s4);
-    q[3] = q_pair<5, 4>(s4);
-    q[4] = q_pair<0, 2>(s12);
-    q[5] = q_pair<3, 5>(s12);
-    q[6] = q_pair<4, 6>(w1);
-    q[7] = q_pair<7, 3>(w1);
-    q[8] = q_pair<1, 0>(s41);
-    q[9] = q_pair<4, 6>(s41);
-    q[10] = q_pair<7, 3>(s41);
-    q[11] = q_pair<2, 4>(w2);
-    q[12] = q_pair<5, 1>(w2);
-    q[13] = q_pair<1, 0>(s71);
-    q[14] = q_pair<4, 6>(s71);
-    q[15] = q_pair<7, 3>(s71);
+// 0x64006400 (two fp16 1024.0) in a VGPR the compiler cannot constant-fold.
+__device__ __forceinline__ uint32_t magic_vgpr() {
+    uint32_t m;
+    asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(m));
+    return m;
+}
+
+template <int I>
+__device__ __forceinline__ h2_t q_pair_i(const uint32_t (&win)[7], uint32_t magic) {
+    constexpr PairSpec ps = kPairs[I];
+    return q_pair<ps.p, ps.pp>(win[ps.win], magic);
+}
+
+// The 32 codes of words (w0, w1, w2) as 16 exact fp16 pairs, kPairs order.
+__device__ __forceinline__ void decode_block(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t magic,
+                                             h2_t (&q)[16]) {
+    const uint32_t win[7] = {w0,
+                             __builtin_amdgcn_alignbit(w1, w0, 4),
+                             __builtin_amdgcn_alignbit(w1, w0, 12),
+                             w1,
+                             __builtin_amdgcn_alignbit(w2, w1, 9),
+                             w2,
+                             w2 >> 7};
+    q[0] = q_pair_i<0>(win, magic);
+    q[1] = q_pair_i<1>(win, magic);
+    q[2] = q_pair_i<2>(win, magic);
+    q[3] = q_pair_i<3>(win, magic);
+    q[4] = q_pair_i<4>(win, magic);
+    q[5] = q_pair_i<5>(win, magic);
+    q[6] = q_pair_i<6>(win, magic);
+    q[7] = q_pair_i<7>(win, magic);
+    q[8] = q_pair_i<8>(win, magic);
+    q[9] = q_pair_i<9>(win, magic);
+    q[10] = q_pair_i<10>(win, magic);
+    q[11] = q_pair_i<11>(win, magic);
+    q[12] = q_pair_i<12>(win, magic);
+    q[13] = q_pair_i<13>(win, magic);
+    q[14] = q_pair_i<14>(win, magic);
+    q[15] = q_pair_i<15>(win, magic);
 }
 
 // acc + sum over the block of q * x', x' given as 16 fp16 pairs in pair order.
-__device__ __forceinline__ float dot_block(uint32_t w0, uint32_t w1, uint32_t w2,
+__device__ __forceinline__ float dot_block(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t magic,
                                            const uint32_t *xp, float acc) {
     h2_t q[16];
-    decode_block(w0, w1, w2, q);
+    decode_block(w0, w1, w2, magic, q);
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc = __builtin_amdgcn_fdot2(q[i], as_h2(xp[i]), acc, false);
     return acc;
@@ -157,20 +198,24 @@ __device__ __forceinline__ int group_exponent(uint32_t absmax_bits) {
     return __builtin_amdgcn_frexp_expf(bf16_to_f32(absmax_bits)) - 15;
 }
 
-// 32 bf16 values -> x * 2^-e as fp16, arranged as the 16 pairs of a block.
+// 32 bf16 values -> x * 2^-(e + slot offset) as fp16, arranged as the 16
+// pairs of a block (kPairs order).
 __device__ __forceinline__ void convert_block(const uint4 (&xb)[4], int e, uint32_t (&out)[16]) {
-    _Float16 h[32];
+    float f[32];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const uint32_t d[4] = {xb[i].x, xb[i].y, xb[i].z, xb[i].w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            h[8 * i + 2 * j] = (_Float16)ldexpf(bf16_to_f32(d[j] & 0xFFFFu), -e);
-            h[8 * i + 2 * j + 1] = (_Float16)ldexpf(bf16_to_f32(d[j] >> 16), -e);
+            f[8 * i + 2 * j] = bf16_to_f32(d[j] & 0xFFFFu);
+            f[8 * i + 2 * j + 1] = bf16_to_f32(d[j] >> 16);
         }
     }
 #pragma unroll
-    for (int p = 0; p < 16; ++p) out[p] = pack_h2(h[kPairLo[p]], h[kPairHi[p]]);
+    for (int p = 0; p < 16; ++p) {
+        const PairSpec ps = kPairs[p];
+        out[p] = pack_h2((_Float16)ldexpf(f[ps.lo], -e - ps.p), (_Float16)ldexpf(f[ps.hi], -e - ps.pp));
+    }
 }
 
 __device__ __forceinline__ void load_x32(const uint16_t *src, uint4 (&xb)[4]) {
@@ -250,156 +295,282 @@ __global__ __launch_bounds__(256) void qdequant_kernel(const uint32_t *__restric
 // ------------------------------------------------------------ qgemv -------
 // Batch-1 fused GEMV.  A team of T lanes owns one output row at a time; lane
 // g of the team owns weight group g (128 weights = 12 words = 48 contiguous
-// bytes), so a team's three 16-byte loads per lane cover the row contiguously.
-// The lane's 128 activations stay in 64 VGPRs as fp16 pairs for the whole
-// kernel ("x-stationary").  WG = T * R threads process R rows per iteration
-// in a grid-stride loop, with the next row's loads issued before the current
-// row is decoded.  The team's partial sums are reduced in a fixed order with
-// DPP (T <= 64) or DPP + LDS (T > 64), so results are run-to-run identical.
-template <int T>
-struct GemvCfg {
-    static constexpr int R = T >= 512 ? 1 : 512 / T;  // rows per iteration
-    static constexpr int WGS = T * R;                  // threads per workgroup
-    static constexpr int WAVES_PER_TEAM = T > 64 ? T / 64 : 1;
+// bytes), so the team's three 16-byte loads per lane cover the row
+// contiguously.  The lane's 128 activations stay in 64 VGPRs as fp16 pairs
+// for the whole kernel ("x-stationary").  R = WGS / T teams per workgroup walk
+// the rows in a grid-stride loop.  Each lane keeps a ring of D rows in flight:
+// the loads of row i + D are issued as soon as row i has been decoded, so the
+// memory system always holds D rows per team (the GEMV is latency-bound
+// without it).  Partial sums are reduced in a fixed order (DPP inside a wave,
+// then LDS across waves), so results are run-to-run identical.
+#ifndef QW3_GEMV_DEPTH
+#define QW3_GEMV_DEPTH 3
+#endif
+constexpr int kGemvDepth = QW3_GEMV_DEPTH;
+#ifndef QW3_GEMV_WGS
+#define QW3_GEMV_WGS 256
+#endif
+constexpr int kGemvWGS = QW3_GEMV_WGS;  // threads per workgroup, teams of T <= 64
+#ifdef QW3_GEMV_WAVES
+#define QW3_GEMV_OCC __attribute__((amdgpu_waves_per_eu(QW3_GEMV_WAVES)))
+#else
+#define QW3_GEMV_OCC
+#endif
+constexpr size_t kMaxLdsX = 64 * 1024;
+
+struct RowBuf {
+    uint4 a, b, c;  // the lane's 12 words of the row
+    uint32_t s;     // the lane's bf16 scale
 };
 
-template <int T, bool kLdsX>
-__global__ __launch_bounds__(GemvCfg<T>::WGS) void qgemv_kernel(
-    const uint16_t *__restrict__ x, const uint32_t *__restrict__ packed,
-    const uint16_t *__restrict__ scales, float *__restrict__ y, int64_t N, int G) {
-    using Cfg = GemvCfg<T>;
-    constexpr int R = Cfg::R;
-    extern __shared__ uint32_t smem[];
+// Loads the lane's 12 words and scale of row r.  Every load is issued
+// unconditionally -- rows past the end read the last row, lanes without a
+// group read the last group -- so the code between loads is straight-line and
+// the compiler can wait for exactly the loads a step needs (s_waitcnt vmcnt(n))
+// instead of draining every load in flight.  The extra rows are never stored
+// and the extra groups meet zero activations.
+__device__ __forceinline__ void load_row(const uint32_t *__restrict__ packed, const uint16_t *__restrict__ scales,
+                                         int64_t r, int64_t N, int64_t W, int G, int g_load, RowBuf &rb) {
+    const int64_t rr = r < N ? r : N - 1;
+    const uint4 *p = reinterpret_cast<const uint4 *>(packed + rr * W + g_load * kWordsPerGroup);
+    rb.a = p[0];
+    rb.b = p[1];
+    rb.c = p[2];
+    rb.s = scales[rr * G + g_load];
+}
 
-    const int tid = threadIdx.x;
-    const int gl = tid % T;  // weight group owned by this lane
-    const int team = tid / T;
-    const bool lane_on = gl < G;
-    const int64_t W = (int64_t)G * kWordsPerGroup;
-    const int64_t stride = (int64_t)gridDim.x * R;
-    int64_t row = (int64_t)blockIdx.x * R + team;
+// sum_k q_k x'_k * 2^e * s over the lane's group of one row.
+__device__ __forceinline__ float row_partial(const RowBuf &rb, const uint32_t (&xp)[64], int e, uint32_t magic) {
+    const float a0 = dot_block(rb.a.x, rb.a.y, rb.a.z, magic, xp + 0, 0.f);
+    const float a1 = dot_block(rb.a.w, rb.b.x, rb.b.y, magic, xp + 16, 0.f);
+    const float a2 = dot_block(rb.b.z, rb.b.w, rb.c.x, magic, xp + 32, 0.f);
+    const float a3 = dot_block(rb.c.y, rb.c.z, rb.c.w, magic, xp + 48, 0.f);
+    return ldexpf((a0 + a1) + (a2 + a3), e) * bf16_to_f32(rb.s);
+}
 
-    auto load_row = [&](int64_t r, uint4 &a0, uint4 &a1, uint4 &a2, uint32_t &s) {
-        if (lane_on && r < N) {
-            const uint4 *p = reinterpret_cast<const uint4 *>(packed + r * W + gl * kWordsPerGroup);
-            a0 = p[0];
-            a1 = p[1];
-            a2 = p[2];
-            s = scales[r * G + gl];
-        } else {
-            a0 = a1 = a2 = make_uint4(0, 0, 0, 0);
-            s = 0;
-        }
-    };
+// Activation staging, LDS path.  The workgroup converts x once: 4 threads (a
+// quad) per group, one 32-value block each, U blocks per thread at most; then
+// every lane copies its own group's 64 pairs and exponent into registers.
+// Issue (raw loads) and finish (convert, exchange) are split so the row loads
+// can be issued in between.
+template <int U>
+struct XStage {
+    uint4 raw[U][4];
+};
 
-    // First row in flight while the activations are converted.
-    uint4 a0, a1, a2;
-    uint32_t sa;
-    load_row(row, a0, a1, a2, sa);
+template <int U>
+__device__ __forceinline__ void xstage_issue(const uint16_t *__restrict__ x, int G, XStage<U> &st) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        int idx = threadIdx.x + u * blockDim.x;
+        if (idx >= 4 * G) idx = 4 * G - 1;  // clamped: always issued
+        load_x32(x + (size_t)(idx >> 2) * kGroup + (idx & 3) * 32, st.raw[u]);
+    }
+}
 
-    uint32_t xp[64];
-    int e = 0;
-    if constexpr (kLdsX) {
-        // The workgroup converts x once into LDS: 4 lanes (a quad) per group,
-        // one 32-value block each, then every lane copies its group's pairs.
-        uint32_t *xs = smem;                                        // [G][64] pairs
-        int *xe = reinterpret_cast<int *>(smem + (size_t)G * 64);  // [G]
-        for (int idx = tid; idx < 4 * G; idx += Cfg::WGS) {
+// LDS layout of the converted activations: xs4[q][g] holds pairs 4q..4q+3 of
+// group g (16 bytes), q = 0..15, so that when lane g fetches its group the 64
+// lanes of each ds_read_b128 touch 64 consecutive 16-byte chunks (no bank
+// conflicts); exponents follow as int[G].
+template <int U>
+__device__ __forceinline__ void xstage_convert(const XStage<U> &st, int G, uint32_t *smem) {
+    uint4 *xs4 = reinterpret_cast<uint4 *>(smem);                // [16][G]
+    int *xe = reinterpret_cast<int *>(smem + (size_t)G * 64);  // [G]
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int idx = threadIdx.x + u * blockDim.x;  // quads share validity: 4G and blockDim are multiples of 4
+        uint32_t m = absmax32(st.raw[u]);
+        m = max(m, dpp_u32<kDppQuadXor1>(m));
+        m = max(m, dpp_u32<kDppQuadXor2>(m));
+        if (idx < 4 * G) {
             const int g = idx >> 2, blk = idx & 3;
-            uint4 xb[4];
-            load_x32(x + (size_t)g * kGroup + blk * 32, xb);
-            uint32_t m = absmax32(xb);
-            m = max(m, dpp_u32<kDppQuadXor1>(m));
-            m = max(m, dpp_u32<kDppQuadXor2>(m));
             const int eg = group_exponent(m);
             uint32_t out[16];
-            convert_block(xb, eg, out);
-            uint4 *dst = reinterpret_cast<uint4 *>(xs + ((size_t)g * 4 + blk) * 16);
+            convert_block(st.raw[u], eg, out);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dst[i] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
+            for (int i = 0; i < 4; ++i)
+                xs4[(size_t)(4 * blk + i) * G + g] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
             if (blk == 0) xe[g] = eg;
         }
+    }
+}
+
+// After a barrier: this lane's pairs and exponent (zeros for lanes without a group).
+__device__ __forceinline__ void xstage_fetch(const uint32_t *smem, int G, int gl, bool lane_on,
+                                             uint32_t (&xp)[64], int &e) {
+    const int *xe = reinterpret_cast<const int *>(smem + (size_t)G * 64);
+    const int gs = lane_on ? gl : 0;
+    const uint4 *xs4 = reinterpret_cast<const uint4 *>(smem);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const uint4 v = xs4[(size_t)i * G + gs];
+        xp[4 * i] = lane_on ? v.x : 0u;
+        xp[4 * i + 1] = lane_on ? v.y : 0u;
+        xp[4 * i + 2] = lane_on ? v.z : 0u;
+        xp[4 * i + 3] = lane_on ? v.w : 0u;
+    }
+    e = lane_on ? xe[gs] : 0;
+}
+
+// Activation staging without LDS (very long rows): each lane converts its own
+// group in two passes (max, then convert).
+__device__ __forceinline__ void xstage_lane(const uint16_t *__restrict__ x, int gl, bool lane_on,
+                                            uint32_t (&xp)[64], int &e) {
+    const uint16_t *xg = x + (size_t)(lane_on ? gl : 0) * kGroup;
+    uint32_t m = 0;
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+        uint4 xb[4];
+        load_x32(xg + blk * 32, xb);
+        m = max(m, absmax32(xb));
+    }
+    e = group_exponent(m);
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+        uint4 xb[4];
+        load_x32(xg + blk * 32, xb);
+        uint32_t out[16];
+        convert_block(xb, e, out);
+#pragma unroll
+        for (int p = 0; p < 16; ++p) xp[blk * 16 + p] = lane_on ? out[p] : 0u;
+    }
+    if (!lane_on) e = 0;
+}
+
+// Teams of T <= 64 lanes (T a power of two >= G): the reduction is DPP only.
+// Order of the prologue: activation loads, then the first D rows, then the
+// conversion (which waits only for the activation loads).
+template <int T>
+__global__ __launch_bounds__(kGemvWGS) QW3_GEMV_OCC void qgemv_small_kernel(const uint16_t *__restrict__ x,
+                                                               const uint32_t *__restrict__ packed,
+                                                               const uint16_t *__restrict__ scales,
+                                                               float *__restrict__ y, int64_t N, int G,
+                                                               int lds_x) {
+    constexpr int R = kGemvWGS / T;
+    constexpr int D = kGemvDepth;
+    extern __shared__ uint32_t smem[];
+    const int gl = threadIdx.x % T;
+    const bool lane_on = gl < G;
+    const int g_load = lane_on ? gl : G - 1;
+    const int64_t W = (int64_t)G * kWordsPerGroup;
+    const int64_t stride = (int64_t)gridDim.x * R;
+    const int64_t row0 = (int64_t)blockIdx.x * R + threadIdx.x / T;
+
+    // Ring of E = D + 1 row buffers.  Step i first issues the loads of row
+    // i + D into the buffer that step i - 1 finished with, then decodes row i:
+    // D rows are in flight while a row is decoded (the scheduling barrier
+    // keeps the compiler from sinking the loads behind the decode).
+    constexpr int E = D + 1;
+    uint32_t xp[64];
+    int e = 0;
+    RowBuf ring[E];
+    if (lds_x) {
+        XStage<1> st;  // 4G <= 256 <= blockDim: one block per thread
+        xstage_issue<1>(x, G, st);
+#pragma unroll
+        for (int d = 0; d < D; ++d) load_row(packed, scales, row0 + d * stride, N, W, G, g_load, ring[d]);
+        xstage_convert<1>(st, G, smem);
         __syncthreads();
-        if (lane_on) {
-            const uint4 *src = reinterpret_cast<const uint4 *>(xs + (size_t)gl * 64);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const uint4 v = src[i];
-                xp[4 * i] = v.x;
-                xp[4 * i + 1] = v.y;
-                xp[4 * i + 2] = v.z;
-                xp[4 * i + 3] = v.w;
-            }
-            e = xe[gl];
-        } else {
-#pragma unroll
-            for (int i = 0; i < 64; ++i) xp[i] = 0;
-        }
+        xstage_fetch(smem, G, gl, lane_on, xp, e);
     } else {
-        // Each lane converts its own group (two passes: max, then convert).
 #pragma unroll
-        for (int i = 0; i < 64; ++i) xp[i] = 0;
-        if (lane_on) {
-            const uint16_t *xg = x + (size_t)gl * kGroup;
-            uint32_t m = 0;
+        for (int d = 0; d < D; ++d) load_row(packed, scales, row0 + d * stride, N, W, G, g_load, ring[d]);
+        xstage_lane(x, gl, lane_on, xp, e);
+    }
+    const uint32_t magic = magic_vgpr();
+
+    for (int64_t row = row0; row < N; row += E * stride) {
 #pragma unroll
-            for (int blk = 0; blk < 4; ++blk) {
-                uint4 xb[4];
-                load_x32(xg + blk * 32, xb);
-                m = max(m, absmax32(xb));
-            }
-            e = group_exponent(m);
-#pragma unroll
-            for (int blk = 0; blk < 4; ++blk) {
-                uint4 xb[4];
-                load_x32(xg + blk * 32, xb);
-                uint32_t out[16];
-                convert_block(xb, e, out);
-#pragma unroll
-                for (int p = 0; p < 16; ++p) xp[blk * 16 + p] = out[p];
-            }
+        for (int i = 0; i < E; ++i) {
+            const int64_t r = row + i * stride;
+            load_row(packed, scales, r + D * stride, N, W, G, g_load, ring[(i + D) % E]);
+            __builtin_amdgcn_sched_barrier(0);
+            const float part = row_partial(ring[i], xp, e, magic);
+            const float tot = segment_sum<T>(part);
+            if (gl == T - 1 && r < N) y[r] = tot;
         }
     }
+}
 
-    float *red = reinterpret_cast<float *>(smem);  // T > 64 only; reused after xs
-    int parity = 0;
-    if constexpr (T > 64) __syncthreads();  // xs/xe fully consumed before reuse
+// Workgroup barrier for LDS hand-offs: waits for this wave's LDS operations
+// only, so its global loads stay in flight across the barrier, and the
+// "memory" clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-    // WG-uniform trip count (the LDS reduction below needs every wave).
-    for (int64_t base = (int64_t)blockIdx.x * R; base < N; base += stride) {
-        uint4 b0, b1, b2;
-        uint32_t sb;
-        load_row(row + stride, b0, b1, b2, sb);
+// Teams of T > 64 lanes, T a multiple of 32 (>= G): each half-wave sums its 32
+// lanes with DPP, the half sums go through LDS, and lane 0 of the team adds
+// its T/32 halves in order.  One barrier per D + 1 rows.  1024-thread
+// workgroups (K > 65536) keep a single row in flight to stay within 128 VGPRs.  The LDS holds the
+// converted activations first, then (after a barrier) the half sums.
+template <int MAXWGS, int D>
+__global__ __launch_bounds__(MAXWGS) QW3_GEMV_OCC void qgemv_big_kernel(const uint16_t *__restrict__ x,
+                                                         const uint32_t *__restrict__ packed,
+                                                         const uint16_t *__restrict__ scales,
+                                                         float *__restrict__ y, int64_t N, int G, int T,
+                                                         int lds_x) {
+    extern __shared__ uint32_t smem[];
+    const int tid = threadIdx.x;
+    const int wgs = blockDim.x;
+    const int R = wgs / T;
+    const int gl = tid % T;
+    const int team = tid / T;
+    const int halves = T / 32;
+    const bool lane_on = gl < G;
+    const int g_load = lane_on ? gl : G - 1;
+    const int64_t W = (int64_t)G * kWordsPerGroup;
+    const int64_t stride = (int64_t)gridDim.x * R;
+    const int64_t row0 = (int64_t)blockIdx.x * R + team;
 
-        float acc0 = 0.f, acc1 = 0.f;
-        acc0 = dot_block(a0.x, a0.y, a0.z, xp + 0, acc0);
-        acc1 = dot_block(a0.w, a1.x, a1.y, xp + 16, acc1);
-        acc0 = dot_block(a1.z, a1.w, a2.x, xp + 32, acc0);
-        acc1 = dot_block(a2.y, a2.z, a2.w, xp + 48, acc1);
-        const float part = ldexpf(acc0 + acc1, e) * bf16_to_f32(sa);
-
-        if constexpr (T <= 64) {
-            const float tot = segment_sum<T>(part);
-            if (gl == T - 1 && row < N) y[row] = tot;
-        } else {
-            const float wsum = segment_sum<64>(part);
-            const int wave = tid >> 6;
-            float *slot = red + parity * (Cfg::WGS / 64);
-            if ((tid & 63) == 63) slot[wave] = wsum;
-            __syncthreads();
-            if (gl == 0 && row < N) {
-                float tot = 0.f;
+    // Issue-first ring of E = D + 1 row buffers, as in qgemv_small_kernel.
+    constexpr int E = D + 1;
+    uint32_t xp[64];
+    int e = 0;
+    RowBuf ring[E];
+    if (lds_x) {
+        XStage<4> st;  // 4G <= 4 * blockDim (T >= G, blockDim >= T)
+        xstage_issue<4>(x, G, st);
 #pragma unroll
-                for (int i = 0; i < Cfg::WAVES_PER_TEAM; ++i) tot += slot[team * Cfg::WAVES_PER_TEAM + i];
-                y[row] = tot;
-            }
-            parity ^= 1;
+        for (int d = 0; d < D; ++d) load_row(packed, scales, row0 + d * stride, N, W, G, g_load, ring[d]);
+        xstage_convert<4>(st, G, smem);
+        __syncthreads();
+        xstage_fetch(smem, G, gl, lane_on, xp, e);
+        __syncthreads();  // LDS is reused for the half sums below
+    } else {
+#pragma unroll
+        for (int d = 0; d < D; ++d) load_row(packed, scales, row0 + d * stride, N, W, G, g_load, ring[d]);
+        xstage_lane(x, gl, lane_on, xp, e);
+    }
+    const uint32_t magic = magic_vgpr();
+
+    float *red = reinterpret_cast<float *>(smem);  // [2][E][wgs/32]
+    int parity = 0;
+    for (int64_t base = (int64_t)blockIdx.x * R; base < N; base += E * stride) {  // WG-uniform
+        const int64_t row = base + team;
+        float *slot = red + parity * E * (wgs / 32);
+#pragma unroll
+        for (int i = 0; i < E; ++i) {
+            const int64_t r = row + i * stride;
+            load_row(packed, scales, r + D * stride, N, W, G, g_load, ring[(i + D) % E]);
+            __builtin_amdgcn_sched_barrier(0);
+            const float part = row_partial(ring[i], xp, e, magic);
+            const float hs = segment_sum<32>(part);
+            if ((tid & 31) == 31) slot[i * (wgs / 32) + (tid >> 5)] = hs;
         }
-        a0 = b0;
-        a1 = b1;
-        a2 = b2;
-        sa = sb;
-        row += stride;
+        // Half sums written (lgkmcnt) before the barrier; global loads stay in
+        // flight (a __syncthreads fence would wait for them too).
+        lds_barrier();
+        if (gl == 0) {
+#pragma unroll
+            for (int i = 0; i < E; ++i) {
+                const int64_t r = row + i * stride;
+                if (r < N) {
+                    float tot = 0.f;
+                    for (int h = 0; h < halves; ++h) tot += slot[i * (wgs / 32) + team * halves + h];
+                    y[r] = tot;
+                }
+            }
+        }
+        parity ^= 1;
     }
 }
 
@@ -467,13 +638,14 @@ __global__ __launch_bounds__(256) void qgemm_mfma_kernel(const uint4 *__restrict
     f4_t acc[MT];
 #pragma unroll
     for (int t = 0; t < MT; ++t) acc[t] = f4_t{0.f, 0.f, 0.f, 0.f};
+    const uint32_t magic = magic_vgpr();
 
     for (int g = 0; g < G; ++g) {
         const uint32_t *wp = wrow + (int64_t)g * kWordsPerGroup;
         const uint32_t w0 = wp[0], w1 = wp[1], w2 = wp[2];
         const float s = bf16_to_f32(srow[g]);
         h2_t q[16];
-        decode_block(w0, w1, w2, q);
+        decode_block(w0, w1, w2, magic, q);
         h8_t bop[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t)
@@ -560,66 +732,88 @@ qw3_status fill_zero(float *y, int64_t n, hipStream_t stream) {
     return check_launch();
 }
 
-// LDS bytes of the x-stationary GEMV: fp16 pairs + exponents, or the
-// cross-wave reduction slots, whichever is larger.
-size_t gemv_lds_bytes(int G, int wgs, bool lds_x) {
-    const size_t red = 2 * (size_t)(wgs / 64) * sizeof(float);
-    const size_t xs = lds_x ? (size_t)G * 64 * 4 + (size_t)G * 4 : 0;
-    return xs > red ? xs : red;
+// Workgroups of `kernel` that fit on one CU at `wgs` threads and `lds` bytes.
+qw3_status blocks_per_cu(const void *kernel, int wgs, size_t lds, int *out) {
+    int nb = 0;
+    const hipError_t err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, wgs, lds);
+    if (err != hipSuccess) return hip_fail(err);
+    *out = nb > 0 ? nb : 1;
+    return QW3_OK;
 }
 
-constexpr size_t kMaxLdsX = 64 * 1024;
-
+#ifndef QW3_GEMV_BPC
+#define QW3_GEMV_BPC 1
+#endif
 template <int T>
-qw3_status launch_gemv_t(const uint16_t *x, const uint32_t *packed, const uint16_t *scales, float *y,
-                         int64_t N, int G, hipStream_t stream) {
-    using Cfg = GemvCfg<T>;
-    int cus = 0;
+qw3_status launch_gemv_small(const uint16_t *x, const uint32_t *packed, const uint16_t *scales, float *y,
+                             int64_t N, int G, hipStream_t stream) {
+    constexpr int R = kGemvWGS / T;
+    const size_t xs_bytes = (size_t)G * 64 * 4 + (size_t)G * 4;
+    const bool lds_x = xs_bytes <= kMaxLdsX;
+    const size_t lds = lds_x ? xs_bytes : 0;
+    const void *kern = reinterpret_cast<const void *>(&qgemv_small_kernel<T>);
+    int cus = 0, per_cu = 0;
     qw3_status st = cu_count(&cus);
+    if (st == QW3_OK) st = blocks_per_cu(kern, kGemvWGS, lds, &per_cu);
     if (st != QW3_OK) return st;
-    const bool lds_x = (size_t)G * 64 * 4 + (size_t)G * 4 <= kMaxLdsX;
-    const size_t lds = gemv_lds_bytes(G, Cfg::WGS, lds_x);
-    // Two resident workgroups per CU is what the register and LDS budget of
-    // this kernel allows at up to 512 threads; more blocks only add tail.
-    const int per_cu = Cfg::WGS <= 512 ? 2 : 1;
-    int64_t blocks = ceil_div(N, Cfg::R);
+    if (QW3_GEMV_BPC > 0 && per_cu > QW3_GEMV_BPC) per_cu = QW3_GEMV_BPC;
+    int64_t blocks = ceil_div(N, R);
     if (blocks > (int64_t)cus * per_cu) blocks = (int64_t)cus * per_cu;
-    if (lds_x)
-        hipLaunchKernelGGL((qgemv_kernel<T, true>), dim3((unsigned)blocks), dim3(Cfg::WGS), lds, stream, x,
-                           packed, scales, y, N, G);
+    hipLaunchKernelGGL(qgemv_small_kernel<T>, dim3((unsigned)blocks), dim3(kGemvWGS), lds, stream, x, packed,
+                       scales, y, N, G, lds_x ? 1 : 0);
+    return check_launch();
+}
+
+qw3_status launch_gemv_big(const uint16_t *x, const uint32_t *packed, const uint16_t *scales, float *y,
+                           int64_t N, int G, hipStream_t stream) {
+    // Team of T >= G lanes, T a multiple of 32; the workgroup holds whole
+    // waves and at most 1024 threads (T <= 1024 since K <= QW3_MAX_K).
+    int T = 32 * ((G + 31) / 32);
+    int R = T >= 512 ? 1 : 512 / T;
+    int wgs = T * R;
+    if (wgs % 64 != 0) {
+        if (2 * wgs <= 1024) {
+            R *= 2;
+            wgs *= 2;
+        } else {
+            T = 64 * ((G + 63) / 64);
+            R = 1;
+            wgs = T;
+        }
+    }
+    const size_t xs_bytes = (size_t)G * 64 * 4 + (size_t)G * 4;
+    const bool lds_x = xs_bytes <= kMaxLdsX;
+    constexpr int kBigD = kGemvDepth, kHugeD = 1;
+    const size_t red_bytes = 2 * (size_t)((wgs <= 512 ? kBigD : kHugeD) + 1) * (wgs / 32) * sizeof(float);
+    const size_t lds = (lds_x && xs_bytes > red_bytes) ? xs_bytes : red_bytes;
+    const void *kern = wgs <= 512 ? reinterpret_cast<const void *>(&qgemv_big_kernel<512, kBigD>)
+                                  : reinterpret_cast<const void *>(&qgemv_big_kernel<1024, kHugeD>);
+    int cus = 0, per_cu = 0;
+    qw3_status st = cu_count(&cus);
+    if (st == QW3_OK) st = blocks_per_cu(kern, wgs, lds, &per_cu);
+    if (st != QW3_OK) return st;
+    int64_t blocks = ceil_div(N, R);
+    if (blocks > (int64_t)cus * per_cu) blocks = (int64_t)cus * per_cu;
+    if (wgs <= 512)
+        hipLaunchKernelGGL((qgemv_big_kernel<512, kBigD>), dim3((unsigned)blocks), dim3(wgs), lds, stream, x, packed, scales,
+                           y, N, G, T, lds_x ? 1 : 0);
     else
-        hipLaunchKernelGGL((qgemv_kernel<T, false>), dim3((unsigned)blocks), dim3(Cfg::WGS), lds, stream, x,
-                           packed, scales, y, N, G);
+        hipLaunchKernelGGL((qgemv_big_kernel<1024, kHugeD>), dim3((unsigned)blocks), dim3(wgs), lds, stream, x, packed,
+                           scales, y, N, G, T, lds_x ? 1 : 0);
     return check_launch();
 }
 
 qw3_status launch_gemv(const uint16_t *x, const uint32_t *packed, const uint16_t *scales, float *y,
                        int64_t N, int64_t K, hipStream_t stream) {
     const int G = (int)(K / kGroup);
-    if (G <= 1) return launch_gemv_t<1>(x, packed, scales, y, N, G, stream);
-    if (G <= 2) return launch_gemv_t<2>(x, packed, scales, y, N, G, stream);
-    if (G <= 4) return launch_gemv_t<4>(x, packed, scales, y, N, G, stream);
-    if (G <= 8) return launch_gemv_t<8>(x, packed, scales, y, N, G, stream);
-    if (G <= 16) return launch_gemv_t<16>(x, packed, scales, y, N, G, stream);
-    if (G <= 32) return launch_gemv_t<32>(x, packed, scales, y, N, G, stream);
-    if (G <= 64) return launch_gemv_t<64>(x, packed, scales, y, N, G, stream);
-    switch ((G + 63) / 64) {
-        case 2: return launch_gemv_t<128>(x, packed, scales, y, N, G, stream);
-        case 3: return launch_gemv_t<192>(x, packed, scales, y, N, G, stream);
-        case 4: return launch_gemv_t<256>(x, packed, scales, y, N, G, stream);
-        case 5: return launch_gemv_t<320>(x, packed, scales, y, N, G, stream);
-        case 6: return launch_gemv_t<384>(x, packed, scales, y, N, G, stream);
-        case 7: return launch_gemv_t<448>(x, packed, scales, y, N, G, stream);
-        case 8: return launch_gemv_t<512>(x, packed, scales, y, N, G, stream);
-        case 9: return launch_gemv_t<576>(x, packed, scales, y, N, G, stream);
-        case 10: return launch_gemv_t<640>(x, packed, scales, y, N, G, stream);
-        case 11: return launch_gemv_t<704>(x, packed, scales, y, N, G, stream);
-        case 12: return launch_gemv_t<768>(x, packed, scales, y, N, G, stream);
-        case 13: return launch_gemv_t<832>(x, packed, scales, y, N, G, stream);
-        case 14: return launch_gemv_t<896>(x, packed, scales, y, N, G, stream);
-        case 15: return launch_gemv_t<960>(x, packed, scales, y, N, G, stream);
-        default: return launch_gemv_t<1024>(x, packed, scales, y, N, G, stream);
-    }
+    if (G <= 1) return launch_gemv_small<1>(x, packed, scales, y, N, G, stream);
+    if (G <= 2) return launch_gemv_small<2>(x, packed, scales, y, N, G, stream);
+    if (G <= 4) return launch_gemv_small<4>(x, packed, scales, y, N, G, stream);
+    if (G <= 8) return launch_gemv_small<8>(x, packed, scales, y, N, G, stream);
+    if (G <= 16) return launch_gemv_small<16>(x, packed, scales, y, N, G, stream);
+    if (G <= 32) return launch_gemv_small<32>(x, packed, scales, y, N, G, stream);
+    if (G <= 64) return launch_gemv_small<64>(x, packed, scales, y, N, G, stream);
+    return launch_gemv_big(x, packed, scales, y, N, G, stream);
 }
 
 // Small-M path: convert x once into scratch, then one streaming pass over W
