@@ -680,6 +680,168 @@ __global__ __launch_bounds__(256) void qgemm_mfma_kernel(const uint4 *__restrict
         }
 }
 
+// ------------------------------------------ batched decode, K-split, LDS DMA --
+// y[m][n] for up to 16 tokens at once, rows of 64 groups (K = 8192).  The 8
+// waves of a workgroup split the groups of a row (wave w owns groups 8w..8w+7)
+// and keep the A operands of those groups (x' of the 16 tokens, 128 VGPRs)
+// for the whole kernel, so activations are read once per workgroup.  The
+// workgroup walks 16-row tiles; each tile's packed words (48 KB) are copied
+// into LDS with global_load_lds_dwordx4 -- 1 KB contiguous per instruction,
+// issued one tile ahead into the other of two slots -- with row pitches of
+// 3088 bytes so that the 64 lanes' reads of (row l%16, block l/16) fall in
+// distinct banks.  Per group: decode (the B operand), 4 MFMAs, then
+// D[m][n] * 2^e[g][m] * s[n][g] into the accumulator.  At the end of a tile
+// each wave leaves its 16 x 16 partial sums in LDS; after the tile barrier one
+// wave (rotating) adds the 8 partials in wave order and stores y.
+// LDS reads and writes inside the loop are asm blocks that wait for
+// themselves: the compiler would otherwise drain every LDS DMA in flight
+// before each one (it cannot tell the ring slots apart).
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void gbl_void_t;
+
+// s_waitcnt immediate that constrains vmcnt only (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+constexpr int kBdWaves = 8;
+constexpr int kBdG = 64;
+constexpr int kBdGPW = kBdG / kBdWaves;
+constexpr int kBdRowBytes = kBdG * 48;
+constexpr int kBdRowPitch = kBdRowBytes + 16;
+constexpr int kBdSlotBytes = 16 * kBdRowPitch;
+constexpr int kBdRedBytes = kBdWaves * 64 * 16;
+constexpr size_t kBdLds = 2 * (size_t)kBdSlotBytes + 2 * (size_t)kBdRedBytes;
+constexpr int kBdDmaPerWave = 16 * (kBdRowBytes / 1024) / kBdWaves;
+static_assert(kBdDmaPerWave * kBdWaves == 16 * (kBdRowBytes / 1024), "tile loads must split evenly");
+static_assert(kBdLds <= 160 * 1024, "LDS budget");
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char *)p;
+}
+
+// The lane's 3 words (block j of one row's group) from a tile slot.
+__device__ __forceinline__ void bd_read_words(uint32_t addr, uint32_t &w0, uint32_t &w1, uint32_t &w2) {
+    asm volatile(
+        "ds_read_b32 %0, %3\n\t"
+        "ds_read_b32 %1, %3 offset:4\n\t"
+        "ds_read_b32 %2, %3 offset:8\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(w0), "=&v"(w1), "=&v"(w2)
+        : "v"(addr)
+        : "memory");
+}
+
+__device__ __forceinline__ void bd_write_partial(uint32_t addr, f4_t v) {
+    asm volatile("ds_write_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : : "v"(addr), "v"(v) : "memory");
+}
+
+__device__ __forceinline__ f4_t bd_read_partial(uint32_t addr) {
+    f4_t v;
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(addr) : "memory");
+    return v;
+}
+
+__global__ __launch_bounds__(512) void qgemm_bd_kernel(const uint4 *__restrict__ xq, const int16_t *__restrict__ xe,
+                                                     const uint32_t *__restrict__ packed,
+                                                     const uint16_t *__restrict__ scales, float *__restrict__ y,
+                                                     int M, int64_t N, int64_t y_ld) {
+    constexpr int Mp = 16;
+    extern __shared__ __align__(16) unsigned char lds[];
+    unsigned char *slots = lds;
+    unsigned char *red = lds + 2 * (size_t)kBdSlotBytes;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n = lane & 15;  // B column (weight row of the tile); also the A row (token) this lane loads
+    const int j = lane >> 4;  // 32-code block of the group
+    const int g0 = wave * kBdGPW;
+    const int64_t tiles = (N + 15) / 16;
+    const int64_t my_tiles = (tiles - (int64_t)blockIdx.x + gridDim.x - 1) / gridDim.x;  // >= 1
+    const unsigned char *pbytes = reinterpret_cast<const unsigned char *>(packed);
+
+    h8_t xa[kBdGPW][4];
+    float f[kBdGPW][4];
+#pragma unroll
+    for (int gi = 0; gi < kBdGPW; ++gi) {
+        const uint4 *ap = xq + ((((int64_t)(g0 + gi) * Mp + n) * 4 + j) * 4);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) xa[gi][u] = __builtin_bit_cast(h8_t, ap[u]);
+        const int16_t *ep = xe + (int64_t)(g0 + gi) * Mp + 4 * j;  // D rows 4j..4j+3 are tokens
+#pragma unroll
+        for (int r = 0; r < 4; ++r) f[gi][r] = ldexpf(1.f, (int)ep[r]);
+    }
+
+    auto dma_tile = [&](int64_t t, int slot) {
+        const int64_t r0 = ((int64_t)blockIdx.x + t * gridDim.x) * 16;
+        unsigned char *sb = slots + (size_t)slot * kBdSlotBytes;
+#pragma unroll
+        for (int i = 0; i < kBdDmaPerWave; ++i) {
+            const int idx = wave + kBdWaves * i;
+            const int row = idx / 3, c = idx - 3 * (idx / 3);
+            int64_t gr = r0 + row;
+            gr = gr < N ? gr : N - 1;
+            const unsigned char *src = pbytes + gr * kBdRowBytes + c * 1024 + lane * 16;
+            __builtin_amdgcn_global_load_lds((gbl_void_t *)src, (lds_void_t *)(sb + row * kBdRowPitch + c * 1024),
+                                             16, 0, 0);
+        }
+    };
+    auto load_scales = [&](int64_t t) {
+        int64_t gr = ((int64_t)blockIdx.x + t * gridDim.x) * 16 + n;
+        gr = gr < N ? gr : N - 1;
+        return *reinterpret_cast<const uint4 *>(scales + gr * kBdG + g0);
+    };
+    auto reduce_store = [&](int64_t t) {
+        const unsigned char *rb = red + (size_t)(t & 1) * kBdRedBytes;
+        f4_t tot = bd_read_partial(lds_addr(rb + lane * 16));
+#pragma unroll
+        for (int w = 1; w < kBdWaves; ++w) tot += bd_read_partial(lds_addr(rb + w * 1024 + lane * 16));
+        const int64_t row = ((int64_t)blockIdx.x + t * gridDim.x) * 16 + n;
+        if (row < N) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (4 * j + r < M) y[(int64_t)(4 * j + r) * y_ld + row] = tot[r];
+        }
+    };
+
+    dma_tile(0, 0);
+    uint4 sc_next = load_scales(0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    lds_barrier();
+    const uint32_t magic = magic_vgpr();
+    for (int64_t t = 0; t < my_tiles; ++t) {
+        const uint4 sc = sc_next;
+        if (t + 1 < my_tiles) {
+            dma_tile(t + 1, (int)((t + 1) & 1));
+            sc_next = load_scales(t + 1);
+        }
+        if (t > 0 && wave == (int)((t - 1) % kBdWaves)) reduce_store(t - 1);
+        const unsigned char *sb = slots + (size_t)(t & 1) * kBdSlotBytes + n * kBdRowPitch + 12 * j;
+        const uint32_t scw[4] = {sc.x, sc.y, sc.z, sc.w};
+        f4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int gi = 0; gi < kBdGPW; ++gi) {
+            uint32_t w0, w1, w2;
+            bd_read_words(lds_addr(sb + (g0 + gi) * 48), w0, w1, w2);
+            h2_t q[16];
+            decode_block(w0, w1, w2, magic, q);
+            f4_t d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const h8_t bop = {q[4 * u].x, q[4 * u].y, q[4 * u + 1].x, q[4 * u + 1].y,
+                                  q[4 * u + 2].x, q[4 * u + 2].y, q[4 * u + 3].x, q[4 * u + 3].y};
+                d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[gi][u], bop, d, 0, 0, 0);
+            }
+            const uint32_t sw = scw[gi >> 1];
+            const float sv = __uint_as_float((gi & 1) ? (sw & 0xFFFF0000u) : (sw << 16));
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] = fmaf(d[r] * f[gi][r], sv, acc[r]);
+        }
+        bd_write_partial(lds_addr(red + (size_t)(t & 1) * kBdRedBytes + wave * 1024 + lane * 16), acc);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's loads of tile t + 1 have landed
+        lds_barrier();
+    }
+    if (wave == (int)((my_tiles - 1) % kBdWaves)) reduce_store(my_tiles - 1);
+}
+
 __global__ __launch_bounds__(256) void fill_zero_kernel(float *__restrict__ y, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i < n) y[i] = 0.f;
@@ -816,11 +978,50 @@ qw3_status launch_gemv(const uint16_t *x, const uint32_t *packed, const uint16_t
     return launch_gemv_big(x, packed, scales, y, N, G, stream);
 }
 
+// Batched decode for rows of 64 groups: passes of 16 tokens, each one
+// conversion launch and one streaming pass over W.
+qw3_status launch_gemm_bd(const uint16_t *x, const uint32_t *packed, const uint16_t *scales, float *y,
+                          int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+    constexpr int Mp = 16;
+    const int G = (int)(K / kGroup);
+    const size_t xq_bytes = (size_t)Mp * (size_t)K * 2;
+    const size_t xe_bytes = (size_t)G * Mp * sizeof(int16_t);
+    int cus = 0, per_cu = 0;
+    qw3_status st = cu_count(&cus);
+    if (st == QW3_OK)
+        st = blocks_per_cu(reinterpret_cast<const void *>(&qgemm_bd_kernel), 64 * kBdWaves, kBdLds, &per_cu);
+    if (st != QW3_OK) return st;
+    void *scratch = nullptr;
+    hipError_t err = hipMallocAsync(&scratch, xq_bytes + xe_bytes, stream);
+    if (err != hipSuccess) return hip_fail(err);
+    uint4 *xq = reinterpret_cast<uint4 *>(scratch);
+    int16_t *xe = reinterpret_cast<int16_t *>(static_cast<char *>(scratch) + xq_bytes);
+    const int64_t tiles = ceil_div(N, 16);
+    int64_t blocks = (int64_t)cus * per_cu;
+    if (blocks > tiles) blocks = tiles;
+    for (int64_t m0 = 0; m0 < M && st == QW3_OK; m0 += Mp) {
+        const int mc = (int)(M - m0 < Mp ? M - m0 : Mp);
+        const int64_t units = (int64_t)G * Mp * 4;
+        hipLaunchKernelGGL(prep_x_kernel, dim3((unsigned)ceil_div(units, 256)), dim3(256), 0, stream, x + m0 * K, xq,
+                           xe, mc, Mp, K, G);
+        st = check_launch();
+        if (st != QW3_OK) break;
+        hipLaunchKernelGGL(qgemm_bd_kernel, dim3((unsigned)blocks), dim3(64 * kBdWaves), kBdLds, stream, xq, xe,
+                           packed, scales, y + m0 * N, mc, N, N);
+        st = check_launch();
+    }
+    err = hipFreeAsync(scratch, stream);
+    if (st == QW3_OK && err != hipSuccess) st = hip_fail(err);
+    return st;
+}
+
 // Small-M path: convert x once into scratch, then one streaming pass over W
 // per chunk of up to 32 tokens.
 qw3_status launch_gemm_small(const uint16_t *x, const uint32_t *packed, const uint16_t *scales, float *y,
                              int64_t M, int64_t N, int64_t K, hipStream_t stream) {
     const int G = (int)(K / kGroup);
+    if (G == kBdG && (reinterpret_cast<uintptr_t>(scales) & 15) == 0)
+        return launch_gemm_bd(x, packed, scales, y, M, N, K, stream);
     const int mchunk = M > 16 ? 32 : 16;
     const size_t xq_bytes = (size_t)mchunk * (size_t)K * 2;
     const size_t xe_bytes = (size_t)G * mchunk * sizeof(int16_t);
