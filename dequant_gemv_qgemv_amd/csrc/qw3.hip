@@ -842,6 +842,247 @@ __global__ __launch_bounds__(512) void qgemm_bd_kernel(const uint4 *__restrict__
     if (wave == (int)((my_tiles - 1) % kBdWaves)) reduce_store(my_tiles - 1);
 }
 
+// --------------------------------------------------- prefill (large M) tiles --
+// Many tokens: an MFMA GEMM whose B tiles are decoded on the fly.  Because a
+// decoded weight is reused by every token of the tile, the group scale is
+// folded into the decoded value instead of being applied per group after the
+// MFMAs: B = (c-4) * 2^p * s * 2^-E[n], exact in fp16 (3 + 8 significant
+// bits) with E[n] chosen per row so that the row's largest scale maps to
+// [8, 16).  A = x * 2^-(E[m] + p) in fp16 with one exponent per token (largest
+// |x| of the token maps to [2^14, 2^15); exact down to 2^-28 of it).  The
+// accumulators then hold sum_k x w * 2^-(E[m] + E[n]), rescaled once at the
+// end.  Tiles are 128 tokens x 128 rows x one group (128 k) per step, double
+// buffered in LDS; each wave owns 64 x 64 of the output (16 MFMA tiles).
+// LDS rows (256 bytes = 16 chunks of 16 bytes) are stored with chunk index
+// XOR (row & 15) so that the 16 lanes of a quarter-wave reading one chunk of
+// 16 consecutive rows hit 16 different bank groups.
+
+// Per token: E[m] and x' = x * 2^-(E[m] + p) in block pair order, zero rows
+// for m >= M.  One workgroup per token.
+__global__ __launch_bounds__(256) void prep_tile_x_kernel(const uint16_t *__restrict__ x, uint32_t *__restrict__ xq,
+                                                          int *__restrict__ xe, int M, int64_t K) {
+    __shared__ uint32_t wmax[4];
+    const int m = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int64_t units = K / 32;
+    uint32_t *dst = xq + (int64_t)m * (K / 2);
+    if (m >= M) {
+        for (int64_t u = tid; u < units; u += 256) {
+            uint4 *d4 = reinterpret_cast<uint4 *>(dst + u * 16);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) d4[i] = make_uint4(0, 0, 0, 0);
+        }
+        if (tid == 0) xe[m] = 0;
+        return;
+    }
+    const uint16_t *src = x + (int64_t)m * K;
+    uint32_t mx = 0;
+    for (int64_t u = tid; u < units; u += 256) {
+        uint4 xb[4];
+        load_x32(src + u * 32, xb);
+        mx = max(mx, absmax32(xb));
+    }
+    for (int off = 32; off >= 1; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off));
+    if ((tid & 63) == 0) wmax[tid >> 6] = mx;
+    __syncthreads();
+    mx = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+    const int e = group_exponent(mx);
+    for (int64_t u = tid; u < units; u += 256) {
+        uint4 xb[4];
+        load_x32(src + u * 32, xb);
+        uint32_t out[16];
+        convert_block(xb, e, out);
+        uint4 *d4 = reinterpret_cast<uint4 *>(dst + u * 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) d4[i] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
+    }
+    if (tid == 0) xe[m] = e;
+}
+
+constexpr int kTileBM = 128;
+constexpr int kTileBN = 128;
+constexpr int kTileRow = 256;  // bytes of one row of one group (128 fp16)
+constexpr size_t kTileStage = (size_t)(kTileBM + kTileBN) * kTileRow;
+constexpr size_t kTileLds = 2 * kTileStage + (size_t)kTileBN * 4;
+
+__device__ __forceinline__ int tile_off(int row, int chunk) { return row * kTileRow + ((chunk ^ (row & 15)) << 4); }
+
+// One pipeline stage of the tile GEMM held in registers: this thread's share
+// of a group's activations (8 x 16 B) and of its packed words and scales
+// (two 12-byte blocks).
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+struct TileStage {
+    u32x4_t a[8];  // native vector type: stays in registers (HIP's uint4 struct copies did not)
+    uint32_t w[6];
+    uint32_t s[2];
+};
+
+__device__ __forceinline__ void tile_load(TileStage &st, const uint32_t *a_src, const uint32_t *const (&b_w)[2],
+                                          const uint16_t *const (&b_s)[2], int g) {
+    const u32x4_t *ap = reinterpret_cast<const u32x4_t *>(a_src + (int64_t)g * 64);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st.a[i] = ap[i];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t *wp = b_w[h] + (int64_t)g * kWordsPerGroup;
+        st.w[3 * h] = wp[0];
+        st.w[3 * h + 1] = wp[1];
+        st.w[3 * h + 2] = wp[2];
+        st.s[h] = b_s[h][g];
+    }
+}
+
+// Activations as they are; weights decoded to (c-4) * 2^p * s * 2^-E[row].
+__device__ __forceinline__ void tile_store(const TileStage &st, unsigned char *sa, int a_row, int a_half, int tid,
+                                           int b_blk, const int (&b_e)[2], uint32_t magic) {
+    unsigned char *sb = sa + (size_t)kTileBM * kTileRow;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4_t *>(sa + tile_off(a_row, a_half * 8 + i)) = st.a[i];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        h2_t q[16];
+        decode_block(st.w[3 * h], st.w[3 * h + 1], st.w[3 * h + 2], magic, q);
+        const _Float16 sv = (_Float16)ldexpf(bf16_to_f32(st.s[h]), -b_e[h]);
+        const h2_t s2 = {sv, sv};
+        const int rl = h * 64 + (tid >> 2);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const uint4 v = make_uint4(__builtin_bit_cast(uint32_t, q[4 * c] * s2),
+                                       __builtin_bit_cast(uint32_t, q[4 * c + 1] * s2),
+                                       __builtin_bit_cast(uint32_t, q[4 * c + 2] * s2),
+                                       __builtin_bit_cast(uint32_t, q[4 * c + 3] * s2));
+            *reinterpret_cast<uint4 *>(sb + tile_off(rl, 4 * b_blk + c)) = v;
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void qgemm_tile_kernel(const uint32_t *__restrict__ xq, const int *__restrict__ xe,
+                                                       const uint32_t *__restrict__ packed,
+                                                       const uint16_t *__restrict__ scales, float *__restrict__ y,
+                                                       int M, int MT, int64_t N, int G) {
+    extern __shared__ __align__(16) unsigned char lds[];
+    int *En = reinterpret_cast<int *>(lds + 2 * kTileStage);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave & 1, wn = wave >> 1;
+    // Token-tile major: the workgroups in flight together share one token
+    // tile, which then stays in each XCD's L2 while the weight tiles stream.
+    const int64_t NT = (N + kTileBN - 1) / kTileBN;
+    const int m_tile = (int)(blockIdx.x / NT);
+    const int64_t n_tile = blockIdx.x - (int64_t)m_tile * NT;
+    const int64_t n0 = n_tile * kTileBN;
+    const int m0 = m_tile * kTileBM;
+    const int64_t K = (int64_t)G * kGroup;
+    const int64_t W = (int64_t)G * kWordsPerGroup;
+
+    // Row exponents: the largest scale of each row maps to [8, 16).
+    if (tid < kTileBN) {
+        int64_t r = n0 + tid;
+        r = r < N ? r : N - 1;
+        uint32_t mx = 0;
+        for (int g = 0; g < G; ++g) mx = max(mx, (uint32_t)scales[r * G + g] & 0x7FFFu);
+        En[tid] = __builtin_amdgcn_frexp_expf(bf16_to_f32(mx)) - 4;
+    }
+    __syncthreads();
+
+    // Loader roles.  A: token tid/2, 64 fp16 (half a group row) = 8 x 16 B.
+    // B: rows tid/4 and 64 + tid/4, block tid%4 (12 bytes each).
+    const int a_row = tid >> 1, a_half = tid & 1;
+    const uint32_t *a_src = xq + (int64_t)(m0 + a_row) * (K / 2) + a_half * 32;
+    const int b_blk = tid & 3;
+    int64_t b_r[2];
+    int b_e[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int rl = h * 64 + (tid >> 2);
+        int64_t r = n0 + rl;
+        b_r[h] = r < N ? r : N - 1;
+        b_e[h] = En[rl];
+    }
+    // Register ring of 3 stages: the operands of group g + 2 are loaded while
+    // group g is multiplied and group g + 1 is decoded into LDS, so two steps
+    // of latency are hidden.  Loads are unconditional (clamped to the last
+    // group) and the barrier waits for LDS only, so the loads stay in flight.
+    TileStage ring0, ring1, ring2;
+    const uint32_t *b_w[2] = {packed + b_r[0] * W + 3 * b_blk, packed + b_r[1] * W + 3 * b_blk};
+    const uint16_t *b_s[2] = {scales + b_r[0] * G, scales + b_r[1] * G};
+    const uint32_t magic = magic_vgpr();
+#define QW3_RING(k_) ((k_) == 0 ? ring0 : ((k_) == 1 ? ring1 : ring2))
+#define QW3_TILE_LOAD(k_, g_) tile_load(QW3_RING(k_), a_src, b_w, b_s, (g_))
+#define QW3_TILE_STORE(k_, buf_) \
+    tile_store(QW3_RING(k_), lds + (size_t)(buf_) * kTileStage, a_row, a_half, tid, b_blk, b_e, magic)
+
+    f4_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) acc[i][jj] = f4_t{0.f, 0.f, 0.f, 0.f};
+
+    const int lr = lane & 15, lc = lane >> 4;
+    auto mfma_group = [&](int buf) {
+        const unsigned char *sa = lds + (size_t)buf * kTileStage;
+        const unsigned char *sb = sa + (size_t)kTileBM * kTileRow;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            h8_t av[4], bv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                av[i] = *reinterpret_cast<const h8_t *>(sa + tile_off(wm * 64 + 16 * i + lr, 4 * ks + lc));
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                bv[jj] = *reinterpret_cast<const h8_t *>(sb + tile_off(wn * 64 + 16 * jj + lr, 4 * ks + lc));
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[i], bv[jj], acc[i][jj], 0, 0, 0);
+        }
+    };
+
+    QW3_TILE_LOAD(0, 0);
+    QW3_TILE_LOAD(1, (1 < G ? 1 : G - 1));
+    QW3_TILE_STORE(0, 0);
+    lds_barrier();
+    // Step g: load g + 2 into slot (g + 2) % 3, multiply buffer g % 2, decode
+    // slot (g + 1) % 3 into buffer (g + 1) % 2, barrier.  Unrolled by 3 so the
+    // slots are static; steps past the last group only keep the pipeline shape.
+#define QW3_TILE_STEP(u_)                                                                       \
+    do {                                                                                        \
+        const int g_ = g + (u_);                                                                \
+        const int gl_ = g_ + 2 < G ? g_ + 2 : G - 1;                                            \
+        QW3_TILE_LOAD(((u_) + 2) % 3, gl_);                                                     \
+        if (g_ < G) mfma_group(g_ & 1);                                                         \
+        QW3_TILE_STORE(((u_) + 1) % 3, (g_ + 1) & 1);                                           \
+        lds_barrier();                                                                          \
+    } while (0)
+    for (int g = 0; g < G; g += 3) {
+        QW3_TILE_STEP(0);
+        QW3_TILE_STEP(1);
+        QW3_TILE_STEP(2);
+    }
+#undef QW3_TILE_STEP
+
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+        const int nl = wn * 64 + 16 * jj + lr;
+        const int64_t row = n0 + nl;
+        const int en = En[nl];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int tok = m0 + wm * 64 + 16 * i + 4 * lc + r;
+                if (tok < M && row < N) y[(int64_t)tok * N + row] = ldexpf(acc[i][jj][r], en + xe[tok]);
+            }
+        }
+    }
+}
+#undef QW3_TILE_LOAD
+#undef QW3_TILE_STORE
+#undef QW3_RING
+
 __global__ __launch_bounds__(256) void fill_zero_kernel(float *__restrict__ y, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i < n) y[i] = 0.f;
@@ -978,6 +1219,32 @@ qw3_status launch_gemv(const uint16_t *x, const uint32_t *packed, const uint16_t
     return launch_gemv_big(x, packed, scales, y, N, G, stream);
 }
 
+// Prefill: convert x once (per-token exponent), then one tile GEMM launch.
+qw3_status launch_gemm_tile(const uint16_t *x, const uint32_t *packed, const uint16_t *scales, float *y,
+                            int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+    const int G = (int)(K / kGroup);
+    const int MT = (int)ceil_div(M, kTileBM);
+    const int64_t Mp = (int64_t)MT * kTileBM;
+    const size_t xq_bytes = (size_t)Mp * (size_t)K * 2;
+    const size_t xe_bytes = (size_t)Mp * sizeof(int);
+    void *scratch = nullptr;
+    hipError_t err = hipMallocAsync(&scratch, xq_bytes + xe_bytes, stream);
+    if (err != hipSuccess) return hip_fail(err);
+    uint32_t *xq = reinterpret_cast<uint32_t *>(scratch);
+    int *xe = reinterpret_cast<int *>(static_cast<char *>(scratch) + xq_bytes);
+    hipLaunchKernelGGL(prep_tile_x_kernel, dim3((unsigned)Mp), dim3(256), 0, stream, x, xq, xe, (int)M, K);
+    qw3_status st = check_launch();
+    if (st == QW3_OK) {
+        const int64_t blocks = ceil_div(N, kTileBN) * MT;
+        hipLaunchKernelGGL(qgemm_tile_kernel, dim3((unsigned)blocks), dim3(256), kTileLds, stream, xq, xe, packed,
+                           scales, y, (int)M, MT, N, G);
+        st = check_launch();
+    }
+    err = hipFreeAsync(scratch, stream);
+    if (st == QW3_OK && err != hipSuccess) st = hip_fail(err);
+    return st;
+}
+
 // Batched decode for rows of 64 groups: passes of 16 tokens, each one
 // conversion launch and one streaming pass over W.
 qw3_status launch_gemm_bd(const uint16_t *x, const uint32_t *packed, const uint16_t *scales, float *y,
@@ -1020,6 +1287,7 @@ qw3_status launch_gemm_bd(const uint16_t *x, const uint32_t *packed, const uint1
 qw3_status launch_gemm_small(const uint16_t *x, const uint32_t *packed, const uint16_t *scales, float *y,
                              int64_t M, int64_t N, int64_t K, hipStream_t stream) {
     const int G = (int)(K / kGroup);
+    if (M > 32) return launch_gemm_tile(x, packed, scales, y, M, N, K, stream);
     if (G == kBdG && (reinterpret_cast<uintptr_t>(scales) & 15) == 0)
         return launch_gemm_bd(x, packed, scales, y, M, N, K, stream);
     const int mchunk = M > 16 ? 32 : 16;
