@@ -681,18 +681,20 @@ __global__ __launch_bounds__(256) void qgemm_mfma_kernel(const uint4 *__restrict
 }
 
 // ------------------------------------------ batched decode, K-split, LDS DMA --
-// y[m][n] for up to 16 tokens at once, rows of 64 groups (K = 8192).  The 8
-// waves of a workgroup split the groups of a row (wave w owns groups 8w..8w+7)
-// and keep the A operands of those groups (x' of the 16 tokens, 128 VGPRs)
-// for the whole kernel, so activations are read once per workgroup.  The
-// workgroup walks 16-row tiles; each tile's packed words (48 KB) are copied
-// into LDS with global_load_lds_dwordx4 -- 1 KB contiguous per instruction,
-// issued one tile ahead into the other of two slots -- with row pitches of
-// 3088 bytes so that the 64 lanes' reads of (row l%16, block l/16) fall in
-// distinct banks.  Per group: decode (the B operand), 4 MFMAs, then
-// D[m][n] * 2^e[g][m] * s[n][g] into the accumulator.  At the end of a tile
-// each wave leaves its 16 x 16 partial sums in LDS; after the tile barrier one
-// wave (rotating) adds the 8 partials in wave order and stores y.
+// y[m][n] for up to 16 tokens at once.  K is cut into C chunks of 8 * GPW
+// groups; a workgroup owns one chunk and a set of 16-row tiles.  Its 8 waves
+// split the chunk (wave w owns GPW consecutive groups) and keep the A
+// operands of those groups (x' of the 16 tokens, 16 * GPW VGPRs) for the whole
+// kernel, so activations are read once per workgroup.  Each tile's packed
+// words for the chunk are copied into LDS with global_load_lds_dwordx4 --
+// 1 KB contiguous per instruction, issued one tile ahead into the other of
+// two slots -- with row pitches chosen so that the 64 lanes' reads of
+// (row l%16, block l/16) fall in distinct banks.  Per group: decode (the B
+// operand), 4 MFMAs, then D[m][n] * 2^e[g][m] * s[n][g] into the accumulator.
+// At the end of a tile each wave leaves its 16 x 16 partial sums in LDS;
+// after the tile barrier one wave (rotating) adds the 8 partials in wave
+// order and stores them: to y when C == 1, else to chunk-major partial sums
+// that qgemm_chunk_sum_kernel adds in chunk order.
 // LDS reads and writes inside the loop are asm blocks that wait for
 // themselves: the compiler would otherwise drain every LDS DMA in flight
 // before each one (it cannot tell the ring slots apart).
@@ -704,16 +706,20 @@ typedef __attribute__((address_space(1))) const void gbl_void_t;
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 constexpr int kBdWaves = 8;
-constexpr int kBdG = 64;
-constexpr int kBdGPW = kBdG / kBdWaves;
-constexpr int kBdRowBytes = kBdG * 48;
-constexpr int kBdRowPitch = kBdRowBytes + 16;
-constexpr int kBdSlotBytes = 16 * kBdRowPitch;
 constexpr int kBdRedBytes = kBdWaves * 64 * 16;
-constexpr size_t kBdLds = 2 * (size_t)kBdSlotBytes + 2 * (size_t)kBdRedBytes;
-constexpr int kBdDmaPerWave = 16 * (kBdRowBytes / 1024) / kBdWaves;
-static_assert(kBdDmaPerWave * kBdWaves == 16 * (kBdRowBytes / 1024), "tile loads must split evenly");
-static_assert(kBdLds <= 160 * 1024, "LDS budget");
+template <int GPW>
+struct BdShape {
+    static constexpr int kChunkBytes = kBdWaves * GPW * 48;              // one row of one chunk
+    static constexpr int kRowPitch = kChunkBytes + 16;                   // LDS row pitch
+    static constexpr int kSlotBytes = 16 * kRowPitch;                    // one 16-row tile
+    static constexpr int kLoadsPerRow = (kChunkBytes + 1023) / 1024;     // 1 KB loads (last one may be partial)
+    static constexpr int kDmaPerWave = 16 * kLoadsPerRow / kBdWaves;
+    static constexpr size_t kLds = 2 * (size_t)kSlotBytes + 2 * (size_t)kBdRedBytes;
+    static_assert(kDmaPerWave * kBdWaves == 16 * kLoadsPerRow, "tile loads must split evenly");
+    static_assert(kLds <= 160 * 1024, "LDS budget");
+    static_assert((kRowPitch / 4) % 4 == 0 && ((kRowPitch / 4) / 4) % 2 == 1,
+                  "row pitch must spread 16 rows over distinct 4-bank groups");
+};
 
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char *)p;
@@ -741,86 +747,104 @@ __device__ __forceinline__ f4_t bd_read_partial(uint32_t addr) {
     return v;
 }
 
+template <int GPW>
 __global__ __launch_bounds__(512) void qgemm_bd_kernel(const uint4 *__restrict__ xq, const int16_t *__restrict__ xe,
                                                      const uint32_t *__restrict__ packed,
-                                                     const uint16_t *__restrict__ scales, float *__restrict__ y,
-                                                     int M, int64_t N, int64_t y_ld) {
+                                                     const uint16_t *__restrict__ scales, float *__restrict__ out,
+                                                     int M, int64_t N, int G, int C, int64_t out_chunk) {
+    using Sh = BdShape<GPW>;
     constexpr int Mp = 16;
     extern __shared__ __align__(16) unsigned char lds[];
     unsigned char *slots = lds;
-    unsigned char *red = lds + 2 * (size_t)kBdSlotBytes;
+    unsigned char *red = lds + 2 * (size_t)Sh::kSlotBytes;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15;  // B column (weight row of the tile); also the A row (token) this lane loads
     const int j = lane >> 4;  // 32-code block of the group
-    const int g0 = wave * kBdGPW;
+    const int chunk = (int)(blockIdx.x % C);
+    const int64_t tb = blockIdx.x / C, TB = gridDim.x / C;
+    const int gc = chunk * kBdWaves * GPW;  // first group of the chunk
+    const int g0 = gc + wave * GPW;         // first group of this wave
     const int64_t tiles = (N + 15) / 16;
-    const int64_t my_tiles = (tiles - (int64_t)blockIdx.x + gridDim.x - 1) / gridDim.x;  // >= 1
-    const unsigned char *pbytes = reinterpret_cast<const unsigned char *>(packed);
-
-    h8_t xa[kBdGPW][4];
-    float f[kBdGPW][4];
-#pragma unroll
-    for (int gi = 0; gi < kBdGPW; ++gi) {
-        const uint4 *ap = xq + ((((int64_t)(g0 + gi) * Mp + n) * 4 + j) * 4);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) xa[gi][u] = __builtin_bit_cast(h8_t, ap[u]);
-        const int16_t *ep = xe + (int64_t)(g0 + gi) * Mp + 4 * j;  // D rows 4j..4j+3 are tokens
-#pragma unroll
-        for (int r = 0; r < 4; ++r) f[gi][r] = ldexpf(1.f, (int)ep[r]);
-    }
+    const int64_t my_tiles = (tiles - tb + TB - 1) / TB;  // >= 1
+    const int64_t row_bytes = (int64_t)G * 48;
+    const unsigned char *pbytes = reinterpret_cast<const unsigned char *>(packed) + (int64_t)gc * 48;
+    float *y = out + (int64_t)chunk * out_chunk;
 
     auto dma_tile = [&](int64_t t, int slot) {
-        const int64_t r0 = ((int64_t)blockIdx.x + t * gridDim.x) * 16;
-        unsigned char *sb = slots + (size_t)slot * kBdSlotBytes;
+        const int64_t r0 = (tb + t * TB) * 16;
+        unsigned char *sb = slots + (size_t)slot * Sh::kSlotBytes;
 #pragma unroll
-        for (int i = 0; i < kBdDmaPerWave; ++i) {
+        for (int i = 0; i < Sh::kDmaPerWave; ++i) {
             const int idx = wave + kBdWaves * i;
-            const int row = idx / 3, c = idx - 3 * (idx / 3);
+            const int row = idx / Sh::kLoadsPerRow, c = idx - Sh::kLoadsPerRow * row;
             int64_t gr = r0 + row;
             gr = gr < N ? gr : N - 1;
-            const unsigned char *src = pbytes + gr * kBdRowBytes + c * 1024 + lane * 16;
-            __builtin_amdgcn_global_load_lds((gbl_void_t *)src, (lds_void_t *)(sb + row * kBdRowPitch + c * 1024),
-                                             16, 0, 0);
+            const int off = c * 1024 + lane * 16;
+            if (off < Sh::kChunkBytes)
+                __builtin_amdgcn_global_load_lds((gbl_void_t *)(pbytes + gr * row_bytes + off),
+                                                 (lds_void_t *)(sb + row * Sh::kRowPitch + c * 1024), 16, 0, 0);
         }
     };
-    auto load_scales = [&](int64_t t) {
-        int64_t gr = ((int64_t)blockIdx.x + t * gridDim.x) * 16 + n;
+    auto load_scales = [&](int64_t t, uint32_t (&sc)[GPW]) {
+        int64_t gr = (tb + t * TB) * 16 + n;
         gr = gr < N ? gr : N - 1;
-        return *reinterpret_cast<const uint4 *>(scales + gr * kBdG + g0);
+        const uint16_t *sp = scales + gr * G + g0;
+#pragma unroll
+        for (int gi = 0; gi < GPW; ++gi) sc[gi] = sp[gi];
     };
     auto reduce_store = [&](int64_t t) {
         const unsigned char *rb = red + (size_t)(t & 1) * kBdRedBytes;
         f4_t tot = bd_read_partial(lds_addr(rb + lane * 16));
 #pragma unroll
         for (int w = 1; w < kBdWaves; ++w) tot += bd_read_partial(lds_addr(rb + w * 1024 + lane * 16));
-        const int64_t row = ((int64_t)blockIdx.x + t * gridDim.x) * 16 + n;
+        const int64_t row = (tb + t * TB) * 16 + n;
         if (row < N) {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                if (4 * j + r < M) y[(int64_t)(4 * j + r) * y_ld + row] = tot[r];
+                if (4 * j + r < M) y[(int64_t)(4 * j + r) * N + row] = tot[r];
         }
     };
 
+    // First tile in flight before the activations are fetched.
     dma_tile(0, 0);
-    uint4 sc_next = load_scales(0);
+    uint32_t sc_next[GPW];
+    load_scales(0, sc_next);
+
+    // A operands of this wave's groups; rows (tokens) past M stay zero.
+    h8_t xa[GPW][4];
+    float f[GPW][4];
+#pragma unroll
+    for (int gi = 0; gi < GPW; ++gi) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) xa[gi][u] = h8_t{0, 0, 0, 0, 0, 0, 0, 0};
+        if (n < M) {
+            const uint4 *ap = xq + ((((int64_t)(g0 + gi) * Mp + n) * 4 + j) * 4);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) xa[gi][u] = __builtin_bit_cast(h8_t, ap[u]);
+        }
+        const int16_t *ep = xe + (int64_t)(g0 + gi) * Mp + 4 * j;  // D rows 4j..4j+3 are tokens
+#pragma unroll
+        for (int r = 0; r < 4; ++r) f[gi][r] = ldexpf(1.f, (int)ep[r]);
+    }
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     lds_barrier();
     const uint32_t magic = magic_vgpr();
     for (int64_t t = 0; t < my_tiles; ++t) {
-        const uint4 sc = sc_next;
+        uint32_t sc[GPW];
+#pragma unroll
+        for (int gi = 0; gi < GPW; ++gi) sc[gi] = sc_next[gi];
         if (t + 1 < my_tiles) {
             dma_tile(t + 1, (int)((t + 1) & 1));
-            sc_next = load_scales(t + 1);
+            load_scales(t + 1, sc_next);
         }
         if (t > 0 && wave == (int)((t - 1) % kBdWaves)) reduce_store(t - 1);
-        const unsigned char *sb = slots + (size_t)(t & 1) * kBdSlotBytes + n * kBdRowPitch + 12 * j;
-        const uint32_t scw[4] = {sc.x, sc.y, sc.z, sc.w};
+        const unsigned char *sb = slots + (size_t)(t & 1) * Sh::kSlotBytes + n * Sh::kRowPitch + 12 * j;
         f4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int gi = 0; gi < kBdGPW; ++gi) {
+        for (int gi = 0; gi < GPW; ++gi) {
             uint32_t w0, w1, w2;
-            bd_read_words(lds_addr(sb + (g0 + gi) * 48), w0, w1, w2);
+            bd_read_words(lds_addr(sb + (wave * GPW + gi) * 48), w0, w1, w2);
             h2_t q[16];
             decode_block(w0, w1, w2, magic, q);
             f4_t d = {0.f, 0.f, 0.f, 0.f};
@@ -830,8 +854,7 @@ __global__ __launch_bounds__(512) void qgemm_bd_kernel(const uint4 *__restrict__
                                   q[4 * u + 2].x, q[4 * u + 2].y, q[4 * u + 3].x, q[4 * u + 3].y};
                 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[gi][u], bop, d, 0, 0, 0);
             }
-            const uint32_t sw = scw[gi >> 1];
-            const float sv = __uint_as_float((gi & 1) ? (sw & 0xFFFF0000u) : (sw << 16));
+            const float sv = bf16_to_f32(sc[gi]);
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[r] = fmaf(d[r] * f[gi][r], sv, acc[r]);
         }
@@ -840,6 +863,16 @@ __global__ __launch_bounds__(512) void qgemm_bd_kernel(const uint4 *__restrict__
         lds_barrier();
     }
     if (wave == (int)((my_tiles - 1) % kBdWaves)) reduce_store(my_tiles - 1);
+}
+
+// y[m][n] = sum over chunks c, in order, of part[c][m][n].
+__global__ __launch_bounds__(256) void qgemm_chunk_sum_kernel(const float *__restrict__ part, float *__restrict__ y,
+                                                            int64_t count, int C, int64_t chunk_stride) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= count) return;
+    float tot = part[i];
+    for (int c = 1; c < C; ++c) tot += part[(int64_t)c * chunk_stride + i];
+    y[i] = tot;
 }
 
 // --------------------------------------------------- prefill (large M) tiles --
@@ -1245,27 +1278,33 @@ qw3_status launch_gemm_tile(const uint16_t *x, const uint32_t *packed, const uin
     return st;
 }
 
-// Batched decode for rows of 64 groups: passes of 16 tokens, each one
-// conversion launch and one streaming pass over W.
+// Batched decode: passes of 16 tokens, each one conversion launch and one
+// streaming pass over W (plus a chunk sum when K is split).
+template <int GPW>
 qw3_status launch_gemm_bd(const uint16_t *x, const uint32_t *packed, const uint16_t *scales, float *y,
                           int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+    using Sh = BdShape<GPW>;
     constexpr int Mp = 16;
     const int G = (int)(K / kGroup);
+    const int C = G / (kBdWaves * GPW);
     const size_t xq_bytes = (size_t)Mp * (size_t)K * 2;
-    const size_t xe_bytes = (size_t)G * Mp * sizeof(int16_t);
+    const size_t xe_bytes = ((size_t)G * Mp * sizeof(int16_t) + 255) / 256 * 256;
+    const size_t part_bytes = C > 1 ? (size_t)C * Mp * (size_t)N * sizeof(float) : 0;
     int cus = 0, per_cu = 0;
     qw3_status st = cu_count(&cus);
     if (st == QW3_OK)
-        st = blocks_per_cu(reinterpret_cast<const void *>(&qgemm_bd_kernel), 64 * kBdWaves, kBdLds, &per_cu);
+        st = blocks_per_cu(reinterpret_cast<const void *>(&qgemm_bd_kernel<GPW>), 64 * kBdWaves, Sh::kLds, &per_cu);
     if (st != QW3_OK) return st;
     void *scratch = nullptr;
-    hipError_t err = hipMallocAsync(&scratch, xq_bytes + xe_bytes, stream);
+    hipError_t err = hipMallocAsync(&scratch, xq_bytes + xe_bytes + part_bytes, stream);
     if (err != hipSuccess) return hip_fail(err);
     uint4 *xq = reinterpret_cast<uint4 *>(scratch);
     int16_t *xe = reinterpret_cast<int16_t *>(static_cast<char *>(scratch) + xq_bytes);
+    float *part = reinterpret_cast<float *>(static_cast<char *>(scratch) + xq_bytes + xe_bytes);
     const int64_t tiles = ceil_div(N, 16);
-    int64_t blocks = (int64_t)cus * per_cu;
-    if (blocks > tiles) blocks = tiles;
+    int64_t tb = (int64_t)cus * per_cu / C;
+    if (tb < 1) tb = 1;
+    if (tb > tiles) tb = tiles;
     for (int64_t m0 = 0; m0 < M && st == QW3_OK; m0 += Mp) {
         const int mc = (int)(M - m0 < Mp ? M - m0 : Mp);
         const int64_t units = (int64_t)G * Mp * 4;
@@ -1273,8 +1312,14 @@ qw3_status launch_gemm_bd(const uint16_t *x, const uint32_t *packed, const uint1
                            xe, mc, Mp, K, G);
         st = check_launch();
         if (st != QW3_OK) break;
-        hipLaunchKernelGGL(qgemm_bd_kernel, dim3((unsigned)blocks), dim3(64 * kBdWaves), kBdLds, stream, xq, xe,
-                           packed, scales, y + m0 * N, mc, N, N);
+        float *dst = C > 1 ? part : y + m0 * N;
+        hipLaunchKernelGGL(qgemm_bd_kernel<GPW>, dim3((unsigned)(tb * C)), dim3(64 * kBdWaves), Sh::kLds, stream, xq,
+                           xe, packed, scales, dst, mc, N, G, C, (int64_t)Mp * N);
+        st = check_launch();
+        if (st != QW3_OK || C == 1) continue;
+        const int64_t count = (int64_t)mc * N;
+        hipLaunchKernelGGL(qgemm_chunk_sum_kernel, dim3((unsigned)ceil_div(count, 256)), dim3(256), 0, stream, part,
+                           y + m0 * N, count, C, (int64_t)Mp * N);
         st = check_launch();
     }
     err = hipFreeAsync(scratch, stream);
@@ -1288,8 +1333,9 @@ qw3_status launch_gemm_small(const uint16_t *x, const uint32_t *packed, const ui
                              int64_t M, int64_t N, int64_t K, hipStream_t stream) {
     const int G = (int)(K / kGroup);
     if (M > 32) return launch_gemm_tile(x, packed, scales, y, M, N, K, stream);
-    if (G == kBdG && (reinterpret_cast<uintptr_t>(scales) & 15) == 0)
-        return launch_gemm_bd(x, packed, scales, y, M, N, K, stream);
+    // Batched decode: chunks of 64 groups (8 waves x 8), or of 56 (8 x 7).
+    if (G % 64 == 0) return launch_gemm_bd<8>(x, packed, scales, y, M, N, K, stream);
+    if (G % 56 == 0) return launch_gemm_bd<7>(x, packed, scales, y, M, N, K, stream);
     const int mchunk = M > 16 ? 32 : 16;
     const size_t xq_bytes = (size_t)mchunk * (size_t)K * 2;
     const size_t xe_bytes = (size_t)G * mchunk * sizeof(int16_t);
