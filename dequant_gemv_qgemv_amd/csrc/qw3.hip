@@ -306,6 +306,9 @@ __global__ __launch_bounds__(256) void qdequant_kernel(const uint32_t *__restric
 #ifndef QW3_GEMV_DEPTH
 #define QW3_GEMV_DEPTH 3
 #endif
+#ifndef QW3_GEMV_DEFER
+#define QW3_GEMV_DEFER 0
+#endif
 constexpr int kGemvDepth = QW3_GEMV_DEPTH;
 #ifndef QW3_GEMV_WGS
 #define QW3_GEMV_WGS 256
@@ -329,13 +332,27 @@ struct RowBuf {
 // the compiler can wait for exactly the loads a step needs (s_waitcnt vmcnt(n))
 // instead of draining every load in flight.  The extra rows are never stored
 // and the extra groups meet zero activations.
+#ifndef QW3_GEMV_NT
+#define QW3_GEMV_NT 0
+#endif
+typedef unsigned u32x4v_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_words16(const uint32_t *p) {
+#if QW3_GEMV_NT
+    // Streaming data, read once: non-temporal loads keep it out of the caches.
+    const u32x4v_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4v_t *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+#else
+    return *reinterpret_cast<const uint4 *>(p);
+#endif
+}
+
 __device__ __forceinline__ void load_row(const uint32_t *__restrict__ packed, const uint16_t *__restrict__ scales,
                                          int64_t r, int64_t N, int64_t W, int G, int g_load, RowBuf &rb) {
     const int64_t rr = r < N ? r : N - 1;
-    const uint4 *p = reinterpret_cast<const uint4 *>(packed + rr * W + g_load * kWordsPerGroup);
-    rb.a = p[0];
-    rb.b = p[1];
-    rb.c = p[2];
+    const uint32_t *p = packed + rr * W + g_load * kWordsPerGroup;
+    rb.a = load_words16(p);
+    rb.b = load_words16(p + 4);
+    rb.c = load_words16(p + 8);
     rb.s = scales[rr * G + g_load];
 }
 
@@ -480,6 +497,24 @@ __global__ __launch_bounds__(kGemvWGS) QW3_GEMV_OCC void qgemv_small_kernel(cons
     const uint32_t magic = magic_vgpr();
 
     for (int64_t row = row0; row < N; row += E * stride) {
+#if QW3_GEMV_DEFER
+        // Decode all E rows first, then reduce them together: the E DPP chains
+        // are independent, so they fill each other's wait states.
+        float part[E];
+#pragma unroll
+        for (int i = 0; i < E; ++i) {
+            const int64_t r = row + i * stride;
+            load_row(packed, scales, r + D * stride, N, W, G, g_load, ring[(i + D) % E]);
+            __builtin_amdgcn_sched_barrier(0);
+            part[i] = row_partial(ring[i], xp, e, magic);
+        }
+#pragma unroll
+        for (int i = 0; i < E; ++i) {
+            const int64_t r = row + i * stride;
+            const float tot = segment_sum<T>(part[i]);
+            if (gl == T - 1 && r < N) y[r] = tot;
+        }
+#else
 #pragma unroll
         for (int i = 0; i < E; ++i) {
             const int64_t r = row + i * stride;
@@ -489,6 +524,7 @@ __global__ __launch_bounds__(kGemvWGS) QW3_GEMV_OCC void qgemv_small_kernel(cons
             const float tot = segment_sum<T>(part);
             if (gl == T - 1 && r < N) y[r] = tot;
         }
+#endif
     }
 }
 
@@ -680,191 +716,6 @@ __global__ __launch_bounds__(256) void qgemm_mfma_kernel(const uint4 *__restrict
         }
 }
 
-// ------------------------------------------ batched decode, K-split, LDS DMA --
-// y[m][n] for up to 16 tokens at once.  K is cut into C chunks of 8 * GPW
-// groups; a workgroup owns one chunk and a set of 16-row tiles.  Its 8 waves
-// split the chunk (wave w owns GPW consecutive groups) and keep the A
-// operands of those groups (x' of the 16 tokens, 16 * GPW VGPRs) for the whole
-// kernel, so activations are read once per workgroup.  Each tile's packed
-// words for the chunk are copied into LDS with global_load_lds_dwordx4 --
-// 1 KB contiguous per instruction, issued one tile ahead into the other of
-// two slots -- with row pitches chosen so that the 64 lanes' reads of
-// (row l%16, block l/16) fall in distinct banks.  Per group: decode (the B
-// operand), 4 MFMAs, then D[m][n] * 2^e[g][m] * s[n][g] into the accumulator.
-// At the end of a tile each wave leaves its 16 x 16 partial sums in LDS;
-// after the tile barrier one wave (rotating) adds the 8 partials in wave
-// order and stores them: to y when C == 1, else to chunk-major partial sums
-// that qgemm_chunk_sum_kernel adds in chunk order.
-// LDS reads and writes inside the loop are asm blocks that wait for
-// themselves: the compiler would otherwise drain every LDS DMA in flight
-// before each one (it cannot tell the ring slots apart).
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) const void gbl_void_t;
-
-// s_waitcnt immediate that constrains vmcnt only (gfx9 encoding: vmcnt in
-// bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
-constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
-
-constexpr int kBdWaves = 8;
-constexpr int kBdRedBytes = kBdWaves * 64 * 16;
-template <int GPW>
-struct BdShape {
-    static constexpr int kChunkBytes = kBdWaves * GPW * 48;              // one row of one chunk
-    static constexpr int kRowPitch = kChunkBytes + 16;                   // LDS row pitch
-    static constexpr int kSlotBytes = 16 * kRowPitch;                    // one 16-row tile
-    static constexpr int kLoadsPerRow = (kChunkBytes + 1023) / 1024;     // 1 KB loads (last one may be partial)
-    static constexpr int kDmaPerWave = 16 * kLoadsPerRow / kBdWaves;
-    static constexpr size_t kLds = 2 * (size_t)kSlotBytes + 2 * (size_t)kBdRedBytes;
-    static_assert(kDmaPerWave * kBdWaves == 16 * kLoadsPerRow, "tile loads must split evenly");
-    static_assert(kLds <= 160 * 1024, "LDS budget");
-    static_assert((kRowPitch / 4) % 4 == 0 && ((kRowPitch / 4) / 4) % 2 == 1,
-                  "row pitch must spread 16 rows over distinct 4-bank groups");
-};
-
-__device__ __forceinline__ uint32_t lds_addr(const void *p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char *)p;
-}
-
-// The lane's 3 words (block j of one row's group) from a tile slot.
-__device__ __forceinline__ void bd_read_words(uint32_t addr, uint32_t &w0, uint32_t &w1, uint32_t &w2) {
-    asm volatile(
-        "ds_read_b32 %0, %3\n\t"
-        "ds_read_b32 %1, %3 offset:4\n\t"
-        "ds_read_b32 %2, %3 offset:8\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(w0), "=&v"(w1), "=&v"(w2)
-        : "v"(addr)
-        : "memory");
-}
-
-__device__ __forceinline__ void bd_write_partial(uint32_t addr, f4_t v) {
-    asm volatile("ds_write_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : : "v"(addr), "v"(v) : "memory");
-}
-
-__device__ __forceinline__ f4_t bd_read_partial(uint32_t addr) {
-    f4_t v;
-    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(addr) : "memory");
-    return v;
-}
-
-template <int GPW>
-__global__ __launch_bounds__(512) void qgemm_bd_kernel(const uint4 *__restrict__ xq, const int16_t *__restrict__ xe,
-                                                     const uint32_t *__restrict__ packed,
-                                                     const uint16_t *__restrict__ scales, float *__restrict__ out,
-                                                     int M, int64_t N, int G, int C, int64_t out_chunk) {
-    using Sh = BdShape<GPW>;
-    constexpr int Mp = 16;
-    extern __shared__ __align__(16) unsigned char lds[];
-    unsigned char *slots = lds;
-    unsigned char *red = lds + 2 * (size_t)Sh::kSlotBytes;
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int n = lane & 15;  // B column (weight row of the tile); also the A row (token) this lane loads
-    const int j = lane >> 4;  // 32-code block of the group
-    const int chunk = (int)(blockIdx.x % C);
-    const int64_t tb = blockIdx.x / C, TB = gridDim.x / C;
-    const int gc = chunk * kBdWaves * GPW;  // first group of the chunk
-    const int g0 = gc + wave * GPW;         // first group of this wave
-    const int64_t tiles = (N + 15) / 16;
-    const int64_t my_tiles = (tiles - tb + TB - 1) / TB;  // >= 1
-    const int64_t row_bytes = (int64_t)G * 48;
-    const unsigned char *pbytes = reinterpret_cast<const unsigned char *>(packed) + (int64_t)gc * 48;
-    float *y = out + (int64_t)chunk * out_chunk;
-
-    auto dma_tile = [&](int64_t t, int slot) {
-        const int64_t r0 = (tb + t * TB) * 16;
-        unsigned char *sb = slots + (size_t)slot * Sh::kSlotBytes;
-#pragma unroll
-        for (int i = 0; i < Sh::kDmaPerWave; ++i) {
-            const int idx = wave + kBdWaves * i;
-            const int row = idx / Sh::kLoadsPerRow, c = idx - Sh::kLoadsPerRow * row;
-            int64_t gr = r0 + row;
-            gr = gr < N ? gr : N - 1;
-            const int off = c * 1024 + lane * 16;
-            if (off < Sh::kChunkBytes)
-                __builtin_amdgcn_global_load_lds((gbl_void_t *)(pbytes + gr * row_bytes + off),
-                                                 (lds_void_t *)(sb + row * Sh::kRowPitch + c * 1024), 16, 0, 0);
-        }
-    };
-    auto load_scales = [&](int64_t t, uint32_t (&sc)[GPW]) {
-        int64_t gr = (tb + t * TB) * 16 + n;
-        gr = gr < N ? gr : N - 1;
-        const uint16_t *sp = scales + gr * G + g0;
-#pragma unroll
-        for (int gi = 0; gi < GPW; ++gi) sc[gi] = sp[gi];
-    };
-    auto reduce_store = [&](int64_t t) {
-        const unsigned char *rb = red + (size_t)(t & 1) * kBdRedBytes;
-        f4_t tot = bd_read_partial(lds_addr(rb + lane * 16));
-#pragma unroll
-        for (int w = 1; w < kBdWaves; ++w) tot += bd_read_partial(lds_addr(rb + w * 1024 + lane * 16));
-        const int64_t row = (tb + t * TB) * 16 + n;
-        if (row < N) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                if (4 * j + r < M) y[(int64_t)(4 * j + r) * N + row] = tot[r];
-        }
-    };
-
-    // First tile in flight before the activations are fetched.
-    dma_tile(0, 0);
-    uint32_t sc_next[GPW];
-    load_scales(0, sc_next);
-
-    // A operands of this wave's groups; rows (tokens) past M stay zero.
-    h8_t xa[GPW][4];
-    float f[GPW][4];
-#pragma unroll
-    for (int gi = 0; gi < GPW; ++gi) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) xa[gi][u] = h8_t{0, 0, 0, 0, 0, 0, 0, 0};
-        if (n < M) {
-            const uint4 *ap = xq + ((((int64_t)(g0 + gi) * Mp + n) * 4 + j) * 4);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) xa[gi][u] = __builtin_bit_cast(h8_t, ap[u]);
-        }
-        const int16_t *ep = xe + (int64_t)(g0 + gi) * Mp + 4 * j;  // D rows 4j..4j+3 are tokens
-#pragma unroll
-        for (int r = 0; r < 4; ++r) f[gi][r] = ldexpf(1.f, (int)ep[r]);
-    }
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    lds_barrier();
-    const uint32_t magic = magic_vgpr();
-    for (int64_t t = 0; t < my_tiles; ++t) {
-        uint32_t sc[GPW];
-#pragma unroll
-        for (int gi = 0; gi < GPW; ++gi) sc[gi] = sc_next[gi];
-        if (t + 1 < my_tiles) {
-            dma_tile(t + 1, (int)((t + 1) & 1));
-            load_scales(t + 1, sc_next);
-        }
-        if (t > 0 && wave == (int)((t - 1) % kBdWaves)) reduce_store(t - 1);
-        const unsigned char *sb = slots + (size_t)(t & 1) * Sh::kSlotBytes + n * Sh::kRowPitch + 12 * j;
-        f4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int gi = 0; gi < GPW; ++gi) {
-            uint32_t w0, w1, w2;
-            bd_read_words(lds_addr(sb + (wave * GPW + gi) * 48), w0, w1, w2);
-            h2_t q[16];
-            decode_block(w0, w1, w2, magic, q);
-            f4_t d = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const h8_t bop = {q[4 * u].x, q[4 * u].y, q[4 * u + 1].x, q[4 * u + 1].y,
-                                  q[4 * u + 2].x, q[4 * u + 2].y, q[4 * u + 3].x, q[4 * u + 3].y};
-                d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[gi][u], bop, d, 0, 0, 0);
-            }
-            const float sv = bf16_to_f32(sc[gi]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] = fmaf(d[r] * f[gi][r], sv, acc[r]);
-        }
-        bd_write_partial(lds_addr(red + (size_t)(t & 1) * kBdRedBytes + wave * 1024 + lane * 16), acc);
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's loads of tile t + 1 have landed
-        lds_barrier();
-    }
-    if (wave == (int)((my_tiles - 1) % kBdWaves)) reduce_store(my_tiles - 1);
-}
-
 // y[m][n] = sum over chunks c, in order, of part[c][m][n].
 __global__ __launch_bounds__(256) void qgemm_chunk_sum_kernel(const float *__restrict__ part, float *__restrict__ y,
                                                             int64_t count, int C, int64_t chunk_stride) {
@@ -873,6 +724,191 @@ __global__ __launch_bounds__(256) void qgemm_chunk_sum_kernel(const float *__res
     float tot = part[i];
     for (int c = 1; c < C; ++c) tot += part[(int64_t)c * chunk_stride + i];
     y[i] = tot;
+}
+
+// ------------------------------ batched decode from registers, K-split, MFMA --
+// Same decode and MFMAs as qgemm_bd_kernel (lane (n = l%16, j = l/16)
+// decodes block j of each group of weight row n of a 16-row tile; 4 MFMAs
+// per group, then D * s[n][g]), but the words come straight from
+// global memory into registers: lane (n, j) loads all 48 bytes of group
+// 4q + j of its row, so the 4 lanes of a row read 192 contiguous bytes, and
+// a 4 x 4 transpose of 12-byte blocks across the 4 lanes (permlane32 and
+// permlane16 swaps) then gives lane j block j of groups 4q..4q+3.  Each wave
+// owns 8 consecutive groups (2 quads) of a chunk of K; tiles are prefetched
+// one ahead in registers.  The activations of a wave's 8 groups share one
+// exponent per token (prep_x_slice_kernel), so D * s[n][g] accumulates and
+// the token exponent is applied once per tile.
+
+// x' with one exponent per (token, 8-group slice): unit (slice, m, gi, b) =
+// the 32 values of block b of group slice*8 + gi; the 32 units of a
+// (slice, m) are one half-wave.  Same layout as prep_x_kernel:
+// xq[((g*Mp + m)*4 + b)*4 + t]; xe[slice*Mp + m].
+__global__ __launch_bounds__(256) void prep_x_slice_kernel(const uint16_t *__restrict__ x, uint4 *__restrict__ xq,
+                                                           int16_t *__restrict__ xe, int M, int Mp, int64_t K,
+                                                           int S) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t units = (int64_t)S * Mp * 32;
+    if (idx >= units) return;  // units is a multiple of 32: whole half-waves exit together
+    const int b = (int)(idx & 3);
+    const int gi = (int)((idx >> 2) & 7);
+    const int64_t sm = idx >> 5;
+    const int m = (int)(sm % Mp);
+    const int sl = (int)(sm / Mp);
+    const int g = sl * 8 + gi;
+    uint4 xb[4];
+    if (m < M) {
+        load_x32(x + (int64_t)m * K + (int64_t)g * kGroup + b * 32, xb);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xb[i] = make_uint4(0, 0, 0, 0);
+    }
+    uint32_t mx = absmax32(xb);
+#pragma unroll
+    for (int off = 1; off < 32; off <<= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 32));
+    const int e = m < M ? group_exponent(mx) : 0;
+    uint32_t out[16];
+    convert_block(xb, e, out);
+    uint4 *dst = xq + ((((int64_t)g * Mp + m) * 4 + b) * 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
+    if (gi == 0 && b == 0) xe[(int64_t)sl * Mp + m] = (int16_t)e;
+}
+
+// 4 x 4 transpose of 3-dword blocks across the lane rows j = l/16:
+// in: b[k] = block k of lane row j's group; out: b[k] = block j of row k's.
+__device__ __forceinline__ void quad_block_transpose(uint32_t (&b)[4][3]) {
+#pragma unroll
+    for (int d = 0; d < 3; ++d) {
+        // rows {0,1} <-> {2,3}: (b0, b2) and (b1, b3)
+        auto r02 = __builtin_amdgcn_permlane32_swap(b[0][d], b[2][d], false, false);
+        auto r13 = __builtin_amdgcn_permlane32_swap(b[1][d], b[3][d], false, false);
+        // rows 0 <-> 1 and 2 <-> 3: (b0, b1) and (b2, b3)
+        auto r01 = __builtin_amdgcn_permlane16_swap(r02[0], r13[0], false, false);
+        auto r23 = __builtin_amdgcn_permlane16_swap(r02[1], r13[1], false, false);
+        b[0][d] = r01[0];
+        b[1][d] = r01[1];
+        b[2][d] = r23[0];
+        b[3][d] = r23[1];
+    }
+}
+
+typedef unsigned u32x4m_t __attribute__((ext_vector_type(4)));
+struct MtStage {
+    u32x4m_t w[6];  // quad 0: w[0..2] (group 4*0 + j), quad 1: w[3..5] (group 4 + j)
+    u32x4m_t s;     // bf16 scales of the wave's 8 groups for row n
+};
+
+template <int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void qgemm_mt_kernel(const uint4 *__restrict__ xq,
+                                                            const int16_t *__restrict__ xe,
+                                                            const uint32_t *__restrict__ packed,
+                                                            const uint16_t *__restrict__ scales,
+                                                            float *__restrict__ out, int M, int64_t N, int G, int C,
+                                                            int64_t out_chunk) {
+    constexpr int Mp = 16;
+    __shared__ __align__(16) unsigned char red[2][WAVES][64 * 16];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n = lane & 15;
+    const int j = lane >> 4;
+    const int chunk = (int)(blockIdx.x % C);
+    const int64_t tb = blockIdx.x / C, TB = gridDim.x / C;
+    const int g0 = (chunk * WAVES + wave) * 8;  // the wave's 8 groups
+    const int64_t tiles = (N + 15) / 16;
+    const int64_t my_tiles = (tiles - tb + TB - 1) / TB;  // >= 1
+    const int64_t W = (int64_t)G * kWordsPerGroup;
+    float *y = out + (int64_t)chunk * out_chunk;
+
+    auto load_stage = [&](int64_t t, MtStage &st) {
+        t = t < my_tiles ? t : my_tiles - 1;
+        int64_t row = (tb + t * TB) * 16 + n;
+        row = row < N ? row : N - 1;
+        const uint32_t *rp = packed + row * W;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const u32x4m_t *p = reinterpret_cast<const u32x4m_t *>(rp + (int64_t)(g0 + 4 * q + j) * kWordsPerGroup);
+#pragma unroll
+            for (int i = 0; i < 3; ++i) st.w[3 * q + i] = p[i];
+        }
+        const uint16_t *sp = scales + row * G + g0;
+        st.s = u32x4m_t{(uint32_t)sp[0] | ((uint32_t)sp[1] << 16), (uint32_t)sp[2] | ((uint32_t)sp[3] << 16),
+                        (uint32_t)sp[4] | ((uint32_t)sp[5] << 16), (uint32_t)sp[6] | ((uint32_t)sp[7] << 16)};
+    };
+    MtStage ring0, ring1;
+    load_stage(0, ring0);
+
+    h8_t xa[8][4];
+#pragma unroll
+    for (int gi = 0; gi < 8; ++gi) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            xa[gi][u] = h8_t{0, 0, 0, 0, 0, 0, 0, 0};
+            if (n < M) xa[gi][u] = __builtin_bit_cast(h8_t, xq[(((int64_t)(g0 + gi) * Mp + n) * 4 + j) * 4 + u]);
+        }
+    }
+    // One activation exponent per (token, slice): D rows 4j..4j+3 are tokens.
+    int et[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) et[r] = xe[(int64_t)(g0 / 8) * Mp + 4 * j + r];
+    const uint32_t magic = magic_vgpr();
+
+    auto tile = [&](int64_t t, const MtStage &st) {
+        const uint32_t scw[4] = {st.s.x, st.s.y, st.s.z, st.s.w};
+        f4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            uint32_t blk[4][3];
+            const uint32_t wd[12] = {st.w[3 * q].x,     st.w[3 * q].y,     st.w[3 * q].z,     st.w[3 * q].w,
+                                     st.w[3 * q + 1].x, st.w[3 * q + 1].y, st.w[3 * q + 1].z, st.w[3 * q + 1].w,
+                                     st.w[3 * q + 2].x, st.w[3 * q + 2].y, st.w[3 * q + 2].z, st.w[3 * q + 2].w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+#pragma unroll
+                for (int d = 0; d < 3; ++d) blk[k][d] = wd[3 * k + d];
+            quad_block_transpose(blk);  // blk[k] = block j of group g0 + 4q + k
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int gi = 4 * q + k;
+                h2_t qd[16];
+                decode_block(blk[k][0], blk[k][1], blk[k][2], magic, qd);
+                f4_t d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const h8_t bop = {qd[4 * u].x, qd[4 * u].y, qd[4 * u + 1].x, qd[4 * u + 1].y,
+                                      qd[4 * u + 2].x, qd[4 * u + 2].y, qd[4 * u + 3].x, qd[4 * u + 3].y};
+                    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[gi][u], bop, d, 0, 0, 0);
+                }
+                const uint32_t sw = scw[gi >> 1];
+                const float sv = __uint_as_float((gi & 1) ? (sw & 0xFFFF0000u) : (sw << 16));
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[r] = fmaf(d[r], sv, acc[r]);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] = ldexpf(acc[r], et[r]);
+        *reinterpret_cast<f4_t *>(&red[t & 1][wave][lane * 16]) = acc;
+        lds_barrier();  // LDS only: the next tile's loads stay in flight
+        if (wave == (int)(t % WAVES)) {
+            f4_t tot = *reinterpret_cast<const f4_t *>(&red[t & 1][0][lane * 16]);
+#pragma unroll
+            for (int w = 1; w < WAVES; ++w) tot += *reinterpret_cast<const f4_t *>(&red[t & 1][w][lane * 16]);
+            const int64_t row = (tb + t * TB) * 16 + n;
+            if (row < N) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (4 * j + r < M) y[(int64_t)(4 * j + r) * N + row] = tot[r];
+            }
+        }
+    };
+    for (int64_t t = 0; t < my_tiles; t += 2) {
+        load_stage(t + 1, ring1);
+        __builtin_amdgcn_sched_barrier(0);
+        tile(t, ring0);
+        if (t + 1 >= my_tiles) break;  // workgroup-uniform
+        load_stage(t + 2, ring0);
+        __builtin_amdgcn_sched_barrier(0);
+        tile(t + 1, ring1);
+    }
 }
 
 // --------------------------------------------------- prefill (large M) tiles --
@@ -1278,22 +1314,21 @@ qw3_status launch_gemm_tile(const uint16_t *x, const uint32_t *packed, const uin
     return st;
 }
 
-// Batched decode: passes of 16 tokens, each one conversion launch and one
-// streaming pass over W (plus a chunk sum when K is split).
-template <int GPW>
-qw3_status launch_gemm_bd(const uint16_t *x, const uint32_t *packed, const uint16_t *scales, float *y,
-                          int64_t M, int64_t N, int64_t K, hipStream_t stream) {
-    using Sh = BdShape<GPW>;
+// Batched decode from registers (tokens <= 16 per pass), K in chunks of
+// WAVES x 8 groups.
+template <int WAVES>
+qw3_status launch_gemm_mt(const uint16_t *x, const uint32_t *packed, const uint16_t *scales, float *y, int64_t M,
+                          int64_t N, int64_t K, hipStream_t stream) {
     constexpr int Mp = 16;
     const int G = (int)(K / kGroup);
-    const int C = G / (kBdWaves * GPW);
+    const int C = G / (8 * WAVES);
     const size_t xq_bytes = (size_t)Mp * (size_t)K * 2;
-    const size_t xe_bytes = ((size_t)G * Mp * sizeof(int16_t) + 255) / 256 * 256;
+    const size_t xe_bytes = ((size_t)(G / 8) * Mp * sizeof(int16_t) + 255) / 256 * 256;
     const size_t part_bytes = C > 1 ? (size_t)C * Mp * (size_t)N * sizeof(float) : 0;
     int cus = 0, per_cu = 0;
     qw3_status st = cu_count(&cus);
     if (st == QW3_OK)
-        st = blocks_per_cu(reinterpret_cast<const void *>(&qgemm_bd_kernel<GPW>), 64 * kBdWaves, Sh::kLds, &per_cu);
+        st = blocks_per_cu(reinterpret_cast<const void *>(&qgemm_mt_kernel<WAVES>), 64 * WAVES, 0, &per_cu);
     if (st != QW3_OK) return st;
     void *scratch = nullptr;
     hipError_t err = hipMallocAsync(&scratch, xq_bytes + xe_bytes + part_bytes, stream);
@@ -1307,14 +1342,14 @@ qw3_status launch_gemm_bd(const uint16_t *x, const uint32_t *packed, const uint1
     if (tb > tiles) tb = tiles;
     for (int64_t m0 = 0; m0 < M && st == QW3_OK; m0 += Mp) {
         const int mc = (int)(M - m0 < Mp ? M - m0 : Mp);
-        const int64_t units = (int64_t)G * Mp * 4;
-        hipLaunchKernelGGL(prep_x_kernel, dim3((unsigned)ceil_div(units, 256)), dim3(256), 0, stream, x + m0 * K, xq,
-                           xe, mc, Mp, K, G);
+        const int64_t units = (int64_t)(G / 8) * Mp * 32;
+        hipLaunchKernelGGL(prep_x_slice_kernel, dim3((unsigned)ceil_div(units, 256)), dim3(256), 0, stream,
+                           x + m0 * K, xq, xe, mc, Mp, K, G / 8);
         st = check_launch();
         if (st != QW3_OK) break;
         float *dst = C > 1 ? part : y + m0 * N;
-        hipLaunchKernelGGL(qgemm_bd_kernel<GPW>, dim3((unsigned)(tb * C)), dim3(64 * kBdWaves), Sh::kLds, stream, xq,
-                           xe, packed, scales, dst, mc, N, G, C, (int64_t)Mp * N);
+        hipLaunchKernelGGL(qgemm_mt_kernel<WAVES>, dim3((unsigned)(tb * C)), dim3(64 * WAVES), 0, stream, xq, xe,
+                           packed, scales, dst, mc, N, G, C, (int64_t)Mp * N);
         st = check_launch();
         if (st != QW3_OK || C == 1) continue;
         const int64_t count = (int64_t)mc * N;
@@ -1333,9 +1368,9 @@ qw3_status launch_gemm_small(const uint16_t *x, const uint32_t *packed, const ui
                              int64_t M, int64_t N, int64_t K, hipStream_t stream) {
     const int G = (int)(K / kGroup);
     if (M > 32) return launch_gemm_tile(x, packed, scales, y, M, N, K, stream);
-    // Batched decode: chunks of 64 groups (8 waves x 8), or of 56 (8 x 7).
-    if (G % 64 == 0) return launch_gemm_bd<8>(x, packed, scales, y, M, N, K, stream);
-    if (G % 56 == 0) return launch_gemm_bd<7>(x, packed, scales, y, M, N, K, stream);
+    // Batched decode: chunks of 8 waves x 8 groups (or 7 x 8 when K = 28672).
+    if (G % 64 == 0) return launch_gemm_mt<8>(x, packed, scales, y, M, N, K, stream);
+    if (G % 56 == 0) return launch_gemm_mt<7>(x, packed, scales, y, M, N, K, stream);
     const int mchunk = M > 16 ? 32 : 16;
     const size_t xq_bytes = (size_t)mchunk * (size_t)K * 2;
     const size_t xe_bytes = (size_t)G * mchunk * sizeof(int16_t);

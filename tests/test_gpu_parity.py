@@ -232,6 +232,32 @@ def test_qgemm_parity(m, n, k):
     assert_close(y, yr, a, "qgemm M=%d %dx%d" % (m, n, k))
 
 
+@pytest.mark.parametrize("m,n,k", [(5, 48, 16384), (16, 40, 7168), (9, 33, 57344)])
+def test_qgemm_chunked_k(m, n, k):
+    # K split over several workgroup chunks (partial sums added in a second pass)
+    say("qgemm chunked", m, n, k)
+    c = synth.codes_all8(4300 + k, n, k)
+    s = synth.scales(4400 + k, n, k // 128, sigma=0.02, eps=1e-3)
+    x = synth.activations(4500 + m, m, k)
+    y = host(q().qgemm_w3g128_smallM(dev(x), gpu_pack(c), dev(s)))
+    yr, a = oracle.gemm(x, oracle.pack(c), s, k)
+    assert_close(y, yr, a, "qgemm chunked M=%d %dx%d" % (m, n, k))
+
+
+def test_qgemm_scales_view_not_16_byte_aligned():
+    m, n, k = 6, 40, 8192
+    c = synth.codes_all8(4600, n, k)
+    s = synth.scales(4601, n, k // 128, sigma=0.02, eps=1e-3)
+    x = synth.activations(4602, m, k)
+    say("qgemm scales offset by one element")
+    big = torch.zeros(s.size + 8, dtype=torch.int16, device="cuda")
+    big[1:1 + s.size] = torch.from_numpy(s.reshape(-1).view(np.int16)).cuda()
+    sv = big[1:1 + s.size].view(n, k // 128)
+    y = host(q().qgemm_w3g128_smallM(dev(x), gpu_pack(c), sv))
+    yr, a = oracle.gemm(x, oracle.pack(c), s, k)
+    assert_close(y, yr, a, "qgemm scales view")
+
+
 def test_qgemm_m1_is_gemv_and_rows_repeat():
     n, k = 100, 2048
     c = synth.codes(71, n, k)
