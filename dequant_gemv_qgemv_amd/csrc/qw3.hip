@@ -1152,6 +1152,196 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #undef QW3_TILE_STORE
 #undef QW3_RING
 
+// ------------------------------------------ prefill, 256 x 256 output tiles --
+// Larger tiles for the MFMA-bound case.  Four waves, each owning 128 tokens x
+// 128 weight rows (64 MFMA tiles of 16 x 16, 256 accumulators).  Per group
+// (128 k) each wave decodes its 128 rows straight into the B operand
+// registers -- lane (n, j) decodes block j of row n of each 16-row sub-tile,
+// exactly (c-4) * 2^p, times the row-normalised scale s * 2^-E[n] (exact in
+// fp16) -- so only the activations go through LDS: each group's 256 x 128
+// fp16 tile is copied in by global_load_lds_dwordx4 one group ahead (XOR-
+// swizzled rows, double buffered).  The A operands are read by asm blocks
+// that wait for themselves (the compiler would drain the copies in flight
+// before every compiler-visible LDS read).  K may be split into C chunks
+// whose partial sums are added by qgemm_chunk_sum_kernel.
+// s_waitcnt immediate that constrains vmcnt only (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+#ifndef QW3_PF_MIN_M
+#define QW3_PF_MIN_M 129
+#endif
+constexpr int kPfBM = 256, kPfBN = 256;
+constexpr size_t kPfStage = (size_t)kPfBM * kTileRow;  // 64 KB of activations per group
+constexpr size_t kPfLds = 2 * kPfStage;
+
+typedef unsigned u32x3_t __attribute__((ext_vector_type(3)));
+typedef __attribute__((address_space(3))) void pf_lds_void_t;
+typedef __attribute__((address_space(1))) const void pf_gbl_void_t;
+
+__device__ __forceinline__ uint32_t pf_lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char *)p;
+}
+
+// A operands of one k-step for 8 token sub-tiles (rows r0 + 16 mi + lr).
+__device__ __forceinline__ void pf_read_a(const unsigned char *buf, int r0, int lr, int chunk, h8_t (&a)[8]) {
+    uint32_t ad[8];
+#pragma unroll
+    for (int mi = 0; mi < 8; ++mi) ad[mi] = pf_lds_addr(buf + tile_off(r0 + 16 * mi + lr, chunk));
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %9\n\t"
+        "ds_read_b128 %2, %10\n\t"
+        "ds_read_b128 %3, %11\n\t"
+        "ds_read_b128 %4, %12\n\t"
+        "ds_read_b128 %5, %13\n\t"
+        "ds_read_b128 %6, %14\n\t"
+        "ds_read_b128 %7, %15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]), "=&v"(a[5]), "=&v"(a[6]), "=&v"(a[7])
+        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7])
+        : "memory");
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void qgemm_pf_kernel(
+    const uint32_t *__restrict__ xq, const int *__restrict__ xe, const uint32_t *__restrict__ packed,
+    const uint16_t *__restrict__ scales, float *__restrict__ out, int M, int MT, int64_t N, int G, int C,
+    int64_t out_chunk) {
+    extern __shared__ __align__(16) unsigned char lds[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave & 1, wn = wave >> 1;
+    const int lr = lane & 15, lc = lane >> 4;
+    const int64_t NT = (N + kPfBN - 1) / kPfBN;
+    // chunk-major, then token tile, then row tile
+    const int chunk = (int)(blockIdx.x / (NT * MT));
+    const int64_t rest = blockIdx.x - (int64_t)chunk * NT * MT;
+    const int m_tile = (int)(rest / NT);
+    const int64_t n_tile = rest - (int64_t)m_tile * NT;
+    const int64_t n0 = n_tile * kPfBN;
+    const int m0 = m_tile * kPfBM;
+    const int Gc = G / C;
+    const int gbeg = chunk * Gc;
+    const int64_t K = (int64_t)G * kGroup;
+    const int64_t W = (int64_t)G * kWordsPerGroup;
+    float *y = out + (int64_t)chunk * out_chunk;
+
+    // This lane's 8 weight rows (one per 16-row sub-tile of the wave's 128).
+    int64_t rows[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int64_t r = n0 + wn * 128 + 16 * i + lr;
+        rows[i] = r < N ? r : N - 1;
+    }
+    // Row exponents over the chunk: the chunk's largest scale of each row maps
+    // to [8, 16).  The 4 lanes of a row scan a quarter of the groups each.
+    int en[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        uint32_t mx = 0;
+        for (int g = gbeg + lc; g < gbeg + Gc; g += 4) mx = max(mx, (uint32_t)scales[rows[i] * G + g] & 0x7FFFu);
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, 16));
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32));
+        en[i] = __builtin_amdgcn_frexp_expf(bf16_to_f32(mx)) - 4;
+    }
+
+    // Activation tile copies: instruction i of this wave fills LDS bytes
+    // [1024 (16 wave + i), +1024) = rows 4 (16 wave + i) + lane/16, physical
+    // chunk lane%16 (logical chunk = physical ^ (row & 15)).
+    auto dma_a = [&](int g, int buf) {
+        unsigned char *base = lds + (size_t)buf * kPfStage;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int blk = 16 * wave + i;
+            const int r = 4 * blk + (lane >> 4);
+            const int c = (lane & 15) ^ (r & 15);
+            const uint32_t *src = xq + (int64_t)(m0 + r) * (K / 2) + (int64_t)g * 64 + 4 * c;
+            __builtin_amdgcn_global_load_lds((pf_gbl_void_t *)src, (pf_lds_void_t *)(base + (size_t)blk * 1024), 16,
+                                             0, 0);
+        }
+    };
+    // Words of block lc of group g for the lane's 8 rows, and their scales.
+    uint32_t wcur[8][3], wnext[8][3], scur[8], snext[8];
+    auto load_w = [&](int g, uint32_t (&w)[8][3], uint32_t (&sc)[8]) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            // one 12-byte load per block (dwordx3)
+            const u32x3_t v = *reinterpret_cast<const u32x3_t *>(packed + rows[i] * W + (int64_t)g * kWordsPerGroup + 3 * lc);
+            w[i][0] = v.x;
+            w[i][1] = v.y;
+            w[i][2] = v.z;
+            sc[i] = scales[rows[i] * G + g];
+        }
+    };
+
+    f4_t acc[8][8];
+#pragma unroll
+    for (int mi = 0; mi < 8; ++mi)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[mi][i] = f4_t{0.f, 0.f, 0.f, 0.f};
+    const uint32_t magic = magic_vgpr();
+
+    dma_a(gbeg, 0);
+    load_w(gbeg, wcur, scur);
+    __builtin_amdgcn_s_waitcnt(0);  // all counters: the first group has landed
+    lds_barrier();
+    for (int g = gbeg; g < gbeg + Gc; ++g) {
+        const int buf = (g - gbeg) & 1;
+        const int gn = g + 1 < gbeg + Gc ? g + 1 : g;  // the last step re-reads (never used)
+        if (g + 1 < gbeg + Gc) dma_a(gn, buf ^ 1);
+        load_w(gn, wnext, snext);
+        // B operands of the group: 8 sub-tiles x 4 k-steps
+        h8_t bop[8][4];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            h2_t qd[16];
+            decode_block(wcur[i][0], wcur[i][1], wcur[i][2], magic, qd);
+            const _Float16 sv = (_Float16)ldexpf(bf16_to_f32(scur[i]), -en[i]);
+            const h2_t s2 = {sv, sv};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const h2_t p0 = qd[4 * u] * s2, p1 = qd[4 * u + 1] * s2, p2 = qd[4 * u + 2] * s2,
+                           p3 = qd[4 * u + 3] * s2;
+                bop[i][u] = h8_t{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+            }
+        }
+        const unsigned char *abuf = lds + (size_t)buf * kPfStage;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            h8_t a[8];
+            // k-chunk lc of step u: block lc, pairs 4u..4u+3 (as the B operand)
+            pf_read_a(abuf, wm * 128, lr, 4 * lc + u, a);
+#pragma unroll
+            for (int mi = 0; mi < 8; ++mi)
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    acc[mi][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mi], bop[i][u], acc[mi][i], 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            scur[i] = snext[i];
+#pragma unroll
+            for (int d = 0; d < 3; ++d) wcur[i][d] = wnext[i][d];
+        }
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's copies of the next group have landed
+        lds_barrier();
+    }
+
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int64_t row = n0 + wn * 128 + 16 * i + lr;
+#pragma unroll
+        for (int mi = 0; mi < 8; ++mi) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int tok = m0 + wm * 128 + 16 * mi + 4 * lc + r;
+                if (tok < M && row < N) y[(int64_t)tok * N + row] = ldexpf(acc[mi][i][r], en[i] + xe[tok]);
+            }
+        }
+    }
+}
+
 __global__ __launch_bounds__(256) void fill_zero_kernel(float *__restrict__ y, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i < n) y[i] = 0.f;
@@ -1314,6 +1504,48 @@ qw3_status launch_gemm_tile(const uint16_t *x, const uint32_t *packed, const uin
     return st;
 }
 
+// Prefill on 256 x 256 tiles: convert x once (per-token exponent), one tile
+// launch (K split into C chunks when the tiles alone would not fill the
+// GPU), and a chunk sum.
+qw3_status launch_gemm_pf(const uint16_t *x, const uint32_t *packed, const uint16_t *scales, float *y, int64_t M,
+                          int64_t N, int64_t K, hipStream_t stream) {
+    const int G = (int)(K / kGroup);
+    const int MT = (int)ceil_div(M, kPfBM);
+    const int64_t NT = ceil_div(N, kPfBN);
+    int cus = 0;
+    qw3_status st = cu_count(&cus);
+    if (st != QW3_OK) return st;
+    int C = 1;
+    while (NT * MT * C * 2 <= cus && G % (2 * C) == 0) C *= 2;
+    const int64_t Mp = (int64_t)MT * kPfBM;
+    const size_t xq_bytes = (size_t)Mp * (size_t)K * 2;
+    const size_t xe_bytes = ((size_t)Mp * sizeof(int) + 255) / 256 * 256;
+    const size_t part_bytes = C > 1 ? (size_t)C * (size_t)M * (size_t)N * sizeof(float) : 0;
+    void *scratch = nullptr;
+    hipError_t err = hipMallocAsync(&scratch, xq_bytes + xe_bytes + part_bytes, stream);
+    if (err != hipSuccess) return hip_fail(err);
+    uint32_t *xq = reinterpret_cast<uint32_t *>(scratch);
+    int *xe = reinterpret_cast<int *>(static_cast<char *>(scratch) + xq_bytes);
+    float *part = reinterpret_cast<float *>(static_cast<char *>(scratch) + xq_bytes + xe_bytes);
+    hipLaunchKernelGGL(prep_tile_x_kernel, dim3((unsigned)Mp), dim3(256), 0, stream, x, xq, xe, (int)M, K);
+    st = check_launch();
+    if (st == QW3_OK) {
+        float *dst = C > 1 ? part : y;
+        hipLaunchKernelGGL(qgemm_pf_kernel, dim3((unsigned)(NT * MT * C)), dim3(256), kPfLds, stream, xq, xe, packed,
+                           scales, dst, (int)M, MT, N, G, C, (int64_t)M * N);
+        st = check_launch();
+    }
+    if (st == QW3_OK && C > 1) {
+        const int64_t count = M * N;
+        hipLaunchKernelGGL(qgemm_chunk_sum_kernel, dim3((unsigned)ceil_div(count, 256)), dim3(256), 0, stream, part, y,
+                           count, C, count);
+        st = check_launch();
+    }
+    err = hipFreeAsync(scratch, stream);
+    if (st == QW3_OK && err != hipSuccess) st = hip_fail(err);
+    return st;
+}
+
 // Batched decode from registers (tokens <= 16 per pass), K in chunks of
 // WAVES x 8 groups.
 template <int WAVES>
@@ -1367,7 +1599,10 @@ qw3_status launch_gemm_mt(const uint16_t *x, const uint32_t *packed, const uint1
 qw3_status launch_gemm_small(const uint16_t *x, const uint32_t *packed, const uint16_t *scales, float *y,
                              int64_t M, int64_t N, int64_t K, hipStream_t stream) {
     const int G = (int)(K / kGroup);
-    if (M > 32) return launch_gemm_tile(x, packed, scales, y, M, N, K, stream);
+    if (M > 32) {
+        if (M >= QW3_PF_MIN_M) return launch_gemm_pf(x, packed, scales, y, M, N, K, stream);
+        return launch_gemm_tile(x, packed, scales, y, M, N, K, stream);
+    }
     // Batched decode: chunks of 8 waves x 8 groups (or 7 x 8 when K = 28672).
     if (G % 64 == 0) return launch_gemm_mt<8>(x, packed, scales, y, M, N, K, stream);
     if (G % 56 == 0) return launch_gemm_mt<7>(x, packed, scales, y, M, N, K, stream);

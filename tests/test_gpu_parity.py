@@ -244,6 +244,18 @@ def test_qgemm_chunked_k(m, n, k):
     assert_close(y, yr, a, "qgemm chunked M=%d %dx%d" % (m, n, k))
 
 
+@pytest.mark.parametrize("m,n,k", [(300, 72, 1024), (129, 300, 2048), (520, 260, 4096)])
+def test_qgemm_large_m_tiles(m, n, k):
+    # ragged 256-token and 256-row tiles, K split into chunks
+    say("qgemm large M", m, n, k)
+    c = synth.codes_all8(4700 + n + k, n, k)
+    s = synth.scales(4800 + k, n, k // 128, sigma=0.02, eps=1e-3)
+    x = synth.activations(4900 + m, m, k)
+    y = host(q().qgemm_w3g128_smallM(dev(x), gpu_pack(c), dev(s)))
+    yr, a = oracle.gemm(x, oracle.pack(c), s, k)
+    assert_close(y, yr, a, "qgemm large M=%d %dx%d" % (m, n, k))
+
+
 def test_qgemm_scales_view_not_16_byte_aligned():
     m, n, k = 6, 40, 8192
     c = synth.codes_all8(4600, n, k)
