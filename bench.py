@@ -147,10 +147,12 @@ def bench_extra(torch, q, steps, warmup):
     out = []
     layer = {}
     total_bytes, total_ms = 0, 0.0
+    kept = {}
     for name in ("q_proj", "k_proj", "v_proj", "o_proj", "gate_proj", "up_proj", "down_proj"):
         c, s, packed, scales = make_weight(torch, q, name)
         n, k = c.shape
         rot = Rotation(torch, packed, scales)
+        kept[name] = (rot, n, k)
         xd = torch.from_numpy(synth.layer_x(1, k).reshape(-1).view(np.int16)).cuda()
         y = torch.empty(n, dtype=torch.float32, device="cuda")
         ms_launch = time_steps(torch, lambda i: q.qgemv_w3g128(xd, rot[i][0], rot[i][1], out=y), steps, warmup)
@@ -174,13 +176,33 @@ def bench_extra(torch, q, steps, warmup):
                        "TFLOP/s": round(2.0 * m * n * k / ms_m / 1e9, 2)}
                 rec["MFMA_frac"] = round(rec["TFLOP/s"] / BF16_MFMA_PEAK_TFLOPS, 4)
                 out.append(rec)
-        del rot, packed, scales
-        torch.cuda.empty_cache()
+        del packed, scales
+    # The same layer with the projections that share an input fused into one
+    # launch each: q/k/v, o, gate/up, down (4 launches instead of 7).
+    x1 = torch.from_numpy(synth.layer_x(1, 8192).reshape(-1).view(np.int16)).cuda()
+    x2 = torch.from_numpy(synth.layer_x(1, 28672).reshape(-1).view(np.int16)).cuda()
+    ys = {nm: torch.empty(kept[nm][1], dtype=torch.float32, device="cuda") for nm in kept}
+
+    def fused_layer(i):
+        r = {nm: kept[nm][0][i] for nm in kept}
+        q.qgemv_w3g128_multi(x1, [r["q_proj"], r["k_proj"], r["v_proj"]],
+                             outs=[ys["q_proj"], ys["k_proj"], ys["v_proj"]])
+        q.qgemv_w3g128(x1, r["o_proj"][0], r["o_proj"][1], out=ys["o_proj"])
+        q.qgemv_w3g128_multi(x1, [r["gate_proj"], r["up_proj"]], outs=[ys["gate_proj"], ys["up_proj"]])
+        q.qgemv_w3g128(x2, r["down_proj"][0], r["down_proj"][1], out=ys["down_proj"])
+
+    fused_ms = graph_time(torch, fused_layer, 8, max(10, steps // 20), 3)
+    del kept
+    torch.cuda.empty_cache()
     out.insert(0, {"workload": "70B decoder layer, 7 projections back to back, B=1 (device time per call, "
                                "graph replay of 20 calls)",
                    "per_projection": layer, "layer_us_sum": round(total_ms * 1e3, 3),
                    "layer_GB/s": round(total_bytes / total_ms / 1e6, 1),
-                   "layer_HBM_frac": round(total_bytes / total_ms / 1e6 / HBM_PEAK_GBS, 4)})
+                   "layer_HBM_frac": round(total_bytes / total_ms / 1e6 / HBM_PEAK_GBS, 4),
+                   "fused_layer_us": round(fused_ms * 1e3, 3),
+                   "fused_layer_GB/s": round(total_bytes / fused_ms / 1e6, 1),
+                   "fused_layer_note": "q/k/v and gate/up each in one qgemv_w3g128_multi launch; "
+                                       "graph replay of 8 layers"})
     for rec in out:
         print(json.dumps(rec), file=sys.stderr, flush=True)
 

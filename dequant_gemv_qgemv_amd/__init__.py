@@ -23,6 +23,7 @@ __all__ = [
     "qpack_uint3",
     "qdequant_bf16",
     "qgemv_w3g128",
+    "qgemv_w3g128_multi",
     "qgemm_w3g128_smallM",
     "qstatus_str",
     "check_quantization_config",
@@ -35,16 +36,18 @@ __all__ = [
     "QW3_ERR_ALIGN",
     "QW3_ERR_HIP",
     "QW3_MAX_K",
+    "QW3_MAX_MULTI",
 ]
 
 QW3_OK, QW3_ERR_NULL, QW3_ERR_SHAPE, QW3_ERR_ALIGN, QW3_ERR_HIP = 0, -1, -2, -3, -4
 QW3_MAX_K = 131072
+QW3_MAX_MULTI = 4
 GROUP = 128
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libqw3.so")
-_EXPORTS = ("qpack_uint3", "qdequant_bf16", "qgemv_w3g128", "qgemm_w3g128_smallM",
-            "qstatus_str", "qw3_last_hip_error", "qw3_abi_version")
+_EXPORTS = ("qpack_uint3", "qdequant_bf16", "qgemv_w3g128", "qgemv_w3g128_multi",
+            "qgemm_w3g128_smallM", "qstatus_str", "qw3_last_hip_error", "qw3_abi_version")
 
 if not os.path.exists(_LIB_PATH):
     raise ImportError(
@@ -57,7 +60,8 @@ _lib.qpack_uint3.argtypes = [_vp, _vp, _i64, _i64, _vp]
 _lib.qdequant_bf16.argtypes = [_vp, _vp, _vp, _i64, _i64, _vp]
 _lib.qgemv_w3g128.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _vp]
 _lib.qgemm_w3g128_smallM.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]
-for _name in ("qpack_uint3", "qdequant_bf16", "qgemv_w3g128", "qgemm_w3g128_smallM"):
+_lib.qgemv_w3g128_multi.argtypes = [_vp, ctypes.c_int32, _vp, _vp, _vp, _vp, _i64, _vp]
+for _name in ("qpack_uint3", "qdequant_bf16", "qgemv_w3g128", "qgemv_w3g128_multi", "qgemm_w3g128_smallM"):
     getattr(_lib, _name).restype = ctypes.c_int
 _lib.qstatus_str.argtypes = [ctypes.c_int]
 _lib.qstatus_str.restype = ctypes.c_char_p
@@ -190,6 +194,44 @@ def qgemv_w3g128(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
         _check(_lib.qgemv_w3g128(_ptr(x), _ptr(packed), _ptr(scales), _ptr(out), n, k, _stream()),
                "qgemv_w3g128")
     return out
+
+
+def qgemv_w3g128_multi(x: torch.Tensor, weights, outs=None):
+    """qgemv_w3g128 for several matrices sharing x and K, in one launch.
+
+    weights: sequence of (packed, scales) pairs (1..QW3_MAX_MULTI); returns the
+    list of float32 outputs [N_i] (or fills `outs`)."""
+    weights = list(weights)
+    if not 1 <= len(weights) <= QW3_MAX_MULTI:
+        raise ValueError("1..%d matrices per call" % QW3_MAX_MULTI)
+    shapes = [_check_weight(p, s) for p, s in weights]
+    k = shapes[0][1]
+    if any(kk != k for _, kk in shapes):
+        raise ValueError("all matrices must have the same K")
+    dev = weights[0][0].device
+    if any(p.device != dev for p, _ in weights):
+        raise ValueError("all matrices must be on one device")
+    _need(x, "x", _BF16, 1)
+    if x.shape[0] != k or x.device != dev:
+        raise ValueError("x must be [%d] on %s" % (k, dev))
+    if outs is None:
+        outs = [torch.empty((n,), dtype=torch.float32, device=dev) for n, _ in shapes]
+    outs = list(outs)
+    if len(outs) != len(weights):
+        raise ValueError("one output per matrix")
+    for (n, _), o in zip(shapes, outs):
+        _need(o, "out", (torch.float32,), 1)
+        if o.shape[0] != n or o.device != dev:
+            raise ValueError("out must be [%d] on %s" % (n, dev))
+    cnt = len(weights)
+    arr_p = (ctypes.c_void_p * cnt)(*[_ptr(p) for p, _ in weights])
+    arr_s = (ctypes.c_void_p * cnt)(*[_ptr(s) for _, s in weights])
+    arr_y = (ctypes.c_void_p * cnt)(*[_ptr(o) for o in outs])
+    arr_n = (ctypes.c_int64 * cnt)(*[n for n, _ in shapes])
+    with torch.cuda.device(dev):
+        _check(_lib.qgemv_w3g128_multi(_ptr(x), cnt, arr_p, arr_s, arr_y, arr_n, k, _stream()),
+               "qgemv_w3g128_multi")
+    return outs
 
 
 def qgemm_w3g128_smallM(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,

@@ -306,9 +306,6 @@ __global__ __launch_bounds__(256) void qdequant_kernel(const uint32_t *__restric
 #ifndef QW3_GEMV_DEPTH
 #define QW3_GEMV_DEPTH 3
 #endif
-#ifndef QW3_GEMV_DEFER
-#define QW3_GEMV_DEFER 0
-#endif
 constexpr int kGemvDepth = QW3_GEMV_DEPTH;
 #ifndef QW3_GEMV_WGS
 #define QW3_GEMV_WGS 256
@@ -454,24 +451,54 @@ __device__ __forceinline__ void xstage_lane(const uint16_t *__restrict__ x, int 
     if (!lane_on) e = 0;
 }
 
+// Up to 4 weight matrices with the same K that share one activation vector
+// (e.g. the q, k and v projections of a layer) in one launch (one activation
+// staging): the workgroups are dealt to the matrices in proportion to their
+// rows, so each workgroup works on one matrix and its pointers stay uniform.
+constexpr int kMaxSegs = 4;
+struct GemvSegs {
+    const uint32_t *packed[kMaxSegs];
+    const uint16_t *scales[kMaxSegs];
+    float *y[kMaxSegs];
+    int64_t rows[kMaxSegs];
+    int blk_end[kMaxSegs];  // cumulative workgroup counts; unused entries repeat the total
+};
+
+template <typename P>
+__device__ __forceinline__ P seg_pick(const P (&v)[kMaxSegs], int k) {
+    return k == 0 ? v[0] : (k == 1 ? v[1] : (k == 2 ? v[2] : v[3]));
+}
+
 // Teams of T <= 64 lanes (T a power of two >= G): the reduction is DPP only.
 // Order of the prologue: activation loads, then the first D rows, then the
 // conversion (which waits only for the activation loads).
-template <int T>
+template <int T, bool MULTI>
 __global__ __launch_bounds__(kGemvWGS) QW3_GEMV_OCC void qgemv_small_kernel(const uint16_t *__restrict__ x,
-                                                               const uint32_t *__restrict__ packed,
-                                                               const uint16_t *__restrict__ scales,
-                                                               float *__restrict__ y, int64_t N, int G,
-                                                               int lds_x) {
+                                                               const GemvSegs sg, int G, int lds_x) {
     constexpr int R = kGemvWGS / T;
     constexpr int D = kGemvDepth;
     extern __shared__ uint32_t smem[];
+    // This workgroup's matrix (workgroup-uniform) and its place among the
+    // workgroups of that matrix.
+    int kseg = 0, blk = blockIdx.x, nblk = gridDim.x;
+    if constexpr (MULTI) {
+        kseg = ((int)blockIdx.x >= sg.blk_end[0]) + ((int)blockIdx.x >= sg.blk_end[1]) +
+               ((int)blockIdx.x >= sg.blk_end[2]);
+        const int b0 = kseg == 0 ? 0 : seg_pick(sg.blk_end, kseg - 1);
+        blk = blockIdx.x - b0;
+        nblk = seg_pick(sg.blk_end, kseg) - b0;
+    }
+    const uint32_t *__restrict__ packed = MULTI ? seg_pick(sg.packed, kseg) : sg.packed[0];
+    const uint16_t *__restrict__ scales = MULTI ? seg_pick(sg.scales, kseg) : sg.scales[0];
+    float *__restrict__ y = MULTI ? seg_pick(sg.y, kseg) : sg.y[0];
+    const int64_t N = MULTI ? seg_pick(sg.rows, kseg) : sg.rows[0];
     const int gl = threadIdx.x % T;
     const bool lane_on = gl < G;
     const int g_load = lane_on ? gl : G - 1;
     const int64_t W = (int64_t)G * kWordsPerGroup;
-    const int64_t stride = (int64_t)gridDim.x * R;
-    const int64_t row0 = (int64_t)blockIdx.x * R + threadIdx.x / T;
+    const int64_t stride = (int64_t)nblk * R;
+    const int64_t row0 = (int64_t)blk * R + threadIdx.x / T;
+    auto load = [&](int64_t r, RowBuf &rb) { load_row(packed, scales, r, N, W, G, g_load, rb); };
 
     // Ring of E = D + 1 row buffers.  Step i first issues the loads of row
     // i + D into the buffer that step i - 1 finished with, then decodes row i:
@@ -485,46 +512,27 @@ __global__ __launch_bounds__(kGemvWGS) QW3_GEMV_OCC void qgemv_small_kernel(cons
         XStage<1> st;  // 4G <= 256 <= blockDim: one block per thread
         xstage_issue<1>(x, G, st);
 #pragma unroll
-        for (int d = 0; d < D; ++d) load_row(packed, scales, row0 + d * stride, N, W, G, g_load, ring[d]);
+        for (int d = 0; d < D; ++d) load(row0 + d * stride, ring[d]);
         xstage_convert<1>(st, G, smem);
         __syncthreads();
         xstage_fetch(smem, G, gl, lane_on, xp, e);
     } else {
 #pragma unroll
-        for (int d = 0; d < D; ++d) load_row(packed, scales, row0 + d * stride, N, W, G, g_load, ring[d]);
+        for (int d = 0; d < D; ++d) load(row0 + d * stride, ring[d]);
         xstage_lane(x, gl, lane_on, xp, e);
     }
     const uint32_t magic = magic_vgpr();
 
     for (int64_t row = row0; row < N; row += E * stride) {
-#if QW3_GEMV_DEFER
-        // Decode all E rows first, then reduce them together: the E DPP chains
-        // are independent, so they fill each other's wait states.
-        float part[E];
 #pragma unroll
         for (int i = 0; i < E; ++i) {
             const int64_t r = row + i * stride;
-            load_row(packed, scales, r + D * stride, N, W, G, g_load, ring[(i + D) % E]);
-            __builtin_amdgcn_sched_barrier(0);
-            part[i] = row_partial(ring[i], xp, e, magic);
-        }
-#pragma unroll
-        for (int i = 0; i < E; ++i) {
-            const int64_t r = row + i * stride;
-            const float tot = segment_sum<T>(part[i]);
-            if (gl == T - 1 && r < N) y[r] = tot;
-        }
-#else
-#pragma unroll
-        for (int i = 0; i < E; ++i) {
-            const int64_t r = row + i * stride;
-            load_row(packed, scales, r + D * stride, N, W, G, g_load, ring[(i + D) % E]);
+            load(r + D * stride, ring[(i + D) % E]);
             __builtin_amdgcn_sched_barrier(0);
             const float part = row_partial(ring[i], xp, e, magic);
             const float tot = segment_sum<T>(part);
             if (gl == T - 1 && r < N) y[r] = tot;
         }
-#endif
     }
 }
 
@@ -1406,24 +1414,49 @@ qw3_status blocks_per_cu(const void *kernel, int wgs, size_t lds, int *out) {
 #ifndef QW3_GEMV_BPC
 #define QW3_GEMV_BPC 1
 #endif
-template <int T>
-qw3_status launch_gemv_small(const uint16_t *x, const uint32_t *packed, const uint16_t *scales, float *y,
-                             int64_t N, int G, hipStream_t stream) {
+template <int T, bool MULTI>
+qw3_status launch_gemv_small(const uint16_t *x, GemvSegs sg, int count, int G, hipStream_t stream) {
     constexpr int R = kGemvWGS / T;
     const size_t xs_bytes = (size_t)G * 64 * 4 + (size_t)G * 4;
     const bool lds_x = xs_bytes <= kMaxLdsX;
     const size_t lds = lds_x ? xs_bytes : 0;
-    const void *kern = reinterpret_cast<const void *>(&qgemv_small_kernel<T>);
+    const void *kern = reinterpret_cast<const void *>(&qgemv_small_kernel<T, MULTI>);
     int cus = 0, per_cu = 0;
     qw3_status st = cu_count(&cus);
     if (st == QW3_OK) st = blocks_per_cu(kern, kGemvWGS, lds, &per_cu);
     if (st != QW3_OK) return st;
     if (QW3_GEMV_BPC > 0 && per_cu > QW3_GEMV_BPC) per_cu = QW3_GEMV_BPC;
-    int64_t blocks = ceil_div(N, R);
-    if (blocks > (int64_t)cus * per_cu) blocks = (int64_t)cus * per_cu;
-    hipLaunchKernelGGL(qgemv_small_kernel<T>, dim3((unsigned)blocks), dim3(kGemvWGS), lds, stream, x, packed,
-                       scales, y, N, G, lds_x ? 1 : 0);
+    const int64_t budget = (int64_t)cus * per_cu;
+    int64_t tot = 0;
+    for (int i = 0; i < count; ++i) tot += sg.rows[i];
+    // Workgroups per matrix: in proportion to its rows (rounded down, so the
+    // total stays within one workgroup per CU), at least one for a non-empty
+    // matrix, at most one per R rows.
+    int64_t blocks = 0;
+    for (int i = 0; i < kMaxSegs; ++i) {
+        int64_t b = 0;
+        if (i < count && sg.rows[i] > 0) {
+            b = budget * sg.rows[i] / tot;
+            const int64_t cap = ceil_div(sg.rows[i], R);
+            b = b < 1 ? 1 : (b > cap ? cap : b);
+        }
+        blocks += b;
+        sg.blk_end[i] = (int)blocks;
+    }
+    hipLaunchKernelGGL((qgemv_small_kernel<T, MULTI>), dim3((unsigned)blocks), dim3(kGemvWGS), lds, stream, x, sg,
+                       G, lds_x ? 1 : 0);
     return check_launch();
+}
+
+template <bool MULTI>
+qw3_status launch_gemv_small_any(const uint16_t *x, const GemvSegs &sg, int count, int G, hipStream_t stream) {
+    if (G <= 1) return launch_gemv_small<1, MULTI>(x, sg, count, G, stream);
+    if (G <= 2) return launch_gemv_small<2, MULTI>(x, sg, count, G, stream);
+    if (G <= 4) return launch_gemv_small<4, MULTI>(x, sg, count, G, stream);
+    if (G <= 8) return launch_gemv_small<8, MULTI>(x, sg, count, G, stream);
+    if (G <= 16) return launch_gemv_small<16, MULTI>(x, sg, count, G, stream);
+    if (G <= 32) return launch_gemv_small<32, MULTI>(x, sg, count, G, stream);
+    return launch_gemv_small<64, MULTI>(x, sg, count, G, stream);
 }
 
 qw3_status launch_gemv_big(const uint16_t *x, const uint32_t *packed, const uint16_t *scales, float *y,
@@ -1468,14 +1501,43 @@ qw3_status launch_gemv_big(const uint16_t *x, const uint32_t *packed, const uint
 qw3_status launch_gemv(const uint16_t *x, const uint32_t *packed, const uint16_t *scales, float *y,
                        int64_t N, int64_t K, hipStream_t stream) {
     const int G = (int)(K / kGroup);
-    if (G <= 1) return launch_gemv_small<1>(x, packed, scales, y, N, G, stream);
-    if (G <= 2) return launch_gemv_small<2>(x, packed, scales, y, N, G, stream);
-    if (G <= 4) return launch_gemv_small<4>(x, packed, scales, y, N, G, stream);
-    if (G <= 8) return launch_gemv_small<8>(x, packed, scales, y, N, G, stream);
-    if (G <= 16) return launch_gemv_small<16>(x, packed, scales, y, N, G, stream);
-    if (G <= 32) return launch_gemv_small<32>(x, packed, scales, y, N, G, stream);
-    if (G <= 64) return launch_gemv_small<64>(x, packed, scales, y, N, G, stream);
+    if (G <= 64) {
+        GemvSegs sg = {};
+        sg.packed[0] = packed;
+        sg.scales[0] = scales;
+        sg.y[0] = y;
+        sg.rows[0] = N;
+        return launch_gemv_small_any<false>(x, sg, 1, G, stream);
+    }
     return launch_gemv_big(x, packed, scales, y, N, G, stream);
+}
+
+// Several matrices sharing x: one launch when rows fit one wave (K <= 8192),
+// else one launch per matrix.
+qw3_status launch_gemv_multi(const uint16_t *x, int count, const uint32_t *const *packed,
+                             const uint16_t *const *scales, float *const *y, const int64_t *N, int64_t K,
+                             hipStream_t stream) {
+    const int G = (int)(K / kGroup);
+    if (G > 64) {
+        for (int i = 0; i < count; ++i) {
+            if (N[i] == 0) continue;
+            const qw3_status st = launch_gemv(x, packed[i], scales[i], y[i], N[i], K, stream);
+            if (st != QW3_OK) return st;
+        }
+        return QW3_OK;
+    }
+    GemvSegs sg = {};
+    int64_t tot = 0;
+    for (int i = 0; i < kMaxSegs; ++i) {
+        const int j = i < count ? i : count - 1;
+        sg.packed[i] = packed[j];
+        sg.scales[i] = scales[j];
+        sg.y[i] = y[j];
+        sg.rows[i] = i < count ? N[i] : 0;
+        tot += sg.rows[i];
+    }
+    if (tot == 0) return QW3_OK;
+    return launch_gemv_small_any<true>(x, sg, count, G, stream);
 }
 
 // Prefill: convert x once (per-token exponent), then one tile GEMM launch.
@@ -1677,6 +1739,40 @@ qw3_status qgemv_w3g128(const uint16_t *x, const int32_t *packed, const uint16_t
     if (!x || !packed || !scales) return QW3_ERR_NULL;
     if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scales, 2)) return QW3_ERR_ALIGN;
     return launch_gemv(x, reinterpret_cast<const uint32_t *>(packed), scales, y, N, K, (hipStream_t)hip_stream);
+}
+
+qw3_status qgemv_w3g128_multi(const uint16_t *x, int32_t count, const int32_t *const *packed,
+                              const uint16_t *const *scales, float *const *y, const int64_t *N, int64_t K,
+                              void *hip_stream) {
+    if (count < 1 || count > QW3_MAX_MULTI) return QW3_ERR_SHAPE;
+    if (!packed || !scales || !y || !N) return QW3_ERR_NULL;
+    int64_t tot = 0;
+    for (int i = 0; i < count; ++i) {
+        const qw3_status st = check_shape(N[i], K);
+        if (st != QW3_OK) return st;
+        tot += N[i];
+    }
+    if (tot == 0) return QW3_OK;
+    for (int i = 0; i < count; ++i) {
+        if (N[i] == 0) continue;
+        if (!y[i]) return QW3_ERR_NULL;
+        if (!aligned(y[i], 4)) return QW3_ERR_ALIGN;
+        if (K == 0) continue;
+        if (!packed[i] || !scales[i]) return QW3_ERR_NULL;
+        if (!aligned(packed[i], 16) || !aligned(scales[i], 2)) return QW3_ERR_ALIGN;
+    }
+    if (K == 0) {
+        for (int i = 0; i < count; ++i) {
+            if (N[i] == 0) continue;
+            const qw3_status st = fill_zero(y[i], N[i], (hipStream_t)hip_stream);
+            if (st != QW3_OK) return st;
+        }
+        return QW3_OK;
+    }
+    if (!x) return QW3_ERR_NULL;
+    if (!aligned(x, 16)) return QW3_ERR_ALIGN;
+    return launch_gemv_multi(x, count, reinterpret_cast<const uint32_t *const *>(packed), scales, y, N, K,
+                             (hipStream_t)hip_stream);
 }
 
 qw3_status qgemm_w3g128_smallM(const uint16_t *x, const int32_t *packed, const uint16_t *scales, float *y,

@@ -92,6 +92,25 @@ qw3_status qdequant_bf16(const int32_t *packed, const uint16_t *scales, uint16_t
 qw3_status qgemv_w3g128(const uint16_t *x, const int32_t *packed, const uint16_t *scales,
                         float *y, int64_t N, int64_t K, void *hip_stream);
 
+/* Largest number of matrices in one qgemv_w3g128_multi call. */
+#define QW3_MAX_MULTI 4
+
+/*
+ * qgemv_w3g128_multi -- qgemv_w3g128 for `count` (1..QW3_MAX_MULTI) matrices
+ * that share one activation vector and the same K, e.g. the q, k and v
+ * projections of a decoder layer, in one launch (one activation staging):
+ *   x [K] bf16; for i < count: packed[i] [N[i], 3K/32] int32,
+ *   scales[i] [N[i], K/128] bf16, y[i] [N[i]] float32, written.
+ * `packed`, `scales`, `y` and `N` are HOST arrays of `count` entries holding
+ * device pointers (and row counts).  Each y[i] equals what qgemv_w3g128 gives
+ * for matrix i, bit for bit.  Validation and errors as for qgemv_w3g128 (a
+ * count outside 1..QW3_MAX_MULTI is QW3_ERR_SHAPE); N[i] == 0 skips matrix i.
+ * For K > 8192 the matrices are launched one after another.
+ */
+qw3_status qgemv_w3g128_multi(const uint16_t *x, int32_t count, const int32_t *const *packed,
+                              const uint16_t *const *scales, float *const *y, const int64_t *N,
+                              int64_t K, void *hip_stream);
+
 /*
  * qgemm_w3g128_smallM -- fused product for M activation rows, Y = X dequant(W)^T.
  *   x [M, K] bf16 (row stride K), packed [N, 3K/32] int32, scales [N, K/128] bf16
@@ -99,9 +118,11 @@ qw3_status qgemv_w3g128(const uint16_t *x, const int32_t *packed, const uint16_t
  * Any M >= 0 is accepted.  M == 1 runs the batch-1 kernel; small M streams
  * the weights once for the whole batch through bf16-exact fp16 matrix-core
  * products; large M (prefill) runs a tiled matrix-core kernel.  For M > 1 the
- * call borrows a temporary device buffer of about 2*M*K + M*K/128 bytes from
- * the stream-ordered allocator of `hip_stream` and releases it on the same
- * stream.  Same accuracy bound as qgemv_w3g128.
+ * call borrows a temporary device buffer from the stream-ordered allocator of
+ * `hip_stream` and releases it on the same stream: the activations converted
+ * to fp16 (2 bytes per element, M rounded up to 16 or 256) plus, when K is
+ * split across workgroups, fp32 partial sums (4 bytes per output element and
+ * K chunk).  Same accuracy bound as qgemv_w3g128.
  */
 qw3_status qgemm_w3g128_smallM(const uint16_t *x, const int32_t *packed,
                                const uint16_t *scales, float *y, int64_t M, int64_t N,

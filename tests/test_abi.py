@@ -122,3 +122,32 @@ def test_quantization_config_descriptor():
     del cfg["b_dtype"]
     with pytest.raises(ValueError):
         q.check_quantization_config(cfg)
+
+
+def _arr(ctype, vals):
+    return (ctype * len(vals))(*vals)
+
+
+def test_multi_validation():
+    lib = q.raw()
+    lib.qgemv_w3g128_multi.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    P = _arr(ctypes.c_void_p, [0x10000, 0x20000])
+    Sc = _arr(ctypes.c_void_p, [0x30000, 0x40000])
+    Y = _arr(ctypes.c_void_p, [0x50000, 0x60000])
+    n = _arr(ctypes.c_int64, [4, 8])
+    assert lib.qgemv_w3g128_multi(A16, 0, P, Sc, Y, n, 128, S) == q.QW3_ERR_SHAPE
+    assert lib.qgemv_w3g128_multi(A16, q.QW3_MAX_MULTI + 1, P, Sc, Y, n, 128, S) == q.QW3_ERR_SHAPE
+    assert lib.qgemv_w3g128_multi(A16, 2, None, Sc, Y, n, 128, S) == q.QW3_ERR_NULL
+    assert lib.qgemv_w3g128_multi(A16, 2, P, Sc, Y, None, 128, S) == q.QW3_ERR_NULL
+    assert lib.qgemv_w3g128_multi(A16, 2, P, Sc, Y, _arr(ctypes.c_int64, [4, -1]), 128, S) == q.QW3_ERR_SHAPE
+    assert lib.qgemv_w3g128_multi(A16, 2, P, Sc, Y, n, 100, S) == q.QW3_ERR_SHAPE
+    assert lib.qgemv_w3g128_multi(NULL, 2, P, Sc, Y, n, 128, S) == q.QW3_ERR_NULL
+    assert lib.qgemv_w3g128_multi(MIS, 2, P, Sc, Y, n, 128, S) == q.QW3_ERR_ALIGN
+    Pm = _arr(ctypes.c_void_p, [0x10000, 0x20008])
+    assert lib.qgemv_w3g128_multi(A16, 2, Pm, Sc, Y, n, 128, S) == q.QW3_ERR_ALIGN
+    Yn = _arr(ctypes.c_void_p, [0x50000, 0])
+    assert lib.qgemv_w3g128_multi(A16, 2, P, Sc, Yn, n, 128, S) == q.QW3_ERR_NULL
+    # all matrices empty: valid, nothing enqueued
+    z = _arr(ctypes.c_int64, [0, 0])
+    assert lib.qgemv_w3g128_multi(NULL, 2, P, Sc, Y, z, 128, S) == q.QW3_OK

@@ -218,6 +218,42 @@ def test_binding_rejects_misaligned_view():
     assert ei.value.status == mod.QW3_ERR_ALIGN
 
 
+# -------------------------------------------------- several matrices, one x --
+
+@pytest.mark.parametrize("k,ns", [(8192, (300, 40, 40)), (1024, (5, 0, 77, 130)), (2048, (64,)),
+                                  (28672, (40, 24))])
+def test_qgemv_multi_matches_single(k, ns):
+    say("qgemv multi", k, ns)
+    x = synth.activations(5000 + k, 1, k)
+    xd = dev(x.reshape(-1))
+    mats = []
+    for i, n in enumerate(ns):
+        c = synth.codes_all8(5100 + i, n, k)
+        s = synth.scales(5200 + i, n, k // 128, sigma=0.02, eps=1e-3)
+        mats.append((c, s, gpu_pack(c), dev(s)))
+    ys = [host(o) for o in q().qgemv_w3g128_multi(xd, [(p, sd) for _, _, p, sd in mats])]
+    for (c, s, p, sd), y in zip(mats, ys):
+        assert np.array_equal(y.view(np.uint32), host(q().qgemv_w3g128(xd, p, sd)).view(np.uint32))
+        if c.shape[0]:
+            yr, a = oracle.gemm(x, oracle.pack(c), s, k)
+            assert_close(y[None, :], yr, a, "multi")
+
+
+def test_qgemv_multi_qkv_full_size():
+    names = ("q_proj", "k_proj", "v_proj")
+    k = synth.LAYER_70B["q_proj"][1]
+    x = synth.layer_x(1, k)
+    xd = dev(x.reshape(-1))
+    mats = [layer(nm) for nm in names]
+    packed = [gpu_pack(c) for c, _ in mats]
+    say("qgemv multi q/k/v full size")
+    ys = q().qgemv_w3g128_multi(xd, [(p, dev(s)) for p, (_, s) in zip(packed, mats)])
+    for (c, s), y in zip(mats, ys):
+        rows = sample_rows(c.shape[0], seed=3)
+        yr, a = oracle.gemm(x, oracle.pack(c[rows]), s[rows], k)
+        assert_close(host(y)[None, rows], yr, a, "multi full size")
+
+
 # ------------------------------------------------------------- small M ----
 
 @pytest.mark.parametrize("m", [2, 3, 4, 8, 16, 17, 31, 32, 33, 64, 100])
