@@ -472,11 +472,10 @@ __device__ __forceinline__ P seg_pick(const P (&v)[kMaxSegs], int k) {
 // Teams of T <= 64 lanes (T a power of two >= G): the reduction is DPP only.
 // Order of the prologue: activation loads, then the first D rows, then the
 // conversion (which waits only for the activation loads).
-template <int T, bool MULTI>
+template <int T, bool MULTI, int D>
 __global__ __launch_bounds__(kGemvWGS) QW3_GEMV_OCC void qgemv_small_kernel(const uint16_t *__restrict__ x,
                                                                const GemvSegs sg, int G, int lds_x) {
     constexpr int R = kGemvWGS / T;
-    constexpr int D = kGemvDepth;
     extern __shared__ uint32_t smem[];
     // This workgroup's matrix (workgroup-uniform) and its place among the
     // workgroups of that matrix.
@@ -1420,7 +1419,7 @@ qw3_status launch_gemv_small(const uint16_t *x, GemvSegs sg, int count, int G, h
     const size_t xs_bytes = (size_t)G * 64 * 4 + (size_t)G * 4;
     const bool lds_x = xs_bytes <= kMaxLdsX;
     const size_t lds = lds_x ? xs_bytes : 0;
-    const void *kern = reinterpret_cast<const void *>(&qgemv_small_kernel<T, MULTI>);
+    const void *kern = reinterpret_cast<const void *>(&qgemv_small_kernel<T, MULTI, kGemvDepth>);
     int cus = 0, per_cu = 0;
     qw3_status st = cu_count(&cus);
     if (st == QW3_OK) st = blocks_per_cu(kern, kGemvWGS, lds, &per_cu);
@@ -1443,8 +1442,15 @@ qw3_status launch_gemv_small(const uint16_t *x, GemvSegs sg, int count, int G, h
         blocks += b;
         sg.blk_end[i] = (int)blocks;
     }
-    hipLaunchKernelGGL((qgemv_small_kernel<T, MULTI>), dim3((unsigned)blocks), dim3(kGemvWGS), lds, stream, x, sg,
-                       G, lds_x ? 1 : 0);
+    // Waves with at most two rows each keep one row in flight instead of
+    // kGemvDepth (deeper rings would only re-read the last row).
+    const int64_t rows_per_wave = ceil_div(tot, blocks * R);
+    if (rows_per_wave <= 2)
+        hipLaunchKernelGGL((qgemv_small_kernel<T, MULTI, 1>), dim3((unsigned)blocks), dim3(kGemvWGS), lds, stream, x,
+                           sg, G, lds_x ? 1 : 0);
+    else
+        hipLaunchKernelGGL((qgemv_small_kernel<T, MULTI, kGemvDepth>), dim3((unsigned)blocks), dim3(kGemvWGS), lds,
+                           stream, x, sg, G, lds_x ? 1 : 0);
     return check_launch();
 }
 
