@@ -545,12 +545,14 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // its T/32 halves in order.  One barrier per D + 1 rows.  1024-thread
 // workgroups (K > 65536) keep a single row in flight to stay within 128 VGPRs.  The LDS holds the
 // converted activations first, then (after a barrier) the half sums.
-template <int MAXWGS, int D>
+// LDS_X: the converted activations fit in LDS (K <= 32768); otherwise each
+// lane converts its own group.  A template parameter, so that one prologue
+// reaches the loop and the loop's waits are exact.
+template <int MAXWGS, int D, bool LDS_X>
 __global__ __launch_bounds__(MAXWGS) QW3_GEMV_OCC void qgemv_big_kernel(const uint16_t *__restrict__ x,
                                                          const uint32_t *__restrict__ packed,
                                                          const uint16_t *__restrict__ scales,
-                                                         float *__restrict__ y, int64_t N, int G, int T,
-                                                         int lds_x) {
+                                                         float *__restrict__ y, int64_t N, int G, int T) {
     extern __shared__ uint32_t smem[];
     const int tid = threadIdx.x;
     const int wgs = blockDim.x;
@@ -569,18 +571,26 @@ __global__ __launch_bounds__(MAXWGS) QW3_GEMV_OCC void qgemv_big_kernel(const ui
     uint32_t xp[64];
     int e = 0;
     RowBuf ring[E];
-    if (lds_x) {
+    if constexpr (LDS_X) {
         XStage<4> st;  // 4G <= 4 * blockDim (T >= G, blockDim >= T)
         xstage_issue<4>(x, G, st);
 #pragma unroll
-        for (int d = 0; d < D; ++d) load_row(packed, scales, row0 + d * stride, N, W, G, g_load, ring[d]);
+        for (int d = 0; d < D; ++d) {
+            __builtin_amdgcn_sched_barrier(0);  // rows issued in ring order
+            load_row(packed, scales, row0 + d * stride, N, W, G, g_load, ring[d]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
         xstage_convert<4>(st, G, smem);
         __syncthreads();
         xstage_fetch(smem, G, gl, lane_on, xp, e);
         __syncthreads();  // LDS is reused for the half sums below
     } else {
 #pragma unroll
-        for (int d = 0; d < D; ++d) load_row(packed, scales, row0 + d * stride, N, W, G, g_load, ring[d]);
+        for (int d = 0; d < D; ++d) {
+            __builtin_amdgcn_sched_barrier(0);
+            load_row(packed, scales, row0 + d * stride, N, W, G, g_load, ring[d]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
         xstage_lane(x, gl, lane_on, xp, e);
     }
     const uint32_t magic = magic_vgpr();
@@ -614,6 +624,163 @@ __global__ __launch_bounds__(MAXWGS) QW3_GEMV_OCC void qgemv_big_kernel(const ui
             }
         }
         parity ^= 1;
+    }
+}
+
+// ------------------------------------- batch 1, K = 8192, on the matrix cores --
+// The same fused GEMV with the dot products on v_mfma_f32_16x16x32_f16, which
+// leaves two VALU ops per weight pair (the exact decode) instead of three.
+// Workgroups of four waves walk 16-row tiles; wave w owns the 16 groups
+// 16q + 4w + j (q, j = 0..3) of every row of a tile, so the four waves together
+// cover K = 8192 and a tile's super-step q reads bytes [768q, 768q + 768) of
+// each of its rows.  In super-step q, lane (n, j) (n = lane % 16, j = lane / 16)
+// decodes group 16q + 4w + j of row n straight into the B operand (k chunk j
+// of 8 weights, 4 MFMAs per 32-code block).  The A operand is x' and stays in
+// 64 VGPRs for the whole kernel: row m = 4q' + j' of A carries the activations
+// of group 16q' + 4w + j' in k chunk j' and zero elsewhere.  So output row
+// 4q' + j' only ever sums products of group 16q' + 4w + j' activations; in
+// super-step q the rows 4q..4q+3 hold the partial sums of groups 16q + 4w + r
+// (r = 0..3) exactly apart, in lane row q, and the other 12 rows are discarded.
+// Those four partials are multiplied by their group scale (and the
+// activation exponent) and accumulated in fp32.  The wave's per-row partials
+// are summed across lane rows with permlane swaps and across the four waves
+// through LDS, in a fixed order, once per batch of tiles.  Loads run three
+// super-steps ahead in a register ring, as in qgemv_small_kernel.
+constexpr int kMfGroups = 64;
+#ifndef QW3_MF_BATCH
+#define QW3_MF_BATCH 8
+#endif
+#ifndef QW3_MF_ILV
+#define QW3_MF_ILV 1
+#endif
+constexpr int kMfBatch = QW3_MF_BATCH;  // tiles per cross-wave reduction
+constexpr size_t kMfLds = (size_t)kMfGroups * 64 * 4 + (size_t)kMfGroups * 4 + 2 * kMfBatch * 4 * 16 * sizeof(float);
+typedef unsigned u32x2v_t __attribute__((ext_vector_type(2)));
+struct MfSlot {
+    u32x4v_t a, b, c;  // the lane's 12 words of one group of one row
+    u32x2v_t s;        // (super-step 0 only) the bf16 scales of the lane's four groups of lane row j
+};
+
+// First of the four groups that wave w handles in super-step q.
+__device__ __forceinline__ int mf_group(int w, int q) { return QW3_MF_ILV ? 16 * q + 4 * w : 16 * w + 4 * q; }
+
+template <bool MULTI>
+__global__ __launch_bounds__(256) void qgemv_mfma_kernel(const uint16_t *__restrict__ x, const GemvSegs sg) {
+    constexpr int G = kMfGroups;
+    constexpr int64_t W = (int64_t)G * kWordsPerGroup;
+    extern __shared__ uint32_t smem[];
+    float *red = reinterpret_cast<float *>(smem + G * 64 + G);  // [2][kMfBatch][4 waves][16 rows]
+    int kseg = 0, blk = blockIdx.x, nblk = gridDim.x;
+    if constexpr (MULTI) {
+        kseg = ((int)blockIdx.x >= sg.blk_end[0]) + ((int)blockIdx.x >= sg.blk_end[1]) +
+               ((int)blockIdx.x >= sg.blk_end[2]);
+        const int b0 = kseg == 0 ? 0 : seg_pick(sg.blk_end, kseg - 1);
+        blk = blockIdx.x - b0;
+        nblk = seg_pick(sg.blk_end, kseg) - b0;
+    }
+    const uint32_t *__restrict__ packed = MULTI ? seg_pick(sg.packed, kseg) : sg.packed[0];
+    const uint16_t *__restrict__ scales = MULTI ? seg_pick(sg.scales, kseg) : sg.scales[0];
+    float *__restrict__ y = MULTI ? seg_pick(sg.y, kseg) : sg.y[0];
+    const int64_t N = MULTI ? seg_pick(sg.rows, kseg) : sg.rows[0];
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n = lane & 15, lj = lane >> 4;
+    const int64_t my_tiles = (((N + 15) >> 4) - blk + nblk - 1) / nblk;  // >= 1: at most one workgroup per tile
+    // Unconditional loads (see load_row): tiles past the last re-read it, rows past N read row N - 1.
+    auto load = [&](int64_t it, int q, MfSlot &sl) {
+        it = it < my_tiles ? it : my_tiles - 1;
+        int64_t r = (blk + it * nblk) * 16 + n;
+        r = r < N ? r : N - 1;
+        const u32x4v_t *p = reinterpret_cast<const u32x4v_t *>(packed + r * W + (mf_group(w, q) + lj) * kWordsPerGroup);
+        sl.a = p[0];
+        sl.b = p[1];
+        sl.c = p[2];
+        if (q == 0) sl.s = *reinterpret_cast<const u32x2v_t *>(scales + r * G + mf_group(w, lj));
+    };
+    MfSlot ring[4];
+    XStage<1> st;
+    xstage_issue<1>(x, G, st);
+    // Issued strictly in ring order: the waits in the loop count on it.
+    load(0, 0, ring[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    load(0, 1, ring[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    load(0, 2, ring[2]);
+    __builtin_amdgcn_sched_barrier(0);
+    xstage_convert<1>(st, G, smem);
+    __syncthreads();
+    h8_t xa[16];  // step t = 4 * block + u: pairs 4u .. 4u + 3 of 32-code block `block`
+    float fe[4];  // 2^e of the groups 16 lj + 4w + r whose partials this lane scales
+    {
+        const bool on = (n & 3) == lj;
+        const int ga = mf_group(w, n >> 2) + lj;
+        const uint4 *xs4 = reinterpret_cast<const uint4 *>(smem);
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            const uint4 v = xs4[t * G + ga];
+            xa[t] = on ? __builtin_bit_cast(h8_t, v) : h8_t{0, 0, 0, 0, 0, 0, 0, 0};
+        }
+        const int *xe = reinterpret_cast<const int *>(smem + G * 64);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) fe[r] = ldexpf(1.0f, xe[mf_group(w, lj) + r]);
+    }
+    const uint32_t magic = magic_vgpr();
+    for (int64_t it = 0; it < my_tiles; ++it) {
+        float acc[4] = {0.f, 0.f, 0.f, 0.f}, sc[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            // ring slot q holds super-step q of this tile; refill the slot freed
+            // by the previous super-step with the one three ahead
+            load(it + (q + 3) / 4, (q + 3) & 3, ring[(q + 3) & 3]);
+            __builtin_amdgcn_sched_barrier(0);
+            const MfSlot &sl = ring[q];
+            if (q == 0) {
+                sc[0] = bf16_to_f32(sl.s.x & 0xFFFFu) * fe[0];
+                sc[1] = __uint_as_float(sl.s.x & 0xFFFF0000u) * fe[1];
+                sc[2] = bf16_to_f32(sl.s.y & 0xFFFFu) * fe[2];
+                sc[3] = __uint_as_float(sl.s.y & 0xFFFF0000u) * fe[3];
+            }
+            const uint32_t wd[12] = {sl.a.x, sl.a.y, sl.a.z, sl.a.w, sl.b.x, sl.b.y,
+                                     sl.b.z, sl.b.w, sl.c.x, sl.c.y, sl.c.z, sl.c.w};
+            f4_t d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                h2_t qd[16];
+                decode_block(wd[3 * b], wd[3 * b + 1], wd[3 * b + 2], magic, qd);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const h8_t bop = {qd[4 * u].x,     qd[4 * u].y,     qd[4 * u + 1].x, qd[4 * u + 1].y,
+                                      qd[4 * u + 2].x, qd[4 * u + 2].y, qd[4 * u + 3].x, qd[4 * u + 3].y};
+                    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[4 * b + u], bop, d, 0, 0, 0);
+                }
+            }
+            if (lj == q) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[r] = fmaf(d[r], sc[r], acc[r]);
+            }
+        }
+        // Row n's partial over the wave's 16 groups: the four lane rows, then LDS.
+        float part = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+        part = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+        const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+        part = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+        const int bt = (int)(it % kMfBatch);
+        float *rb = red + ((it / kMfBatch) & 1) * (kMfBatch * 64);
+        if (lj == 0) rb[bt * 64 + w * 16 + n] = part;
+        if (bt == kMfBatch - 1 || it == my_tiles - 1) {
+            // The batch's partials are in LDS (lgkmcnt) before the barrier; the
+            // loads of the next tiles stay in flight.  The other half of `red`
+            // is written next, so one barrier per batch suffices.
+            lds_barrier();
+            const int i = threadIdx.x;
+            if (i < (bt + 1) * 16) {
+                const float *rr = rb + (i >> 4) * 64 + (i & 15);
+                const float tot = (rr[0] + rr[16]) + (rr[32] + rr[48]);
+                const int64_t row = (blk + (it - bt + (i >> 4)) * nblk) * 16 + (i & 15);
+                if (row < N) y[row] = tot;
+            }
+        }
     }
 }
 
@@ -1487,21 +1654,63 @@ qw3_status launch_gemv_big(const uint16_t *x, const uint32_t *packed, const uint
     constexpr int kBigD = kGemvDepth, kHugeD = 1;
     const size_t red_bytes = 2 * (size_t)((wgs <= 512 ? kBigD : kHugeD) + 1) * (wgs / 32) * sizeof(float);
     const size_t lds = (lds_x && xs_bytes > red_bytes) ? xs_bytes : red_bytes;
-    const void *kern = wgs <= 512 ? reinterpret_cast<const void *>(&qgemv_big_kernel<512, kBigD>)
-                                  : reinterpret_cast<const void *>(&qgemv_big_kernel<1024, kHugeD>);
+    const void *kern =
+        wgs <= 512 ? (lds_x ? reinterpret_cast<const void *>(&qgemv_big_kernel<512, kBigD, true>)
+                            : reinterpret_cast<const void *>(&qgemv_big_kernel<512, kBigD, false>))
+                   : (lds_x ? reinterpret_cast<const void *>(&qgemv_big_kernel<1024, kHugeD, true>)
+                            : reinterpret_cast<const void *>(&qgemv_big_kernel<1024, kHugeD, false>));
     int cus = 0, per_cu = 0;
     qw3_status st = cu_count(&cus);
     if (st == QW3_OK) st = blocks_per_cu(kern, wgs, lds, &per_cu);
     if (st != QW3_OK) return st;
     int64_t blocks = ceil_div(N, R);
     if (blocks > (int64_t)cus * per_cu) blocks = (int64_t)cus * per_cu;
-    if (wgs <= 512)
-        hipLaunchKernelGGL((qgemv_big_kernel<512, kBigD>), dim3((unsigned)blocks), dim3(wgs), lds, stream, x, packed, scales,
-                           y, N, G, T, lds_x ? 1 : 0);
-    else
-        hipLaunchKernelGGL((qgemv_big_kernel<1024, kHugeD>), dim3((unsigned)blocks), dim3(wgs), lds, stream, x, packed,
-                           scales, y, N, G, T, lds_x ? 1 : 0);
+    hipLaunchKernelGGL(reinterpret_cast<void (*)(const uint16_t *, const uint32_t *, const uint16_t *, float *,
+                                                 int64_t, int, int)>(const_cast<void *>(kern)),
+                       dim3((unsigned)blocks), dim3(wgs), lds, stream, x, packed, scales, y, N, G, T);
     return check_launch();
+}
+
+// The matrix-core GEMV (K = 8192 only): one workgroup per CU, workgroups dealt
+// to the matrices in proportion to their 16-row tiles, at least one and at
+// most one per tile each.
+#ifndef QW3_GEMV_MFMA
+#define QW3_GEMV_MFMA 1
+#endif
+template <bool MULTI>
+qw3_status launch_gemv_mfma(const uint16_t *x, GemvSegs sg, int count, hipStream_t stream) {
+    int cus = 0;
+    const qw3_status st = cu_count(&cus);
+    if (st != QW3_OK) return st;
+    int64_t tiles[kMaxSegs], tot = 0;
+    for (int i = 0; i < kMaxSegs; ++i) {
+        tiles[i] = i < count ? ceil_div(sg.rows[i], 16) : 0;
+        tot += tiles[i];
+    }
+    int64_t blocks = 0;
+    for (int i = 0; i < kMaxSegs; ++i) {
+        int64_t b = 0;
+        if (tiles[i] > 0) {
+            b = (int64_t)cus * tiles[i] / tot;
+            b = b < 1 ? 1 : (b > tiles[i] ? tiles[i] : b);
+        }
+        blocks += b;
+        sg.blk_end[i] = (int)blocks;
+    }
+    hipLaunchKernelGGL((qgemv_mfma_kernel<MULTI>), dim3((unsigned)blocks), dim3(256), kMfLds, stream, x, sg);
+    return check_launch();
+}
+
+// Whether the matrix-core GEMV takes a matrix: K = 8192, scale rows 8-byte
+// aligned (8-byte scale loads) and at least four 16-row tiles per CU (with
+// fewer it is no faster than the lane-per-group kernel).  The choice depends
+// on the matrix alone, so a matrix gets the same kernel -- and the same bits --
+// from qgemv_w3g128 and from qgemv_w3g128_multi.
+bool gemv_mfma_takes(int G, const uint16_t *scales, int64_t N) {
+    if (!QW3_GEMV_MFMA || G != kMfGroups || N == 0 || !aligned(scales, 8)) return false;
+    int cus = 0;
+    if (cu_count(&cus) != QW3_OK) return false;
+    return ceil_div(N, 16) >= 4 * (int64_t)cus;
 }
 
 qw3_status launch_gemv(const uint16_t *x, const uint32_t *packed, const uint16_t *scales, float *y,
@@ -1513,6 +1722,7 @@ qw3_status launch_gemv(const uint16_t *x, const uint32_t *packed, const uint16_t
         sg.scales[0] = scales;
         sg.y[0] = y;
         sg.rows[0] = N;
+        if (gemv_mfma_takes(G, scales, N)) return launch_gemv_mfma<false>(x, sg, 1, stream);
         return launch_gemv_small_any<false>(x, sg, 1, G, stream);
     }
     return launch_gemv_big(x, packed, scales, y, N, G, stream);
@@ -1532,18 +1742,31 @@ qw3_status launch_gemv_multi(const uint16_t *x, int count, const uint32_t *const
         }
         return QW3_OK;
     }
-    GemvSegs sg = {};
-    int64_t tot = 0;
-    for (int i = 0; i < kMaxSegs; ++i) {
-        const int j = i < count ? i : count - 1;
-        sg.packed[i] = packed[j];
-        sg.scales[i] = scales[j];
-        sg.y[i] = y[j];
-        sg.rows[i] = i < count ? N[i] : 0;
-        tot += sg.rows[i];
+    // The matrices the matrix-core kernel takes go in one launch, the others
+    // in one launch of the lane-per-group kernel.
+    for (int pass = 0; pass < 2; ++pass) {
+        GemvSegs sg = {};
+        int cnt = 0;
+        for (int i = 0; i < count; ++i) {
+            if (N[i] == 0 || gemv_mfma_takes(G, scales[i], N[i]) != (pass == 0)) continue;
+            sg.packed[cnt] = packed[i];
+            sg.scales[cnt] = scales[i];
+            sg.y[cnt] = y[i];
+            sg.rows[cnt] = N[i];
+            ++cnt;
+        }
+        if (cnt == 0) continue;
+        for (int i = cnt; i < kMaxSegs; ++i) {
+            sg.packed[i] = sg.packed[cnt - 1];
+            sg.scales[i] = sg.scales[cnt - 1];
+            sg.y[i] = sg.y[cnt - 1];
+            sg.rows[i] = 0;
+        }
+        const qw3_status st = pass == 0 ? launch_gemv_mfma<true>(x, sg, cnt, stream)
+                                        : launch_gemv_small_any<true>(x, sg, cnt, G, stream);
+        if (st != QW3_OK) return st;
     }
-    if (tot == 0) return QW3_OK;
-    return launch_gemv_small_any<true>(x, sg, count, G, stream);
+    return QW3_OK;
 }
 
 // Prefill: convert x once (per-token exponent), then one tile GEMM launch.

@@ -218,10 +218,102 @@ def test_binding_rejects_misaligned_view():
     assert ei.value.status == mod.QW3_ERR_ALIGN
 
 
+# ------------------------------------ batch 1 on the matrix cores, K = 8192 --
+# qgemv_w3g128 runs its matrix-core kernel for K = 8192 when the matrix has at
+# least four 16-row tiles per CU (N >= 16384 rows on a 256-CU part) and its
+# scale rows are 8-byte aligned; these cases are sized to take it.
+
+MF_K = 8192
+
+
+@pytest.mark.parametrize("n", [16411, 17000])
+def test_qgemv_mfma_parity_all_codes(n):
+    say("qgemv matrix cores", n, MF_K)
+    c = synth.codes_all8(7000 + n, n, MF_K)
+    s = synth.scales(7100 + n, n, MF_K // 128, sigma=0.02, eps=1e-3)
+    x = synth.activations(7200 + n, 1, MF_K)
+    y = run_gemv(c, s, x)
+    yr, a = ref_gemv(c, s, x)
+    assert_close(y, yr, a, "qgemv matrix cores %dx%d" % (n, MF_K))
+
+
+def test_qgemv_mfma_zero_rows_and_one_hot():
+    """Rows of code 4 give exact zeros; one nonzero weight per row, anywhere
+    in the row, gives the exact product."""
+    n = 16400
+    c = np.full((n, MF_K), 4, dtype=np.uint8)
+    odd = np.arange(1, n, 2)
+    col = (odd * 131) % MF_K  # every group, block and pair slot
+    c[odd, col] = 7  # q = +3
+    s = synth.scales(71, n, MF_K // 128, sigma=0.1, eps=1e-3)
+    say("qgemv matrix cores zero rows")
+    x3 = np.full((1, MF_K), 0x4040, dtype=np.uint16)  # 3.0 everywhere
+    y = run_gemv(c, s, x3)
+    assert np.all(y[0::2] == 0.0)
+    sf = synth.bf16_bits_to_f32(s)
+    assert np.array_equal(y[odd], (9.0 * sf[odd, col // 128]).astype(np.float32))
+    x = synth.activations(72, 1, MF_K)
+    y = run_gemv(c, s, x)
+    assert np.all(y[0::2] == 0.0)
+    yr, a = ref_gemv(c, s, x)
+    assert_close(y, yr, a, "matrix cores one-hot")
+
+
+def test_qgemv_mfma_wide_activation_range():
+    n = 16400
+    c = synth.codes_all8(73, n, MF_K)
+    s = synth.scales(74, n, MF_K // 128, sigma=0.05, eps=1e-3)
+    rng = np.random.default_rng(75)
+    xf = rng.standard_normal(MF_K).astype(np.float32)
+    xf[:128] *= np.float32(2.0 ** 60)
+    xf[128:256] *= np.float32(2.0 ** -60)
+    xf[256:384] *= np.exp2(rng.integers(-12, 12, 128)).astype(np.float32)
+    xf[384:512] = 0.0
+    xf[4096:4224] *= np.float32(2.0 ** -100)
+    x = synth.f32_to_bf16_bits(xf)
+    say("qgemv matrix cores wide range")
+    y = run_gemv(c, s, x)
+    yr, a = ref_gemv(c, s, x)
+    assert_close(y, yr, a, "matrix cores wide range")
+
+
+@pytest.mark.parametrize("offset_elems", [4, 1])
+def test_qgemv_mfma_scale_views(offset_elems):
+    """Scales 8-byte aligned but not 16 (matrix cores), and only 2-byte aligned
+    (the lane-per-group kernel takes the matrix): both match the oracle."""
+    n = 16400
+    c = synth.codes(76, n, MF_K)
+    s = synth.scales(77, n, MF_K // 128)
+    x = synth.activations(78, 1, MF_K)
+    packed, xd = gpu_pack(c), dev(x.reshape(-1))
+    base = torch.zeros(n * 64 + 8, dtype=torch.int16, device="cuda")
+    view = base[offset_elems:offset_elems + n * 64].view(n, 64)
+    view.copy_(dev(s))
+    say("qgemv matrix cores scale view offset", offset_elems)
+    y = host(q().qgemv_w3g128(xd, packed, view))
+    yr, a = ref_gemv(c, s, x)
+    assert_close(y, yr, a, "scale view +%d" % offset_elems)
+    y_al = host(q().qgemv_w3g128(xd, packed, dev(s)))
+    if offset_elems == 4:
+        assert np.array_equal(y.view(np.uint32), y_al.view(np.uint32))
+
+
+def test_qgemv_mfma_deterministic():
+    n = 16400
+    c = synth.codes(79, n, MF_K)
+    s = synth.scales(80, n, MF_K // 128)
+    x = synth.activations(81, 1, MF_K)
+    say("qgemv matrix cores determinism")
+    packed, sd, xd = gpu_pack(c), dev(s), dev(x.reshape(-1))
+    y1 = host(q().qgemv_w3g128(xd, packed, sd))
+    y2 = host(q().qgemv_w3g128(xd, packed, sd))
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+
+
 # -------------------------------------------------- several matrices, one x --
 
 @pytest.mark.parametrize("k,ns", [(8192, (300, 40, 40)), (1024, (5, 0, 77, 130)), (2048, (64,)),
-                                  (28672, (40, 24))])
+                                  (28672, (40, 24)), (8192, (16411, 300, 0, 17000)), (8192, (16400, 16411))])
 def test_qgemv_multi_matches_single(k, ns):
     say("qgemv multi", k, ns)
     x = synth.activations(5000 + k, 1, k)
