@@ -124,6 +124,38 @@ def cpu_baseline(c, s, x, k, budget_s=2.5):
     }
 
 
+def cpu_rate(c, s, k, m, step):
+    """The oracle's rate (algorithmic GB/s) over every `step`-th row, M rows of x."""
+    import oracle
+    import synth
+    rows = np.arange(0, c.shape[0], step, dtype=np.int64)
+    words = oracle.pack(c[rows])
+    sc = np.ascontiguousarray(s[rows])
+    x = synth.layer_x(m, k)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.gemm(x, words, sc, k)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= 0.3:
+            break
+    return {"GB/s": round(gemv_bytes(rows.size, k, m) * reps / dt / 1e9, 4), "cores": oracle.num_threads()}
+
+
+def cpu_one_thread():
+    """The oracle's gate_proj rate on one host thread (a child process with
+    OMP_NUM_THREADS=1, every 64th row)."""
+    import subprocess
+    code = ("import sys; sys.path.insert(0, %r); import bench, synth, json; "
+            "c, s = synth.layer_weights('gate_proj'); "
+            "print(json.dumps(bench.cpu_rate(c, s, c.shape[1], 1, step=64)))" % ROOT)
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    res = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=300)
+    if res.returncode != 0:
+        return None
+    return json.loads(res.stdout.strip().splitlines()[-1])["GB/s"]
+
+
 def graph_time(torch, fn, reps: int, replays: int, warmup: int):
     """Per-call device time of fn(i), i = 0..reps-1, captured once in a HIP graph
     and replayed: host launch overhead (which exceeds the run time of the small
@@ -148,9 +180,14 @@ def bench_extra(torch, q, steps, warmup):
     layer = {}
     total_bytes, total_ms = 0, 0.0
     kept = {}
+    cpu_layer, cpu_m32 = {}, None
     for name in ("q_proj", "k_proj", "v_proj", "o_proj", "gate_proj", "up_proj", "down_proj"):
         c, s, packed, scales = make_weight(torch, q, name)
         n, k = c.shape
+        cpu_layer[name] = cpu_rate(c, s, k, 1, step=16)
+        if name == "gate_proj":
+            cpu_m32 = cpu_rate(c, s, k, 32, step=64)
+        del c
         rot = Rotation(torch, packed, scales)
         kept[name] = (rot, n, k)
         xd = torch.from_numpy(synth.layer_x(1, k).reshape(-1).view(np.int16)).cuda()
@@ -164,6 +201,7 @@ def bench_extra(torch, q, steps, warmup):
         total_bytes += b
         total_ms += ms
         if name in ("gate_proj", "down_proj"):
+            fused_512 = None
             for m in (4, 8, 16, 32, 512):
                 xm = torch.from_numpy(synth.layer_x(m, k).view(np.int16)).cuda()
                 ym = torch.empty((m, n), dtype=torch.float32, device="cuda")
@@ -176,6 +214,9 @@ def bench_extra(torch, q, steps, warmup):
                        "TFLOP/s": round(2.0 * m * n * k / ms_m / 1e9, 2)}
                 rec["MFMA_frac"] = round(rec["TFLOP/s"] / BF16_MFMA_PEAK_TFLOPS, 4)
                 out.append(rec)
+                if m == 512:
+                    fused_512 = ms_m
+            out.append(dense_branch(torch, q, name, n, k, rot, fused_512))
         del packed, scales
     # The same layer with the projections that share an input fused into one
     # launch each: q/k/v, o, gate/up, down (4 launches instead of 7).
@@ -203,8 +244,69 @@ def bench_extra(torch, q, steps, warmup):
                    "fused_layer_GB/s": round(total_bytes / fused_ms / 1e6, 1),
                    "fused_layer_note": "q/k/v and gate/up each in one qgemv_w3g128_multi launch; "
                                        "graph replay of 8 layers"})
+    cpu_ms = sum(gemv_bytes(*synth.LAYER_70B[nm][:2]) / (r["GB/s"] * 1e6) for nm, r in cpu_layer.items())
+    out.append({"workload": "oracle on the host (fp64, OpenMP over rows): one decoder layer at B=1, "
+                            "every 16th row of each projection timed, the layer time scaled from those rates",
+                "per_projection_GB/s": {nm: r["GB/s"] for nm, r in cpu_layer.items()},
+                "layer_ms": round(cpu_ms, 2), "cores": cpu_layer["gate_proj"]["cores"],
+                "gate_proj_M32_GB/s": cpu_m32["GB/s"],
+                "gate_proj_1_thread_GB/s": cpu_one_thread()})
     for rec in out:
         print(json.dumps(rec), file=sys.stderr, flush=True)
+
+
+def dense_branch(torch, q, name, n, k, rot, fused_ms):
+    """Prefill the unfused way, for comparison with the fused tile kernel:
+    qdequant_bf16 writes the dense bf16 weight, then a library bf16 GEMM
+    (torch linear, hipBLASLt) multiplies the M = 512 activations by it."""
+    import synth
+    m = 512
+    wd = torch.empty((n, k), dtype=torch.bfloat16, device="cuda")
+    x = torch.from_numpy(synth.layer_x(m, k).view(np.int16)).cuda().view(torch.bfloat16)
+    ms_deq = time_steps(torch, lambda i: q.qdequant_bf16(rot[i][0], rot[i][1], out=wd), 20, 3)
+    ms_mm = time_steps(torch, lambda i: torch.nn.functional.linear(x, wd), 20, 3)
+    del wd, x
+    torch.cuda.empty_cache()
+    tot = ms_deq + ms_mm
+    return {"workload": "%s M=512 dense branch: qdequant_bf16, then bf16 GEMM (torch linear)" % name,
+            "dequant_us": round(ms_deq * 1e3, 3), "gemm_us": round(ms_mm * 1e3, 3),
+            "dense_total_us": round(tot * 1e3, 3), "fused_us": round(fused_ms * 1e3, 3),
+            "fused_speedup": round(tot / fused_ms, 3),
+            "gemm_TFLOP/s": round(2.0 * m * n * k / ms_mm / 1e9, 2)}
+
+
+def read_sweep_ceiling(torch):
+    """A plain streaming-read kernel (libqw3_ceiling.so) over slices of a 1 GiB
+    buffer the size of the gate_proj weights + scales, rotated so no slice is
+    cache resident: the read rate HBM gives a kernel on this part."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "dequant_gemv_qgemv_amd", "libqw3_ceiling.so"))
+    lib.qw3_read_sweep.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                                   ctypes.c_void_p]
+    lib.qw3_read_sweep.restype = ctypes.c_int
+    buf = torch.ones(256 * 2 ** 20, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+    n, k = 28672, 8192
+    nbytes = (n * (3 * k // 32) * 4 + n * (k // 128) * 2) // 16 * 16
+    slices = buf.numel() * 4 // nbytes
+    base = buf.data_ptr()
+    stream = torch.cuda.current_stream().cuda_stream
+    best = None
+    for blocks in (512, 1024, 2048):
+        def step(i, blocks=blocks):
+            rc = lib.qw3_read_sweep(base + (i % slices) * nbytes, nbytes, blocks, sink.data_ptr(), stream)
+            if rc != 0:
+                raise RuntimeError("qw3_read_sweep failed: %d" % rc)
+        ms = time_steps(torch, step, 400, 40)
+        if best is None or ms < best[0]:
+            best = (ms, blocks)
+    rec = {"workload": "ceiling: streaming read of %d-byte slices of a 1 GiB buffer (%d slices rotated)"
+                       % (nbytes, slices),
+           "read_GB/s": round(nbytes / best[0] / 1e6, 1), "us_per_slice": round(best[0] * 1e3, 3),
+           "workgroups": best[1]}
+    print(json.dumps(rec), file=sys.stderr, flush=True)
+    del buf, sink
+    return rec
 
 
 def read_copy_ceiling(torch):
@@ -219,6 +321,34 @@ def read_copy_ceiling(torch):
     del src, dst
 
 
+def run_case(torch, q, case: str, steps: int, warmup: int):
+    """One projection of the 70B layer at M rows of activations, stream launches."""
+    import synth
+    name, m = case.split(":")
+    m = int(m)
+    if name not in synth.LAYER_70B or m < 1:
+        raise SystemExit("--case wants NAME:M with NAME one of %s" % ", ".join(synth.LAYER_70B))
+    c, s, packed, scales = make_weight(torch, q, name)
+    n, k = c.shape
+    del c, s
+    rot = Rotation(torch, packed, scales)
+    x = torch.from_numpy(synth.layer_x(m, k).view(np.int16)).cuda()
+    if m == 1:
+        x = x.reshape(-1)
+        y = torch.empty(n, dtype=torch.float32, device="cuda")
+        fn = lambda i: q.qgemv_w3g128(x, rot[i][0], rot[i][1], out=y)  # noqa: E731
+    else:
+        y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+        fn = lambda i: q.qgemm_w3g128_smallM(x, rot[i][0], rot[i][1], out=y)  # noqa: E731
+    ms = time_steps(torch, fn, steps, warmup)
+    b = gemv_bytes(n, k, m)
+    tf = 2.0 * m * n * k / ms / 1e9
+    print(json.dumps({"workload": "%s [%d, %d] M=%d" % (name, n, k, m), "steps": steps, "us": round(ms * 1e3, 3),
+                      "GB/s": round(b / ms / 1e6, 1), "HBM_frac": round(b / ms / 1e6 / HBM_PEAK_GBS, 4),
+                      "TFLOP/s": round(tf, 2), "MFMA_frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                      "algorithmic_bytes": b}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -230,7 +360,11 @@ def main():
                     help="first run 5 plain 256 MiB device copies (torch copy_), the known-size "
                          "reference for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE counters")
     ap.add_argument("--ceiling", action="store_true",
-                    help="also time a plain 1 GiB device copy and print its GB/s on stderr")
+                    help="also time a plain 1 GiB device copy and a streaming-read kernel and print "
+                         "their GB/s on stderr")
+    ap.add_argument("--case", metavar="NAME:M",
+                    help="time one other workload instead of the default line, e.g. gate_proj:16 or "
+                         "down_proj:512 (for profiling); prints its JSON line on stdout")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
@@ -252,8 +386,14 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    ceiling = None
     if args.ceiling:
         read_copy_ceiling(torch)
+        ceiling = read_sweep_ceiling(torch)
+
+    if args.case:
+        run_case(torch, q, args.case, args.steps, args.warmup)
+        return
 
     n, k = synth.LAYER_70B["gate_proj"][:2]
     c, s, packed, scales = make_weight(torch, q, "gate_proj")
@@ -265,6 +405,11 @@ def main():
     ms = time_steps(torch, lambda i: q.qgemv_w3g128(xd, rot[i][0], rot[i][1], out=y), args.steps, args.warmup)
     nbytes = gemv_bytes(n, k)
     gbs = nbytes / ms / 1e6
+    if ceiling is not None:
+        print(json.dumps({"workload": "gate_proj GEMV against the streaming-read ceiling",
+                          "gemv_GB/s": round(gbs, 1), "read_ceiling_GB/s": ceiling["read_GB/s"],
+                          "frac_of_read_ceiling": round(gbs / ceiling["read_GB/s"], 4)}),
+              file=sys.stderr, flush=True)
     line = {
         "metric": METRIC,
         "value": round(gbs, 2),

@@ -225,11 +225,9 @@ __device__ __forceinline__ void load_x32(const uint16_t *src, uint4 (&xb)[4]) {
 }
 
 // ------------------------------------------------------------- qpack -------
-// One thread per (row, group): 128 codes in, 12 words out.
-__global__ __launch_bounds__(256) void qpack_kernel(const uint8_t *__restrict__ codes,
-                                                    uint32_t *__restrict__ packed, int64_t units) {
-    const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (u >= units) return;
+// One thread per (row, group): 128 codes in, 12 words out (grid-stride loop).
+__device__ __forceinline__ void pack_group(const uint8_t *__restrict__ codes, uint32_t *__restrict__ packed,
+                                           int64_t u) {
     const uint4 *src = reinterpret_cast<const uint4 *>(codes + u * kGroup);
     uint32_t words[kWordsPerGroup];
     uint64_t acc = 0;
@@ -256,6 +254,12 @@ __global__ __launch_bounds__(256) void qpack_kernel(const uint8_t *__restrict__ 
     dst[2] = make_uint4(words[8], words[9], words[10], words[11]);
 }
 
+__global__ __launch_bounds__(256) void qpack_kernel(const uint8_t *__restrict__ codes,
+                                                    uint32_t *__restrict__ packed, int64_t units) {
+    for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < units; u += (int64_t)gridDim.x * 256)
+        pack_group(codes, packed, u);
+}
+
 // ----------------------------------------------------------- qdequant -----
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     const uint32_t u = __float_as_uint(f);
@@ -263,33 +267,33 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// One thread per (row, group): 12 words + 1 scale in, 128 bf16 out.
+// Chunk i of 8 consecutive weights: group i / 16 (row-major groups: row n's
+// group g is group n * G + g), from bit 24 * (i % 16) of it (at most two
+// words), to one 16-byte store.
+__device__ __forceinline__ void dequant_chunk(const uint32_t *__restrict__ packed, const uint16_t *__restrict__ scales,
+                                              uint16_t *__restrict__ w_out, int64_t i) {
+    const int64_t u = i >> 4;
+    const int b0 = 24 * (int)(i & 15);
+    const int j = b0 >> 5;
+    const uint32_t *gw = packed + u * kWordsPerGroup;
+    const uint32_t lo = gw[j];
+    const uint32_t hi = gw[j < kWordsPerGroup - 1 ? j + 1 : j];  // the last chunk sits in word 11 alone
+    const uint32_t field = (uint32_t)(((((uint64_t)hi) << 32) | lo) >> (b0 & 31));
+    const float s = bf16_to_f32(scales[u]);
+    uint32_t h[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) h[t] = f32_to_bf16_rne((float)((int)((field >> (3 * t)) & 7u) - 4) * s);
+    reinterpret_cast<uint4 *>(w_out)[i] =
+        make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+}
+
+// Consecutive threads take consecutive chunks, so their 16-byte stores are
+// contiguous; grid-stride loop for any size.
 __global__ __launch_bounds__(256) void qdequant_kernel(const uint32_t *__restrict__ packed,
                                                        const uint16_t *__restrict__ scales,
-                                                       uint16_t *__restrict__ w_out, int64_t units) {
-    const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (u >= units) return;
-    const uint4 *src = reinterpret_cast<const uint4 *>(packed + u * kWordsPerGroup);
-    const uint4 a = src[0], b = src[1], c = src[2];
-    const uint32_t w[kWordsPerGroup] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w, c.x, c.y, c.z, c.w};
-    const float s = bf16_to_f32(scales[u]);
-    uint4 *dst = reinterpret_cast<uint4 *>(w_out + u * kGroup);
-#pragma unroll
-    for (int o = 0; o < 16; ++o) {  // 8 outputs per 16-byte store
-        uint32_t h[8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const int k = 8 * o + t;
-            const int bit = 3 * k;
-            const uint64_t pair = (bit >> 5) + 1 < kWordsPerGroup
-                                      ? ((uint64_t)w[(bit >> 5) + 1] << 32) | w[bit >> 5]
-                                      : (uint64_t)w[bit >> 5];
-            const int c3 = (int)((pair >> (bit & 31)) & 7u);
-            h[t] = f32_to_bf16_rne((float)(c3 - 4) * s);
-        }
-        dst[o] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                            h[6] | (h[7] << 16));
-    }
+                                                       uint16_t *__restrict__ w_out, int64_t chunks) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < chunks; i += (int64_t)gridDim.x * 256)
+        dequant_chunk(packed, scales, w_out, i);
 }
 
 // ------------------------------------------------------------ qgemv -------
@@ -1939,7 +1943,8 @@ qw3_status qpack_uint3(const uint8_t *codes, int32_t *packed, int64_t N, int64_t
     if (!codes || !packed) return QW3_ERR_NULL;
     if (!aligned(codes, 16) || !aligned(packed, 16)) return QW3_ERR_ALIGN;
     const int64_t units = N * (K / kGroup);
-    hipLaunchKernelGGL(qpack_kernel, dim3((unsigned)ceil_div(units, 256)), dim3(256), 0,
+    const int64_t blocks = ceil_div(units, 256);
+    hipLaunchKernelGGL(qpack_kernel, dim3((unsigned)(blocks < (1 << 20) ? blocks : (1 << 20))), dim3(256), 0,
                        (hipStream_t)hip_stream, codes, reinterpret_cast<uint32_t *>(packed), units);
     return check_launch();
 }
@@ -1951,9 +1956,10 @@ qw3_status qdequant_bf16(const int32_t *packed, const uint16_t *scales, uint16_t
     if (N == 0 || K == 0) return QW3_OK;
     if (!packed || !scales || !w_out) return QW3_ERR_NULL;
     if (!aligned(packed, 16) || !aligned(w_out, 16) || !aligned(scales, 2)) return QW3_ERR_ALIGN;
-    const int64_t units = N * (K / kGroup);
-    hipLaunchKernelGGL(qdequant_kernel, dim3((unsigned)ceil_div(units, 256)), dim3(256), 0,
-                       (hipStream_t)hip_stream, reinterpret_cast<const uint32_t *>(packed), scales, w_out, units);
+    const int64_t chunks = N * (K / kGroup) * 16;  // 8 weights each
+    const int64_t blocks = ceil_div(chunks, 256);
+    hipLaunchKernelGGL(qdequant_kernel, dim3((unsigned)(blocks < (1 << 20) ? blocks : (1 << 20))), dim3(256), 0,
+                       (hipStream_t)hip_stream, reinterpret_cast<const uint32_t *>(packed), scales, w_out, chunks);
     return check_launch();
 }
 
