@@ -1089,6 +1089,148 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_mt_kernel(const uint4 *__res
     }
 }
 
+// ----------------------- batched decode, a ring of 4-group steps (M <= 16) --
+// The layout of qgemm_mt_kernel -- a wave owns 8 groups of a K chunk and 16
+// tokens' activations in VGPRs; lane (n, j) loads group g0 + 4q + j of row n
+// and a 4 x 4 block transpose gives it block j of each of the four groups --
+// walked as 4-group super-steps (two per 16-row tile) through a ring of four
+// register slots, the loads of a super-step issued three ahead.  The partial
+// sums of a tile (token 4j + r, row n in lane (n, j), register r) go to LDS;
+// every kMrBatch tiles one barrier lets the workgroup add its waves' partials
+// in wave order and store them.  Scale rows must be 8-byte aligned (one
+// 8-byte load per lane and super-step).
+constexpr int kMrBatch = 4;
+template <int WAVES>
+constexpr size_t mr_lds() { return (size_t)2 * kMrBatch * WAVES * 64 * 16; }
+struct MrSlot {
+    u32x4v_t w[3];  // group g0 + 4q + j of row n: 12 words
+    u32x2v_t s;     // bf16 scales of groups g0 + 4q .. g0 + 4q + 3 of row n
+};
+
+template <int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void qgemm_mr_kernel(const uint4 *__restrict__ xq,
+                                                            const int16_t *__restrict__ xe,
+                                                            const uint32_t *__restrict__ packed,
+                                                            const uint16_t *__restrict__ scales,
+                                                            float *__restrict__ out, int M, int64_t N, int G, int C,
+                                                            int64_t out_chunk) {
+    constexpr int Mp = 16;
+    extern __shared__ __align__(16) unsigned char lds[];  // [2][kMrBatch][WAVES][64 lanes] x f4
+    f4_t *red = reinterpret_cast<f4_t *>(lds);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n = lane & 15;
+    const int j = lane >> 4;
+    const int chunk = (int)(blockIdx.x % C);
+    const int64_t tb = blockIdx.x / C, TB = gridDim.x / C;
+    const int g0 = (chunk * WAVES + wave) * 8;  // the wave's 8 groups
+    const int64_t my_tiles = (((N + 15) >> 4) - tb + TB - 1) / TB;  // >= 1: at most one tile block per tile
+    const int64_t W = (int64_t)G * kWordsPerGroup;
+    float *y = out + (int64_t)chunk * out_chunk;
+
+    // Activations first (L2-resident), then the ring, so the first wait for
+    // the ring counts exactly the ring's loads.
+    h8_t xa[8][4];
+#pragma unroll
+    for (int gi = 0; gi < 8; ++gi)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            xa[gi][u] = __builtin_bit_cast(h8_t, xq[(((int64_t)(g0 + gi) * Mp + n) * 4 + j) * 4 + u]);
+    int et[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) et[r] = xe[(int64_t)(g0 / 8) * Mp + 4 * j + r];
+    // Unconditional loads: tiles past the last re-read it, rows past N read row N - 1.
+    auto load = [&](int64_t t, int q, MrSlot &sl) {
+        t = t < my_tiles ? t : my_tiles - 1;
+        int64_t row = (tb + t * TB) * 16 + n;
+        row = row < N ? row : N - 1;
+        const u32x4v_t *p = reinterpret_cast<const u32x4v_t *>(packed + row * W + (int64_t)(g0 + 4 * q + j) * kWordsPerGroup);
+        sl.w[0] = p[0];
+        sl.w[1] = p[1];
+        sl.w[2] = p[2];
+        sl.s = *reinterpret_cast<const u32x2v_t *>(scales + row * G + g0 + 4 * q);
+    };
+    MrSlot ring[4];
+    __builtin_amdgcn_sched_barrier(0);
+    load(0, 0, ring[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    load(0, 1, ring[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    load(1, 0, ring[2]);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint32_t magic = magic_vgpr();
+    f4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int64_t c0 = 0;; c0 += 2) {  // two tiles (four super-steps) per pass: the ring index is static
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int q = u & 1;
+            const int64_t t = c0 + (u >> 1);
+            if (q == 0 && t >= my_tiles) return;  // workgroup-uniform; the last batch was stored
+            load(c0 + ((u + 3) >> 1), (u + 3) & 1, ring[(u + 3) & 3]);
+            __builtin_amdgcn_sched_barrier(0);
+            const MrSlot &sl = ring[u];
+            uint32_t blk[4][3];
+            const uint32_t wd[12] = {sl.w[0].x, sl.w[0].y, sl.w[0].z, sl.w[0].w, sl.w[1].x, sl.w[1].y,
+                                     sl.w[1].z, sl.w[1].w, sl.w[2].x, sl.w[2].y, sl.w[2].z, sl.w[2].w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+#pragma unroll
+                for (int d = 0; d < 3; ++d) blk[k][d] = wd[3 * k + d];
+            quad_block_transpose(blk);  // blk[k] = block j of group g0 + 4q + k
+            const uint32_t scw[2] = {sl.s.x, sl.s.y};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                h2_t qd[16];
+                decode_block(blk[k][0], blk[k][1], blk[k][2], magic, qd);
+                f4_t d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const h8_t bop = {qd[4 * v].x,     qd[4 * v].y,     qd[4 * v + 1].x, qd[4 * v + 1].y,
+                                      qd[4 * v + 2].x, qd[4 * v + 2].y, qd[4 * v + 3].x, qd[4 * v + 3].y};
+                    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[4 * q + k][v], bop, d, 0, 0, 0);
+                }
+                const uint32_t sw = scw[k >> 1];
+                const float sv = __uint_as_float((k & 1) ? (sw & 0xFFFF0000u) : (sw << 16));
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[r] = fmaf(d[r], sv, acc[r]);
+            }
+            if (q == 1) {
+                // Tile t done: its partials (times the activation exponents) to LDS.
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[r] = ldexpf(acc[r], et[r]);
+                const int bt = (int)(t % kMrBatch);
+                f4_t *rb = red + ((t / kMrBatch) & 1) * (kMrBatch * WAVES * 64);
+                rb[(bt * WAVES + wave) * 64 + lane] = acc;
+                acc = f4_t{0.f, 0.f, 0.f, 0.f};
+                if (bt == kMrBatch - 1 || t == my_tiles - 1) {
+                    // One barrier per batch; the other half of `red` is written
+                    // next, and the loads in flight stay in flight.
+                    lds_barrier();
+                    // (tile, lane, r) outputs, a fixed number of passes: a
+                    // data-dependent store count would leave the compiler
+                    // unsure of the memory counter and make it over-wait.
+                    const int outs = (bt + 1) * 256;
+                    constexpr int kPasses = (kMrBatch * 256 + 64 * WAVES - 1) / (64 * WAVES);
+#pragma unroll
+                    for (int ps = 0; ps < kPasses; ++ps) {
+                        const int i = threadIdx.x + ps * 64 * WAVES;
+                        const int tt = i >> 8, l = (i >> 2) & 63, r = i & 3;
+                        const int tok = 4 * (l >> 4) + r;
+                        const int64_t row = (tb + (t - bt + tt) * TB) * 16 + (l & 15);
+                        if (i < outs && tok < M && row < N) {
+                            const float *src = reinterpret_cast<const float *>(rb + tt * WAVES * 64 + l) + r;
+                            float tot = src[0];
+#pragma unroll
+                            for (int w = 1; w < WAVES; ++w) tot += src[w * 64 * 4];
+                            y[(int64_t)tok * N + row] = tot;
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
 // --------------------------------------------------- prefill (large M) tiles --
 // Many tokens: an MFMA GEMM whose B tiles are decoded on the fly.  Because a
 // decoded weight is reused by every token of the tile, the group scale is
@@ -1843,6 +1985,9 @@ qw3_status launch_gemm_pf(const uint16_t *x, const uint32_t *packed, const uint1
 
 // Batched decode from registers (tokens <= 16 per pass), K in chunks of
 // WAVES x 8 groups.
+#ifndef QW3_MT_RING
+#define QW3_MT_RING 1
+#endif
 template <int WAVES>
 qw3_status launch_gemm_mt(const uint16_t *x, const uint32_t *packed, const uint16_t *scales, float *y, int64_t M,
                           int64_t N, int64_t K, hipStream_t stream) {
@@ -1852,10 +1997,15 @@ qw3_status launch_gemm_mt(const uint16_t *x, const uint32_t *packed, const uint1
     const size_t xq_bytes = (size_t)Mp * (size_t)K * 2;
     const size_t xe_bytes = ((size_t)(G / 8) * Mp * sizeof(int16_t) + 255) / 256 * 256;
     const size_t part_bytes = C > 1 ? (size_t)C * Mp * (size_t)N * sizeof(float) : 0;
+    // The ring kernel needs 8-byte aligned scale rows; the other reads its
+    // scales two bytes at a time.
+    const bool ring = QW3_MT_RING && aligned(scales, 8);
     int cus = 0, per_cu = 0;
     qw3_status st = cu_count(&cus);
     if (st == QW3_OK)
-        st = blocks_per_cu(reinterpret_cast<const void *>(&qgemm_mt_kernel<WAVES>), 64 * WAVES, 0, &per_cu);
+        st = ring ? blocks_per_cu(reinterpret_cast<const void *>(&qgemm_mr_kernel<WAVES>), 64 * WAVES, mr_lds<WAVES>(),
+                                  &per_cu)
+                  : blocks_per_cu(reinterpret_cast<const void *>(&qgemm_mt_kernel<WAVES>), 64 * WAVES, 0, &per_cu);
     if (st != QW3_OK) return st;
     void *scratch = nullptr;
     hipError_t err = hipMallocAsync(&scratch, xq_bytes + xe_bytes + part_bytes, stream);
@@ -1875,8 +2025,12 @@ qw3_status launch_gemm_mt(const uint16_t *x, const uint32_t *packed, const uint1
         st = check_launch();
         if (st != QW3_OK) break;
         float *dst = C > 1 ? part : y + m0 * N;
-        hipLaunchKernelGGL(qgemm_mt_kernel<WAVES>, dim3((unsigned)(tb * C)), dim3(64 * WAVES), 0, stream, xq, xe,
-                           packed, scales, dst, mc, N, G, C, (int64_t)Mp * N);
+        if (ring)
+            hipLaunchKernelGGL(qgemm_mr_kernel<WAVES>, dim3((unsigned)(tb * C)), dim3(64 * WAVES), mr_lds<WAVES>(),
+                               stream, xq, xe, packed, scales, dst, mc, N, G, C, (int64_t)Mp * N);
+        else
+            hipLaunchKernelGGL(qgemm_mt_kernel<WAVES>, dim3((unsigned)(tb * C)), dim3(64 * WAVES), 0, stream, xq, xe,
+                               packed, scales, dst, mc, N, G, C, (int64_t)Mp * N);
         st = check_launch();
         if (st != QW3_OK || C == 1) continue;
         const int64_t count = (int64_t)mc * N;

@@ -384,15 +384,18 @@ def test_qgemm_large_m_tiles(m, n, k):
     assert_close(y, yr, a, "qgemm large M=%d %dx%d" % (m, n, k))
 
 
-def test_qgemm_scales_view_not_16_byte_aligned():
+@pytest.mark.parametrize("off", [1, 4])
+def test_qgemm_scales_view_not_16_byte_aligned(off):
+    """Scale views 2-byte aligned (read two bytes at a time) and 8-byte aligned
+    but not 16 (the ring kernel's 8-byte loads)."""
     m, n, k = 6, 40, 8192
     c = synth.codes_all8(4600, n, k)
     s = synth.scales(4601, n, k // 128, sigma=0.02, eps=1e-3)
     x = synth.activations(4602, m, k)
-    say("qgemm scales offset by one element")
+    say("qgemm scales offset by %d elements" % off)
     big = torch.zeros(s.size + 8, dtype=torch.int16, device="cuda")
-    big[1:1 + s.size] = torch.from_numpy(s.reshape(-1).view(np.int16)).cuda()
-    sv = big[1:1 + s.size].view(n, k // 128)
+    big[off:off + s.size] = torch.from_numpy(s.reshape(-1).view(np.int16)).cuda()
+    sv = big[off:off + s.size].view(n, k // 128)
     y = host(q().qgemm_w3g128_smallM(dev(x), gpu_pack(c), sv))
     yr, a = oracle.gemm(x, oracle.pack(c), s, k)
     assert_close(y, yr, a, "qgemm scales view")
