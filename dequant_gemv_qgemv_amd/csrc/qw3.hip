@@ -138,6 +138,39 @@ __device__ __forceinline__ void decode_block(uint32_t w0, uint32_t w1, uint32_t 
     q[15] = q_pair_i<15>(win, magic);
 }
 
+// Pairs 4u .. 4u + 3 of a block (kPairs order), u a compile-time value after
+// unrolling: the same values as decode_block, a quarter at a time.  Each
+// quarter needs one funnel shift (windows 1, 2, 4, 6; windows 0, 3, 5 are the
+// words themselves).
+__device__ __forceinline__ void decode_quarter(int u, uint32_t w0, uint32_t w1, uint32_t w2, uint32_t magic,
+                                               h2_t (&q)[4]) {
+    if (u == 0) {
+        const uint32_t win[7] = {w0, __builtin_amdgcn_alignbit(w1, w0, 4), 0, 0, 0, 0, 0};
+        q[0] = q_pair_i<0>(win, magic);
+        q[1] = q_pair_i<1>(win, magic);
+        q[2] = q_pair_i<2>(win, magic);
+        q[3] = q_pair_i<3>(win, magic);
+    } else if (u == 1) {
+        const uint32_t win[7] = {0, 0, __builtin_amdgcn_alignbit(w1, w0, 12), w1, 0, 0, 0};
+        q[0] = q_pair_i<4>(win, magic);
+        q[1] = q_pair_i<5>(win, magic);
+        q[2] = q_pair_i<6>(win, magic);
+        q[3] = q_pair_i<7>(win, magic);
+    } else if (u == 2) {
+        const uint32_t win[7] = {0, 0, 0, 0, __builtin_amdgcn_alignbit(w2, w1, 9), w2, 0};
+        q[0] = q_pair_i<8>(win, magic);
+        q[1] = q_pair_i<9>(win, magic);
+        q[2] = q_pair_i<10>(win, magic);
+        q[3] = q_pair_i<11>(win, magic);
+    } else {
+        const uint32_t win[7] = {0, 0, 0, 0, 0, w2, w2 >> 7};
+        q[0] = q_pair_i<12>(win, magic);
+        q[1] = q_pair_i<13>(win, magic);
+        q[2] = q_pair_i<14>(win, magic);
+        q[3] = q_pair_i<15>(win, magic);
+    }
+}
+
 // acc + sum over the block of q * x', x' given as 16 fp16 pairs in pair order.
 __device__ __forceinline__ float dot_block(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t magic,
                                            const uint32_t *xp, float acc) {
@@ -1473,12 +1506,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #undef QW3_RING
 
 // ------------------------------------------ prefill, 256 x 256 output tiles --
-// Larger tiles for the MFMA-bound case.  Four waves, each owning 128 tokens x
-// 128 weight rows (64 MFMA tiles of 16 x 16, 256 accumulators).  Per group
-// (128 k) each wave decodes its 128 rows straight into the B operand
-// registers -- lane (n, j) decodes block j of row n of each 16-row sub-tile,
-// exactly (c-4) * 2^p, times the row-normalised scale s * 2^-E[n] (exact in
-// fp16) -- so only the activations go through LDS: each group's 256 x 128
+// Larger tiles for the MFMA-bound case.  Eight waves, two per SIMD, each
+// owning 128 tokens x 64 weight rows (32 MFMA tiles of 16 x 16, 128
+// accumulators): while one wave of a SIMD decodes, the other's MFMAs run.  Per
+// group (128 k) and k-step each wave decodes a quarter block of each of its
+// rows straight into the B operand registers -- lane (n, j) decodes block j
+// of row n of each 16-row sub-tile, exactly (c-4) * 2^p, times the
+// row-normalised scale s * 2^-E[n] (exact in fp16) -- so only the activations
+// go through LDS: each group's 256 x 128
 // fp16 tile is copied in by global_load_lds_dwordx4 one group ahead (XOR-
 // swizzled rows, double buffered).  The A operands are read by asm blocks
 // that wait for themselves (the compiler would drain the copies in flight
@@ -1523,18 +1558,18 @@ __device__ __forceinline__ void pf_read_a(const unsigned char *buf, int r0, int 
         : "memory");
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void qgemm_pf_kernel(
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void qgemm_pf_kernel(
     const uint32_t *__restrict__ xq, const int *__restrict__ xe, const uint32_t *__restrict__ packed,
     const uint16_t *__restrict__ scales, float *__restrict__ out, int M, int MT, int64_t N, int G, int C,
     int64_t out_chunk) {
+    constexpr int NI = 4;  // 16-row sub-tiles per wave
     extern __shared__ __align__(16) unsigned char lds[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave & 1, wn = wave >> 1;
+    const int wm = wave & 1, wn = wave >> 1;  // token half, row quarter
     const int lr = lane & 15, lc = lane >> 4;
     const int64_t NT = (N + kPfBN - 1) / kPfBN;
-    // chunk-major, then token tile, then row tile
     const int chunk = (int)(blockIdx.x / (NT * MT));
     const int64_t rest = blockIdx.x - (int64_t)chunk * NT * MT;
     const int m_tile = (int)(rest / NT);
@@ -1547,33 +1582,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int64_t W = (int64_t)G * kWordsPerGroup;
     float *y = out + (int64_t)chunk * out_chunk;
 
-    // This lane's 8 weight rows (one per 16-row sub-tile of the wave's 128).
-    int64_t rows[8];
+    int64_t rows[NI];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int64_t r = n0 + wn * 128 + 16 * i + lr;
+    for (int i = 0; i < NI; ++i) {
+        const int64_t r = n0 + wn * 16 * NI + 16 * i + lr;
         rows[i] = r < N ? r : N - 1;
     }
-    // Row exponents over the chunk: the chunk's largest scale of each row maps
-    // to [8, 16).  The 4 lanes of a row scan a quarter of the groups each.
-    int en[8];
+    int en[NI];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < NI; ++i) {
         uint32_t mx = 0;
         for (int g = gbeg + lc; g < gbeg + Gc; g += 4) mx = max(mx, (uint32_t)scales[rows[i] * G + g] & 0x7FFFu);
         mx = max(mx, (uint32_t)__shfl_xor((int)mx, 16));
         mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32));
         en[i] = __builtin_amdgcn_frexp_expf(bf16_to_f32(mx)) - 4;
     }
-
-    // Activation tile copies: instruction i of this wave fills LDS bytes
-    // [1024 (16 wave + i), +1024) = rows 4 (16 wave + i) + lane/16, physical
-    // chunk lane%16 (logical chunk = physical ^ (row & 15)).
+    // 64 copy instructions per group, 8 per wave: instruction blk fills LDS
+    // bytes [1024 blk, +1024) = rows 4 blk + lane/16, physical chunk lane%16.
     auto dma_a = [&](int g, int buf) {
         unsigned char *base = lds + (size_t)buf * kPfStage;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int blk = 16 * wave + i;
+        for (int i = 0; i < 8; ++i) {
+            const int blk = 8 * wave + i;
             const int r = 4 * blk + (lane >> 4);
             const int c = (lane & 15) ^ (r & 15);
             const uint32_t *src = xq + (int64_t)(m0 + r) * (K / 2) + (int64_t)g * 64 + 4 * c;
@@ -1581,12 +1611,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                                              0, 0);
         }
     };
-    // Words of block lc of group g for the lane's 8 rows, and their scales.
-    uint32_t wcur[8][3], wnext[8][3], scur[8], snext[8];
-    auto load_w = [&](int g, uint32_t (&w)[8][3], uint32_t (&sc)[8]) {
+    uint32_t wcur[NI][3], wnext[NI][3], scur[NI], snext[NI];
+    auto load_w = [&](int g, uint32_t (&w)[NI][3], uint32_t (&sc)[NI]) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            // one 12-byte load per block (dwordx3)
+        for (int i = 0; i < NI; ++i) {
             const u32x3_t v = *reinterpret_cast<const u32x3_t *>(packed + rows[i] * W + (int64_t)g * kWordsPerGroup + 3 * lc);
             w[i][0] = v.x;
             w[i][1] = v.y;
@@ -1594,63 +1622,59 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             sc[i] = scales[rows[i] * G + g];
         }
     };
-
-    f4_t acc[8][8];
+    f4_t acc[8][NI];
 #pragma unroll
     for (int mi = 0; mi < 8; ++mi)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[mi][i] = f4_t{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < NI; ++i) acc[mi][i] = f4_t{0.f, 0.f, 0.f, 0.f};
     const uint32_t magic = magic_vgpr();
 
     dma_a(gbeg, 0);
     load_w(gbeg, wcur, scur);
-    __builtin_amdgcn_s_waitcnt(0);  // all counters: the first group has landed
+    __builtin_amdgcn_s_waitcnt(0);
     lds_barrier();
     for (int g = gbeg; g < gbeg + Gc; ++g) {
         const int buf = (g - gbeg) & 1;
-        const int gn = g + 1 < gbeg + Gc ? g + 1 : g;  // the last step re-reads (never used)
+        const int gn = g + 1 < gbeg + Gc ? g + 1 : g;
         if (g + 1 < gbeg + Gc) dma_a(gn, buf ^ 1);
         load_w(gn, wnext, snext);
-        // B operands of the group: 8 sub-tiles x 4 k-steps
-        h8_t bop[8][4];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            h2_t qd[16];
-            decode_block(wcur[i][0], wcur[i][1], wcur[i][2], magic, qd);
-            const _Float16 sv = (_Float16)ldexpf(bf16_to_f32(scur[i]), -en[i]);
-            const h2_t s2 = {sv, sv};
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const h2_t p0 = qd[4 * u] * s2, p1 = qd[4 * u + 1] * s2, p2 = qd[4 * u + 2] * s2,
-                           p3 = qd[4 * u + 3] * s2;
-                bop[i][u] = h8_t{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
-            }
-        }
         const unsigned char *abuf = lds + (size_t)buf * kPfStage;
+        h2_t sc2[NI];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const _Float16 sv = (_Float16)ldexpf(bf16_to_f32(scur[i]), -en[i]);
+            sc2[i] = h2_t{sv, sv};
+        }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             h8_t a[8];
-            // k-chunk lc of step u: block lc, pairs 4u..4u+3 (as the B operand)
             pf_read_a(abuf, wm * 128, lr, 4 * lc + u, a);
+            h8_t bop[NI];
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                h2_t qd[4];
+                decode_quarter(u, wcur[i][0], wcur[i][1], wcur[i][2], magic, qd);
+                const h2_t p0 = qd[0] * sc2[i], p1 = qd[1] * sc2[i], p2 = qd[2] * sc2[i], p3 = qd[3] * sc2[i];
+                bop[i] = h8_t{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+            }
 #pragma unroll
             for (int mi = 0; mi < 8; ++mi)
 #pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    acc[mi][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mi], bop[i][u], acc[mi][i], 0, 0, 0);
+                for (int i = 0; i < NI; ++i)
+                    acc[mi][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mi], bop[i], acc[mi][i], 0, 0, 0);
         }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < NI; ++i) {
             scur[i] = snext[i];
 #pragma unroll
             for (int d = 0; d < 3; ++d) wcur[i][d] = wnext[i][d];
         }
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's copies of the next group have landed
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         lds_barrier();
     }
-
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int64_t row = n0 + wn * 128 + 16 * i + lr;
+    for (int i = 0; i < NI; ++i) {
+        const int64_t row = n0 + wn * 16 * NI + 16 * i + lr;
 #pragma unroll
         for (int mi = 0; mi < 8; ++mi) {
 #pragma unroll
@@ -1968,7 +1992,7 @@ qw3_status launch_gemm_pf(const uint16_t *x, const uint32_t *packed, const uint1
     st = check_launch();
     if (st == QW3_OK) {
         float *dst = C > 1 ? part : y;
-        hipLaunchKernelGGL(qgemm_pf_kernel, dim3((unsigned)(NT * MT * C)), dim3(256), kPfLds, stream, xq, xe, packed,
+        hipLaunchKernelGGL(qgemm_pf_kernel, dim3((unsigned)(NT * MT * C)), dim3(512), kPfLds, stream, xq, xe, packed,
                            scales, dst, (int)M, MT, N, G, C, (int64_t)M * N);
         st = check_launch();
     }
