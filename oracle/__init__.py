@@ -64,6 +64,8 @@ def _load():
     lib.oracle_pack.restype = ctypes.c_int
     lib.oracle_unpack.argtypes = [vp, vp, i64, i64]
     lib.oracle_unpack.restype = ctypes.c_int
+    lib.oracle_repack_w4c.argtypes = [vp, vp, i64, i64]
+    lib.oracle_repack_w4c.restype = ctypes.c_int
     lib.oracle_dequant_bf16.argtypes = [vp, vp, vp, i64, i64]
     lib.oracle_dequant_bf16.restype = ctypes.c_int
     lib.oracle_gemm_rows.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, vp, vp]
@@ -111,6 +113,19 @@ def unpack(words: np.ndarray, K: int) -> np.ndarray:
     assert words.shape[1] == words_per_row(K)
     out = np.empty((N, K), dtype=np.uint8)
     _check(_load().oracle_unpack(_ptr(words), _ptr(out), N, K), "unpack")
+    return out
+
+
+def repack_w4c(w4: np.ndarray) -> np.ndarray:
+    """uint32/int32 4-bit-container words [N, K/8] -> uint32 words [N, 3K/32].
+
+    Reading (see oracle.c): nibble k % 8 of word k / 8, least significant
+    first, holds code k in its low 3 bits; the top bit is padding."""
+    w4 = np.ascontiguousarray(w4).view(np.uint32)
+    N, K8 = w4.shape
+    K = 8 * K8
+    out = np.empty((N, max(words_per_row(K), 0)), dtype=np.uint32)
+    _check(_load().oracle_repack_w4c(_ptr(w4), _ptr(out), N, K), "repack_w4c")
     return out
 
 

@@ -89,6 +89,41 @@ int oracle_pack(const uint8_t *codes, uint32_t *words, int64_t N, int64_t K)
     return 0;
 }
 
+/*
+ * repack_w4c: the 4-bit-container intermediate uint32 [N][K/8] -> words
+ * uint32 [N][3K/32].  The GSQ model card ("Storage layout", the note on the
+ * compressed-tensors pack-quantized shards) says only that training writes
+ * the 3-bit codebook padded into a 4-bit INT32 container before the
+ * checkpoint is re-packed to exact width.  Reading taken: weight k of row n
+ * is nibble k % 8 of word k / 8 of that row, counted from the least
+ * significant nibble; the nibble's low 3 bits are its code c (the same code
+ * as the exact-width stream) and its top bit is padding, ignored.  The code
+ * is then stored exactly as pack() stores it, bit by bit.
+ */
+int oracle_repack_w4c(const uint32_t *w4, uint32_t *words, int64_t N, int64_t K)
+{
+    if (K % 128 != 0)
+        return -2;
+    int64_t W = oracle_words_per_row(K);
+    int64_t W4 = K / 8;
+    for (int64_t n = 0; n < N; ++n) {
+        uint32_t *row = words + n * W;
+        for (int64_t w = 0; w < W; ++w)
+            row[w] = 0u;
+        for (int64_t k = 0; k < K; ++k) {
+            uint32_t nibble = (w4[n * W4 + k / 8] >> (4 * (k % 8))) & 0xFu;
+            int c = (int)(nibble & 7u);
+            for (int b = 0; b < 3; ++b) {
+                if ((c >> b) & 1) {
+                    int64_t j = 3 * k + b;
+                    row[j >> 5] |= 1u << (j & 31);
+                }
+            }
+        }
+    }
+    return 0;
+}
+
 /* unpack: words uint32 [N][3K/32] -> codes uint8 [N][K]. */
 int oracle_unpack(const uint32_t *words, uint8_t *codes, int64_t N, int64_t K)
 {

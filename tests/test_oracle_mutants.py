@@ -28,6 +28,9 @@ MUTANTS = {
                           "for (int64_t k = 0; k < K - 1; ++k) {\n                int c = code_at(row, k);"),
     "round_half_up": ("u += 0x7fffu + lsb;", "u += 0x8000u + 0u * lsb;"),
     "transposed_output": ("y[m * nrows + i] = acc;", "y[i * M + m] = acc;"),
+    "w4c_msb_first_nibbles": ("(w4[n * W4 + k / 8] >> (4 * (k % 8)))", "(w4[n * W4 + k / 8] >> (4 * (7 - k % 8)))"),
+    "w4c_word_index": ("(w4[n * W4 + k / 8] >> (4 * (k % 8)))", "(w4[n * W4 + k / 4 % W4] >> (4 * (k % 8)))"),
+    "w4c_padding_bit_kept": ("int c = (int)(nibble & 7u);", "int c = (int)((nibble & 7u) | ((nibble >> 1) & 4u));"),
 }
 
 

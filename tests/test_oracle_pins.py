@@ -128,6 +128,47 @@ def test_pack_rejects_bad_inputs():
         oracle.pack(np.zeros((1, 96), dtype=np.uint8))
 
 
+# ------------------------------------------ 4-bit-container intermediate ---
+# Reading of the GSQ model card ("Storage layout", the note on the
+# pack-quantized shards): nibble k % 8 of word k / 8, least significant first,
+# holds code k in its low 3 bits; the top bit is padding.
+
+def nibbles_twin(w4: np.ndarray) -> np.ndarray:
+    """Codes from 4-bit-container words with numpy shifts (independent of oracle.c)."""
+    w4 = np.asarray(w4, dtype=np.uint32)
+    sh = (4 * np.arange(8)).astype(np.uint32)
+    return ((w4[:, :, None] >> sh) & np.uint32(7)).astype(np.uint8).reshape(w4.shape[0], -1)
+
+
+def test_repack_w4c_worked_example():
+    """Codes k mod 8 in nibble order are words 0x76543210; with every padding
+    bit set they are 0xFEDCBA98.  Both repack to the pinned k-mod-8 stream."""
+    kmod8 = [w for name, _, w in _golden_rows() if name == "kmod8"][0]
+    for word in (0x76543210, 0xFEDCBA98):
+        w4 = np.full((1, 16), word, dtype=np.uint32)
+        assert oracle.repack_w4c(w4)[0].tolist() == kmod8.tolist(), hex(word)
+
+
+def test_repack_w4c_nibble_order():
+    """One code per word: code 5 in nibble 3 of word 2 of a 128-wide row is
+    weight k = 19, i.e. stream bits 57 (set) and 59 (set) of word 1."""
+    w4 = np.zeros((1, 16), dtype=np.uint32)
+    w4[0, 2] = 5 << 12
+    words = oracle.repack_w4c(w4)[0]
+    expect = np.zeros(12, dtype=np.uint32)
+    expect[1] = (1 << (57 - 32)) | (1 << (59 - 32))
+    assert words.tolist() == expect.tolist()
+
+
+@pytest.mark.parametrize("n,k", [(3, 128), (5, 384), (2, 8192)])
+def test_repack_w4c_matches_twin(n, k):
+    rng = np.random.default_rng(40 + k)
+    w4 = rng.integers(0, 2 ** 32, size=(n, k // 8), dtype=np.uint64).astype(np.uint32)
+    codes = nibbles_twin(w4)
+    assert np.array_equal(oracle.repack_w4c(w4), packbits_twin(codes))
+    assert np.array_equal(oracle.unpack(oracle.repack_w4c(w4), k), codes)
+
+
 # --------------------------------------------------------------- dequant ---
 
 def test_dequant_special_values():
