@@ -60,6 +60,18 @@ int64_t oracle_words_per_row(int64_t K) { return (3 * K) / 32; }
 /* Scales per row: one per group of 128 inputs. */
 int64_t oracle_groups_per_row(int64_t K) { return K / 128; }
 
+/* Store code c (0..7) of weight k into a zeroed row: its bit b is stream bit
+ * 3k + b, i.e. bit (3k + b) mod 32 of word (3k + b) div 32. */
+static void put_code(uint32_t *row, int64_t k, int c)
+{
+    for (int b = 0; b < 3; ++b) {
+        if ((c >> b) & 1) {
+            int64_t j = 3 * k + b;
+            row[j >> 5] |= 1u << (j & 31);
+        }
+    }
+}
+
 /*
  * pack: codes uint8 [N][K] (values 0..7) -> words uint32 [N][3K/32].
  * Returns -1 if a code is above 7, -2 if K is not a multiple of 128, else 0.
@@ -78,12 +90,7 @@ int oracle_pack(const uint8_t *codes, uint32_t *words, int64_t N, int64_t K)
             int c = codes[n * K + k];
             if (c > 7)
                 return -1;
-            for (int b = 0; b < 3; ++b) {
-                if ((c >> b) & 1) {
-                    int64_t j = 3 * k + b;
-                    row[j >> 5] |= 1u << (j & 31);
-                }
-            }
+            put_code(row, k, c);
         }
     }
     return 0;
@@ -113,12 +120,7 @@ int oracle_repack_w4c(const uint32_t *w4, uint32_t *words, int64_t N, int64_t K)
         for (int64_t k = 0; k < K; ++k) {
             uint32_t nibble = (w4[n * W4 + k / 8] >> (4 * (k % 8))) & 0xFu;
             int c = (int)(nibble & 7u);
-            for (int b = 0; b < 3; ++b) {
-                if ((c >> b) & 1) {
-                    int64_t j = 3 * k + b;
-                    row[j >> 5] |= 1u << (j & 31);
-                }
-            }
+            put_code(row, k, c);
         }
     }
     return 0;
