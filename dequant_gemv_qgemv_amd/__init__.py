@@ -21,6 +21,7 @@ import torch
 
 __all__ = [
     "qpack_uint3",
+    "qrepack_w4c_uint3",
     "qdequant_bf16",
     "qgemv_w3g128",
     "qgemv_w3g128_multi",
@@ -46,7 +47,7 @@ GROUP = 128
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libqw3.so")
-_EXPORTS = ("qpack_uint3", "qdequant_bf16", "qgemv_w3g128", "qgemv_w3g128_multi",
+_EXPORTS = ("qpack_uint3", "qrepack_w4c_uint3", "qdequant_bf16", "qgemv_w3g128", "qgemv_w3g128_multi",
             "qgemm_w3g128_smallM", "qstatus_str", "qw3_last_hip_error", "qw3_abi_version")
 
 if not os.path.exists(_LIB_PATH):
@@ -57,11 +58,13 @@ if not os.path.exists(_LIB_PATH):
 _lib = ctypes.CDLL(_LIB_PATH)
 _i64, _vp = ctypes.c_int64, ctypes.c_void_p
 _lib.qpack_uint3.argtypes = [_vp, _vp, _i64, _i64, _vp]
+_lib.qrepack_w4c_uint3.argtypes = [_vp, _vp, _i64, _i64, _vp]
 _lib.qdequant_bf16.argtypes = [_vp, _vp, _vp, _i64, _i64, _vp]
 _lib.qgemv_w3g128.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _vp]
 _lib.qgemm_w3g128_smallM.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]
 _lib.qgemv_w3g128_multi.argtypes = [_vp, ctypes.c_int32, _vp, _vp, _vp, _vp, _i64, _vp]
-for _name in ("qpack_uint3", "qdequant_bf16", "qgemv_w3g128", "qgemv_w3g128_multi", "qgemm_w3g128_smallM"):
+for _name in ("qpack_uint3", "qrepack_w4c_uint3", "qdequant_bf16", "qgemv_w3g128", "qgemv_w3g128_multi",
+              "qgemm_w3g128_smallM"):
     getattr(_lib, _name).restype = ctypes.c_int
 _lib.qstatus_str.argtypes = [ctypes.c_int]
 _lib.qstatus_str.restype = ctypes.c_char_p
@@ -160,6 +163,21 @@ def qpack_uint3(codes: torch.Tensor, out: torch.Tensor | None = None) -> torch.T
         raise ValueError("out must have shape [%d, %d]" % (n, 3 * k // 32))
     with torch.cuda.device(codes.device):
         _check(_lib.qpack_uint3(_ptr(codes), _ptr(out), n, k, _stream()), "qpack_uint3")
+    return out
+
+
+def qrepack_w4c_uint3(w4: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """int32 4-bit-container codes [N, K/8] (code k in nibble k % 8 of word
+    k / 8, low 3 bits) -> int32 packed [N, 3K/32]."""
+    _need(w4, "w4", (torch.int32,), 2)
+    n, k = w4.shape[0], 8 * w4.shape[1]
+    if out is None:
+        out = torch.empty((n, 3 * k // 32), dtype=torch.int32, device=w4.device)
+    _need(out, "out", (torch.int32,), 2)
+    if tuple(out.shape) != (n, 3 * k // 32) or out.device != w4.device:
+        raise ValueError("out must be int32 [%d, %d] on %s" % (n, 3 * k // 32, w4.device))
+    with torch.cuda.device(w4.device):
+        _check(_lib.qrepack_w4c_uint3(_ptr(w4), _ptr(out), n, k, _stream()), "qrepack_w4c_uint3")
     return out
 
 

@@ -293,6 +293,46 @@ __global__ __launch_bounds__(256) void qpack_kernel(const uint8_t *__restrict__ 
         pack_group(codes, packed, u);
 }
 
+// ------------------------------------- repack from 4-bit containers -------
+// The intermediate that GSQ training writes (GSQ model card, "Storage
+// layout": the 3-bit codebook padded into a 4-bit INT32 container): code k of
+// a row in nibble k % 8 of word k / 8, least significant nibble first, its top
+// bit padding.  A group of 128 codes is 16 container words in and 12 stream
+// words out; one thread per group, grid-stride loop.
+__device__ __forceinline__ void repack_group(const uint32_t *__restrict__ w4, uint32_t *__restrict__ packed,
+                                             int64_t u) {
+    const uint4 *src = reinterpret_cast<const uint4 *>(w4 + u * 16);
+    uint32_t words[kWordsPerGroup];
+    uint64_t acc = 0;
+    int nbits = 0, nw = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint4 v = src[i];
+        const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+            const uint32_t c = (d[j >> 3] >> (4 * (j & 7))) & 7u;
+            acc |= (uint64_t)c << nbits;
+            nbits += 3;
+            if (nbits >= 32) {
+                words[nw++] = (uint32_t)acc;
+                acc >>= 32;
+                nbits -= 32;
+            }
+        }
+    }
+    uint4 *dst = reinterpret_cast<uint4 *>(packed + u * kWordsPerGroup);
+    dst[0] = make_uint4(words[0], words[1], words[2], words[3]);
+    dst[1] = make_uint4(words[4], words[5], words[6], words[7]);
+    dst[2] = make_uint4(words[8], words[9], words[10], words[11]);
+}
+
+__global__ __launch_bounds__(256) void qrepack_w4c_kernel(const uint32_t *__restrict__ w4,
+                                                          uint32_t *__restrict__ packed, int64_t units) {
+    for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < units; u += (int64_t)gridDim.x * 256)
+        repack_group(w4, packed, u);
+}
+
 // ----------------------------------------------------------- qdequant -----
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     const uint32_t u = __float_as_uint(f);
@@ -2124,6 +2164,20 @@ qw3_status qpack_uint3(const uint8_t *codes, int32_t *packed, int64_t N, int64_t
     const int64_t blocks = ceil_div(units, 256);
     hipLaunchKernelGGL(qpack_kernel, dim3((unsigned)(blocks < (1 << 20) ? blocks : (1 << 20))), dim3(256), 0,
                        (hipStream_t)hip_stream, codes, reinterpret_cast<uint32_t *>(packed), units);
+    return check_launch();
+}
+
+qw3_status qrepack_w4c_uint3(const int32_t *w4, int32_t *packed, int64_t N, int64_t K, void *hip_stream) {
+    qw3_status st = check_shape(N, K);
+    if (st != QW3_OK) return st;
+    if (N == 0 || K == 0) return QW3_OK;
+    if (!w4 || !packed) return QW3_ERR_NULL;
+    if (!aligned(w4, 16) || !aligned(packed, 16)) return QW3_ERR_ALIGN;
+    const int64_t units = N * (K / kGroup);
+    const int64_t blocks = ceil_div(units, 256);
+    hipLaunchKernelGGL(qrepack_w4c_kernel, dim3((unsigned)(blocks < (1 << 20) ? blocks : (1 << 20))), dim3(256), 0,
+                       (hipStream_t)hip_stream, reinterpret_cast<const uint32_t *>(w4),
+                       reinterpret_cast<uint32_t *>(packed), units);
     return check_launch();
 }
 

@@ -71,6 +71,22 @@ qw3_status qpack_uint3(const uint8_t *codes, int32_t *packed, int64_t N, int64_t
                        void *hip_stream);
 
 /*
+ * qrepack_w4c_uint3 -- repack the 4-bit-container intermediate into the
+ * exact-width stream.
+ *   w4     [N, K/8] int32: the codes as GSQ training writes them before the
+ *          checkpoint is re-packed (GSQ model card, "Storage layout": the 3-bit
+ *          codebook padded into a 4-bit INT32 container).  Reading taken: code
+ *          k of a row is nibble k % 8 of word k / 8 of that row, least
+ *          significant nibble first, in the nibble's low 3 bits; the top bit of
+ *          each nibble is padding and ignored.
+ *   packed [N, 3K/32] int32, written: the same codes, exactly as qpack_uint3
+ *          stores them.
+ * Both pointers 16-byte aligned.  Validation and errors as for qpack_uint3.
+ */
+qw3_status qrepack_w4c_uint3(const int32_t *w4, int32_t *packed, int64_t N, int64_t K,
+                             void *hip_stream);
+
+/*
  * qdequant_bf16 -- expand packed codes into a dense bf16 weight.
  *   packed [N, 3K/32] int32, scales [N, K/128] bf16
  *   w_out  [N, K] bf16, written: w_out[n][k] = RNE_bf16(scales[n][k/128] * (c - 4))

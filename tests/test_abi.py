@@ -59,6 +59,7 @@ S = ctypes.c_void_p(0)  # default stream
 def test_bad_shapes(n, k):
     lib = q.raw()
     assert lib.qpack_uint3(A16, A16B, n, k, S) == q.QW3_ERR_SHAPE
+    assert lib.qrepack_w4c_uint3(A16, A16B, n, k, S) == q.QW3_ERR_SHAPE
     assert lib.qdequant_bf16(A16, A16B, A16C, n, k, S) == q.QW3_ERR_SHAPE
     assert lib.qgemv_w3g128(A16, A16B, A16C, A16D, n, k, S) == q.QW3_ERR_SHAPE
     assert lib.qgemm_w3g128_smallM(A16, A16B, A16C, A16D, 2, n, k, S) == q.QW3_ERR_SHAPE
@@ -72,6 +73,8 @@ def test_null_pointers():
     lib = q.raw()
     assert lib.qpack_uint3(NULL, A16B, 4, 128, S) == q.QW3_ERR_NULL
     assert lib.qpack_uint3(A16, NULL, 4, 128, S) == q.QW3_ERR_NULL
+    assert lib.qrepack_w4c_uint3(NULL, A16B, 4, 128, S) == q.QW3_ERR_NULL
+    assert lib.qrepack_w4c_uint3(A16, NULL, 4, 128, S) == q.QW3_ERR_NULL
     assert lib.qdequant_bf16(NULL, A16B, A16C, 4, 128, S) == q.QW3_ERR_NULL
     assert lib.qdequant_bf16(A16, NULL, A16C, 4, 128, S) == q.QW3_ERR_NULL
     assert lib.qdequant_bf16(A16, A16B, NULL, 4, 128, S) == q.QW3_ERR_NULL
@@ -86,6 +89,8 @@ def test_misaligned_pointers():
     lib = q.raw()
     assert lib.qpack_uint3(MIS, A16B, 4, 128, S) == q.QW3_ERR_ALIGN
     assert lib.qpack_uint3(A16, MIS, 4, 128, S) == q.QW3_ERR_ALIGN
+    assert lib.qrepack_w4c_uint3(MIS, A16B, 4, 128, S) == q.QW3_ERR_ALIGN
+    assert lib.qrepack_w4c_uint3(A16, MIS, 4, 128, S) == q.QW3_ERR_ALIGN
     assert lib.qdequant_bf16(MIS, A16B, A16C, 4, 128, S) == q.QW3_ERR_ALIGN
     assert lib.qdequant_bf16(A16, ODD, A16C, 4, 128, S) == q.QW3_ERR_ALIGN
     assert lib.qdequant_bf16(A16, A16B, MIS, 4, 128, S) == q.QW3_ERR_ALIGN
@@ -100,6 +105,7 @@ def test_empty_sizes_enqueue_nothing():
     lib = q.raw()
     # N == 0 or M == 0: valid and nothing to do, even with NULL pointers
     assert lib.qpack_uint3(NULL, NULL, 0, 128, S) == q.QW3_OK
+    assert lib.qrepack_w4c_uint3(NULL, NULL, 0, 128, S) == q.QW3_OK
     assert lib.qdequant_bf16(NULL, NULL, NULL, 0, 1024, S) == q.QW3_OK
     assert lib.qgemv_w3g128(NULL, NULL, NULL, NULL, 0, 1024, S) == q.QW3_OK
     assert lib.qgemm_w3g128_smallM(NULL, NULL, NULL, NULL, 0, 5, 1024, S) == q.QW3_OK

@@ -86,6 +86,34 @@ def test_qpack_tiny_case_and_golden_rows():
     assert np.array_equal(host(gpu_pack(rows)).view(np.uint32), oracle.pack(rows))
 
 
+# 4-bit-container intermediate (GSQ model card, "Storage layout" note), random
+# words: every nibble value, padding bits included.
+@pytest.mark.parametrize("n,k", [(256, 1024), (37, 384), (1, 128), (5, 28672), (300, 256), (3, 131072)])
+def test_qrepack_w4c_bit_exact(n, k):
+    say("qrepack_w4c", n, k)
+    rng = np.random.default_rng(900 + k)
+    w4 = rng.integers(0, 2 ** 32, size=(n, k // 8), dtype=np.uint64).astype(np.uint32)
+    got = host(q().qrepack_w4c_uint3(dev(w4))).view(np.uint32)
+    assert np.array_equal(got, oracle.repack_w4c(w4))
+
+
+def test_qrepack_w4c_then_gemv_matches_pack_path():
+    """Repacked containers drive the GEMV exactly like codes packed directly."""
+    n, k = 300, 8192
+    c = synth.codes_all8(910, n, k)
+    s = synth.scales(911, n, k // 128, sigma=0.02, eps=1e-3)
+    x = synth.activations(912, 1, k)
+    sh = (4 * np.arange(8)).astype(np.uint32)
+    w4 = (c.reshape(n, k // 8, 8).astype(np.uint32) << sh).sum(axis=2, dtype=np.uint64).astype(np.uint32)
+    w4 |= np.uint32(0x88888888)  # padding bits set: ignored
+    say("qrepack_w4c then qgemv")
+    packed = q().qrepack_w4c_uint3(dev(w4))
+    assert np.array_equal(host(packed).view(np.uint32), oracle.pack(c))
+    y = host(q().qgemv_w3g128(dev(x.reshape(-1)), packed, dev(s)))
+    yr, a = ref_gemv(c, s, x)
+    assert_close(y, yr, a, "repacked gemv")
+
+
 @pytest.mark.parametrize("n,k", [(256, 1024), (37, 384), (7, 28672), (2, 131072)])
 def test_qdequant_bit_exact(n, k):
     say("qdequant", n, k)
