@@ -723,7 +723,6 @@ __global__ __launch_bounds__(MAXWGS) QW3_GEMV_OCC void qgemv_big_kernel(const ui
 // are summed across lane rows with permlane swaps and across the four waves
 // through LDS, in a fixed order, once per batch of tiles.  Loads run three
 // super-steps ahead in a register ring, as in qgemv_small_kernel.
-constexpr int kMfGroups = 64;
 #ifndef QW3_MF_BATCH
 #define QW3_MF_BATCH 8
 #endif
@@ -731,22 +730,38 @@ constexpr int kMfGroups = 64;
 #define QW3_MF_ILV 1
 #endif
 constexpr int kMfBatch = QW3_MF_BATCH;  // tiles per cross-wave reduction
-constexpr size_t kMfLds = (size_t)kMfGroups * 64 * 4 + (size_t)kMfGroups * 4 + 2 * kMfBatch * 4 * 16 * sizeof(float);
+// LDS: the converted activations, then the partial sums [2][kMfBatch][WAVES][16].
+template <int GPW, int WAVES>
+constexpr size_t mf_lds() {
+    return (size_t)GPW * WAVES * 64 * 4 + (size_t)GPW * WAVES * 4 + 2 * kMfBatch * WAVES * 16 * sizeof(float);
+}
 typedef unsigned u32x2v_t __attribute__((ext_vector_type(2)));
 struct MfSlot {
     u32x4v_t a, b, c;  // the lane's 12 words of one group of one row
-    u32x2v_t s;        // (super-step 0 only) the bf16 scales of the lane's four groups of lane row j
+    u32x2v_t s;        // (super-steps 0 and 4) the bf16 scales of lane row j's four groups
 };
 
-// First of the four groups that wave w handles in super-step q.
-__device__ __forceinline__ int mf_group(int w, int q) { return QW3_MF_ILV ? 16 * q + 4 * w : 16 * w + 4 * q; }
+// First of the four groups that wave w (of WAVES, GPW groups each) handles in
+// super-step q.
+template <int GPW, int WAVES>
+__device__ __forceinline__ int mf_group(int w, int q) {
+    return QW3_MF_ILV ? 4 * WAVES * q + 4 * w : GPW * w + 4 * q;
+}
 
-template <bool MULTI>
-__global__ __launch_bounds__(256) void qgemv_mfma_kernel(const uint16_t *__restrict__ x, const GemvSegs sg) {
-    constexpr int G = kMfGroups;
+// GPW groups per wave: 16 (K = 8192, 4 waves) or 32 (K = 28672, 7 waves).  A
+// wave then walks GPW / 4 super-steps per tile, and its activations are GPW /
+// 16 A-operand sets: set a serves super-steps 4a .. 4a + 3 with rows
+// m = 4(q mod 4) + j' as above.
+template <int GPW, int WAVES, bool MULTI>
+__global__ __launch_bounds__(64 * WAVES) void qgemv_mfma_kernel(const uint16_t *__restrict__ x, const GemvSegs sg) {
+    constexpr int G = GPW * WAVES;
+    constexpr int NS = GPW / 4;   // super-steps per tile
+    constexpr int AS = GPW / 16;  // A-operand sets
+    constexpr int XU = (4 * G + 64 * WAVES - 1) / (64 * WAVES);  // activation blocks per thread
     constexpr int64_t W = (int64_t)G * kWordsPerGroup;
+    static_assert(NS % 4 == 0, "whole A-operand sets");
     extern __shared__ uint32_t smem[];
-    float *red = reinterpret_cast<float *>(smem + G * 64 + G);  // [2][kMfBatch][4 waves][16 rows]
+    float *red = reinterpret_cast<float *>(smem + G * 64 + G);  // [2][kMfBatch][WAVES][16 rows]
     int kseg = 0, blk = blockIdx.x, nblk = gridDim.x;
     if constexpr (MULTI) {
         kseg = ((int)blockIdx.x >= sg.blk_end[0]) + ((int)blockIdx.x >= sg.blk_end[1]) +
@@ -768,15 +783,17 @@ __global__ __launch_bounds__(256) void qgemv_mfma_kernel(const uint16_t *__restr
         it = it < my_tiles ? it : my_tiles - 1;
         int64_t r = (blk + it * nblk) * 16 + n;
         r = r < N ? r : N - 1;
-        const u32x4v_t *p = reinterpret_cast<const u32x4v_t *>(packed + r * W + (mf_group(w, q) + lj) * kWordsPerGroup);
+        const u32x4v_t *p =
+            reinterpret_cast<const u32x4v_t *>(packed + r * W + (mf_group<GPW, WAVES>(w, q) + lj) * kWordsPerGroup);
         sl.a = p[0];
         sl.b = p[1];
         sl.c = p[2];
-        if (q == 0) sl.s = *reinterpret_cast<const u32x2v_t *>(scales + r * G + mf_group(w, lj));
+        if (q % 4 == 0)
+            sl.s = *reinterpret_cast<const u32x2v_t *>(scales + r * G + mf_group<GPW, WAVES>(w, q + lj));
     };
     MfSlot ring[4];
-    XStage<1> st;
-    xstage_issue<1>(x, G, st);
+    XStage<XU> st;
+    xstage_issue<XU>(x, G, st);
     // Issued strictly in ring order: the waits in the loop count on it.
     load(0, 0, ring[0]);
     __builtin_amdgcn_sched_barrier(0);
@@ -784,38 +801,42 @@ __global__ __launch_bounds__(256) void qgemv_mfma_kernel(const uint16_t *__restr
     __builtin_amdgcn_sched_barrier(0);
     load(0, 2, ring[2]);
     __builtin_amdgcn_sched_barrier(0);
-    xstage_convert<1>(st, G, smem);
+    xstage_convert<XU>(st, G, smem);
     __syncthreads();
-    h8_t xa[16];  // step t = 4 * block + u: pairs 4u .. 4u + 3 of 32-code block `block`
-    float fe[4];  // 2^e of the groups 16 lj + 4w + r whose partials this lane scales
+    h8_t xa[AS][16];  // step t = 4 * block + u: pairs 4u .. 4u + 3 of 32-code block `block`
+    float fe[AS][4];  // 2^e of the groups whose partials this lane scales (lane row lj of each set)
     {
         const bool on = (n & 3) == lj;
-        const int ga = mf_group(w, n >> 2) + lj;
         const uint4 *xs4 = reinterpret_cast<const uint4 *>(smem);
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {
-            const uint4 v = xs4[t * G + ga];
-            xa[t] = on ? __builtin_bit_cast(h8_t, v) : h8_t{0, 0, 0, 0, 0, 0, 0, 0};
-        }
         const int *xe = reinterpret_cast<const int *>(smem + G * 64);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) fe[r] = ldexpf(1.0f, xe[mf_group(w, lj) + r]);
+        for (int a = 0; a < AS; ++a) {
+            const int ga = mf_group<GPW, WAVES>(w, 4 * a + (n >> 2)) + lj;
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                const uint4 v = xs4[t * G + ga];
+                xa[a][t] = on ? __builtin_bit_cast(h8_t, v) : h8_t{0, 0, 0, 0, 0, 0, 0, 0};
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) fe[a][r] = ldexpf(1.0f, xe[mf_group<GPW, WAVES>(w, 4 * a + lj) + r]);
+        }
     }
     const uint32_t magic = magic_vgpr();
     for (int64_t it = 0; it < my_tiles; ++it) {
-        float acc[4] = {0.f, 0.f, 0.f, 0.f}, sc[4];
+        float acc[4] = {0.f, 0.f, 0.f, 0.f}, sc[AS][4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            // ring slot q holds super-step q of this tile; refill the slot freed
-            // by the previous super-step with the one three ahead
-            load(it + (q + 3) / 4, (q + 3) & 3, ring[(q + 3) & 3]);
+        for (int q = 0; q < NS; ++q) {
+            // ring slot q % 4 holds super-step q of this tile; refill the slot
+            // freed by the previous super-step with the one three ahead
+            load(it + (q + 3) / NS, (q + 3) % NS, ring[(q + 3) & 3]);
             __builtin_amdgcn_sched_barrier(0);
-            const MfSlot &sl = ring[q];
-            if (q == 0) {
-                sc[0] = bf16_to_f32(sl.s.x & 0xFFFFu) * fe[0];
-                sc[1] = __uint_as_float(sl.s.x & 0xFFFF0000u) * fe[1];
-                sc[2] = bf16_to_f32(sl.s.y & 0xFFFFu) * fe[2];
-                sc[3] = __uint_as_float(sl.s.y & 0xFFFF0000u) * fe[3];
+            const MfSlot &sl = ring[q & 3];
+            const int a = q / 4;
+            if (q % 4 == 0) {
+                sc[a][0] = bf16_to_f32(sl.s.x & 0xFFFFu) * fe[a][0];
+                sc[a][1] = __uint_as_float(sl.s.x & 0xFFFF0000u) * fe[a][1];
+                sc[a][2] = bf16_to_f32(sl.s.y & 0xFFFFu) * fe[a][2];
+                sc[a][3] = __uint_as_float(sl.s.y & 0xFFFF0000u) * fe[a][3];
             }
             const uint32_t wd[12] = {sl.a.x, sl.a.y, sl.a.z, sl.a.w, sl.b.x, sl.b.y,
                                      sl.b.z, sl.b.w, sl.c.x, sl.c.y, sl.c.z, sl.c.w};
@@ -828,23 +849,23 @@ __global__ __launch_bounds__(256) void qgemv_mfma_kernel(const uint16_t *__restr
                 for (int u = 0; u < 4; ++u) {
                     const h8_t bop = {qd[4 * u].x,     qd[4 * u].y,     qd[4 * u + 1].x, qd[4 * u + 1].y,
                                       qd[4 * u + 2].x, qd[4 * u + 2].y, qd[4 * u + 3].x, qd[4 * u + 3].y};
-                    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[4 * b + u], bop, d, 0, 0, 0);
+                    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[a][4 * b + u], bop, d, 0, 0, 0);
                 }
             }
-            if (lj == q) {
+            if (lj == q % 4) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[r] = fmaf(d[r], sc[r], acc[r]);
+                for (int r = 0; r < 4; ++r) acc[r] = fmaf(d[r], sc[a][r], acc[r]);
             }
         }
-        // Row n's partial over the wave's 16 groups: the four lane rows, then LDS.
+        // Row n's partial over the wave's groups: the four lane rows, then LDS.
         float part = (acc[0] + acc[1]) + (acc[2] + acc[3]);
         const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
         part = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
         const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(part), __float_as_uint(part), false, false);
         part = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
         const int bt = (int)(it % kMfBatch);
-        float *rb = red + ((it / kMfBatch) & 1) * (kMfBatch * 64);
-        if (lj == 0) rb[bt * 64 + w * 16 + n] = part;
+        float *rb = red + ((it / kMfBatch) & 1) * (kMfBatch * WAVES * 16);
+        if (lj == 0) rb[(bt * WAVES + w) * 16 + n] = part;
         if (bt == kMfBatch - 1 || it == my_tiles - 1) {
             // The batch's partials are in LDS (lgkmcnt) before the barrier; the
             // loads of the next tiles stay in flight.  The other half of `red`
@@ -852,8 +873,10 @@ __global__ __launch_bounds__(256) void qgemv_mfma_kernel(const uint16_t *__restr
             lds_barrier();
             const int i = threadIdx.x;
             if (i < (bt + 1) * 16) {
-                const float *rr = rb + (i >> 4) * 64 + (i & 15);
-                const float tot = (rr[0] + rr[16]) + (rr[32] + rr[48]);
+                const float *rr = rb + (i >> 4) * WAVES * 16 + (i & 15);
+                float tot = rr[0];
+#pragma unroll
+                for (int v = 1; v < WAVES; ++v) tot += rr[16 * v];
                 const int64_t row = (blk + (it - bt + (i >> 4)) * nblk) * 16 + (i & 15);
                 if (row < N) y[row] = tot;
             }
@@ -1881,13 +1904,13 @@ qw3_status launch_gemv_big(const uint16_t *x, const uint32_t *packed, const uint
     return check_launch();
 }
 
-// The matrix-core GEMV (K = 8192 only): one workgroup per CU, workgroups dealt
-// to the matrices in proportion to their 16-row tiles, at least one and at
-// most one per tile each.
+// The matrix-core GEMV: one workgroup per CU, workgroups dealt to the
+// matrices in proportion to their 16-row tiles, at least one and at most one
+// per tile each (4 waves x 16 groups at K = 8192).
 #ifndef QW3_GEMV_MFMA
 #define QW3_GEMV_MFMA 1
 #endif
-template <bool MULTI>
+template <int GPW, int WAVES, bool MULTI>
 qw3_status launch_gemv_mfma(const uint16_t *x, GemvSegs sg, int count, hipStream_t stream) {
     int cus = 0;
     const qw3_status st = cu_count(&cus);
@@ -1907,17 +1930,21 @@ qw3_status launch_gemv_mfma(const uint16_t *x, GemvSegs sg, int count, hipStream
         blocks += b;
         sg.blk_end[i] = (int)blocks;
     }
-    hipLaunchKernelGGL((qgemv_mfma_kernel<MULTI>), dim3((unsigned)blocks), dim3(256), kMfLds, stream, x, sg);
+    const size_t lds = mf_lds<GPW, WAVES>();
+    hipLaunchKernelGGL((qgemv_mfma_kernel<GPW, WAVES, MULTI>), dim3((unsigned)blocks), dim3(64 * WAVES), lds, stream,
+                       x, sg);
     return check_launch();
 }
 
 // Whether the matrix-core GEMV takes a matrix: K = 8192, scale rows 8-byte
 // aligned (8-byte scale loads) and at least four 16-row tiles per CU (with
-// fewer it is no faster than the lane-per-group kernel).  The choice depends
-// on the matrix alone, so a matrix gets the same kernel -- and the same bits --
-// from qgemv_w3g128 and from qgemv_w3g128_multi.
+// fewer it is no faster than the lane-per-group kernel).  At K = 28672
+// (7 waves x 32 groups) it measured no faster than qgemv_big_kernel on the
+// 8192-row down projection, two tiles per CU, so it is not used there.  The
+// choice depends on the matrix alone, so a matrix gets the same kernel -- and
+// the same bits -- from qgemv_w3g128 and from qgemv_w3g128_multi.
 bool gemv_mfma_takes(int G, const uint16_t *scales, int64_t N) {
-    if (!QW3_GEMV_MFMA || G != kMfGroups || N == 0 || !aligned(scales, 8)) return false;
+    if (!QW3_GEMV_MFMA || G != 64 || N == 0 || !aligned(scales, 8)) return false;
     int cus = 0;
     if (cu_count(&cus) != QW3_OK) return false;
     return ceil_div(N, 16) >= 4 * (int64_t)cus;
@@ -1932,7 +1959,7 @@ qw3_status launch_gemv(const uint16_t *x, const uint32_t *packed, const uint16_t
         sg.scales[0] = scales;
         sg.y[0] = y;
         sg.rows[0] = N;
-        if (gemv_mfma_takes(G, scales, N)) return launch_gemv_mfma<false>(x, sg, 1, stream);
+        if (gemv_mfma_takes(G, scales, N)) return launch_gemv_mfma<16, 4, false>(x, sg, 1, stream);
         return launch_gemv_small_any<false>(x, sg, 1, G, stream);
     }
     return launch_gemv_big(x, packed, scales, y, N, G, stream);
@@ -1972,7 +1999,7 @@ qw3_status launch_gemv_multi(const uint16_t *x, int count, const uint32_t *const
             sg.y[i] = sg.y[cnt - 1];
             sg.rows[i] = 0;
         }
-        const qw3_status st = pass == 0 ? launch_gemv_mfma<true>(x, sg, cnt, stream)
+        const qw3_status st = pass == 0 ? launch_gemv_mfma<16, 4, true>(x, sg, cnt, stream)
                                         : launch_gemv_small_any<true>(x, sg, cnt, G, stream);
         if (st != QW3_OK) return st;
     }

@@ -254,15 +254,16 @@ def test_binding_rejects_misaligned_view():
 MF_K = 8192
 
 
-@pytest.mark.parametrize("n", [16411, 17000])
-def test_qgemv_mfma_parity_all_codes(n):
-    say("qgemv matrix cores", n, MF_K)
-    c = synth.codes_all8(7000 + n, n, MF_K)
-    s = synth.scales(7100 + n, n, MF_K // 128, sigma=0.02, eps=1e-3)
-    x = synth.activations(7200 + n, 1, MF_K)
+# (the K = 28672 cases check the lane-per-group kernel at the same sizes)
+@pytest.mark.parametrize("n,k", [(16411, MF_K), (17000, MF_K), (8200, 28672), (8213, 28672)])
+def test_qgemv_mfma_parity_all_codes(n, k):
+    say("qgemv matrix cores", n, k)
+    c = synth.codes_all8(7000 + n, n, k)
+    s = synth.scales(7100 + n, n, k // 128, sigma=0.02, eps=1e-3)
+    x = synth.activations(7200 + n, 1, k)
     y = run_gemv(c, s, x)
     yr, a = ref_gemv(c, s, x)
-    assert_close(y, yr, a, "qgemv matrix cores %dx%d" % (n, MF_K))
+    assert_close(y, yr, a, "qgemv matrix cores %dx%d" % (n, k))
 
 
 def test_qgemv_mfma_zero_rows_and_one_hot():
