@@ -36,6 +36,8 @@
 #include <string.h>
 
 #include <mutex>
+#include <vector>
+#include <type_traits>
 
 #include "qw3.h"
 
@@ -704,6 +706,20 @@ __global__ __launch_bounds__(MAXWGS) QW3_GEMV_OCC void qgemv_big_kernel(const ui
     }
 }
 
+// Calls f(std::integral_constant<int, i>{}) for i = 0 .. C - 1, each index a
+// compile-time constant (register-ring slots must be static).
+template <int I, int C, typename F>
+__device__ __forceinline__ void static_for_from(F &&f) {
+    if constexpr (I < C) {
+        f(std::integral_constant<int, I>{});
+        static_for_from<I + 1, C>(f);
+    }
+}
+template <int C, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    static_for_from<0, C>(f);
+}
+
 // ------------------------------------- batch 1, K = 8192, on the matrix cores --
 // The same fused GEMV with the dot products on v_mfma_f32_16x16x32_f16, which
 // leaves two VALU ops per weight pair (the exact decode) instead of three.
@@ -729,7 +745,22 @@ __global__ __launch_bounds__(MAXWGS) QW3_GEMV_OCC void qgemv_big_kernel(const ui
 #ifndef QW3_MF_ILV
 #define QW3_MF_ILV 1
 #endif
+#ifndef QW3_MF_RING
+#define QW3_MF_RING 4
+#endif
+#ifndef QW3_MF_AHEAD
+#define QW3_MF_AHEAD 3
+#endif
 constexpr int kMfBatch = QW3_MF_BATCH;  // tiles per cross-wave reduction
+constexpr int kMfRing = QW3_MF_RING;    // register ring slots (one super-step each)
+constexpr int kMfAhead = QW3_MF_AHEAD;  // super-steps loaded ahead of the one decoded
+#ifndef QW3_MF_NT
+#define QW3_MF_NT 0
+#endif
+#ifndef QW3_MF_PER_CU
+#define QW3_MF_PER_CU 1
+#endif
+constexpr int kMfPerCu = QW3_MF_PER_CU;  // workgroups per CU
 // LDS: the converted activations, then the partial sums [2][kMfBatch][WAVES][16].
 template <int GPW, int WAVES>
 constexpr size_t mf_lds() {
@@ -785,22 +816,36 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_mfma_kernel(const uint16_t *
         r = r < N ? r : N - 1;
         const u32x4v_t *p =
             reinterpret_cast<const u32x4v_t *>(packed + r * W + (mf_group<GPW, WAVES>(w, q) + lj) * kWordsPerGroup);
+#if QW3_MF_NT
+        sl.a = __builtin_nontemporal_load(p);
+        sl.b = __builtin_nontemporal_load(p + 1);
+        sl.c = __builtin_nontemporal_load(p + 2);
+        if (q % 4 == 0)
+            sl.s = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x2v_t *>(scales + r * G + mf_group<GPW, WAVES>(w, q + lj)));
+#else
         sl.a = p[0];
         sl.b = p[1];
         sl.c = p[2];
         if (q % 4 == 0)
             sl.s = *reinterpret_cast<const u32x2v_t *>(scales + r * G + mf_group<GPW, WAVES>(w, q + lj));
+#endif
     };
-    MfSlot ring[4];
+    // Steps are numbered s = NS * tile + q; step s lives in ring slot s % RS.
+    // The body covers UT tiles, a whole number of ring cycles, so every slot
+    // index is static.
+    constexpr int RS = kMfRing, AH = kMfAhead;
+    constexpr int UT = RS > NS ? RS / NS : 1;
+    static_assert(AH < RS && (RS % NS == 0 || NS % RS == 0), "ring cycles must tile the super-steps");
+    MfSlot ring[RS];
     XStage<XU> st;
     xstage_issue<XU>(x, G, st);
     // Issued strictly in ring order: the waits in the loop count on it.
-    load(0, 0, ring[0]);
-    __builtin_amdgcn_sched_barrier(0);
-    load(0, 1, ring[1]);
-    __builtin_amdgcn_sched_barrier(0);
-    load(0, 2, ring[2]);
-    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < AH; ++s) {
+        load(s / NS, s % NS, ring[s % RS]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
     xstage_convert<XU>(st, G, smem);
     __syncthreads();
     h8_t xa[AS][16];  // step t = 4 * block + u: pairs 4u .. 4u + 3 of 32-code block `block`
@@ -822,15 +867,18 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_mfma_kernel(const uint16_t *
         }
     }
     const uint32_t magic = magic_vgpr();
-    for (int64_t it = 0; it < my_tiles; ++it) {
+    // Tile it0 + h, whose super-steps are ring steps h * NS + q.
+    auto tile = [&](int64_t it0, auto hc) __attribute__((always_inline)) {
+        constexpr int h = decltype(hc)::value;
+        const int64_t it = it0 + h;
         float acc[4] = {0.f, 0.f, 0.f, 0.f}, sc[AS][4];
 #pragma unroll
         for (int q = 0; q < NS; ++q) {
-            // ring slot q % 4 holds super-step q of this tile; refill the slot
-            // freed by the previous super-step with the one three ahead
-            load(it + (q + 3) / NS, (q + 3) % NS, ring[(q + 3) & 3]);
+            // refill the slot freed by the previous step with the step AH ahead
+            const int u = h * NS + q;
+            load(it0 + (u + AH) / NS, (u + AH) % NS, ring[(u + AH) % RS]);
             __builtin_amdgcn_sched_barrier(0);
-            const MfSlot &sl = ring[q & 3];
+            const MfSlot &sl = ring[u % RS];
             const int a = q / 4;
             if (q % 4 == 0) {
                 sc[a][0] = bf16_to_f32(sl.s.x & 0xFFFFu) * fe[a][0];
@@ -846,10 +894,10 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_mfma_kernel(const uint16_t *
                 h2_t qd[16];
                 decode_block(wd[3 * b], wd[3 * b + 1], wd[3 * b + 2], magic, qd);
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const h8_t bop = {qd[4 * u].x,     qd[4 * u].y,     qd[4 * u + 1].x, qd[4 * u + 1].y,
-                                      qd[4 * u + 2].x, qd[4 * u + 2].y, qd[4 * u + 3].x, qd[4 * u + 3].y};
-                    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[a][4 * b + u], bop, d, 0, 0, 0);
+                for (int v = 0; v < 4; ++v) {
+                    const h8_t bop = {qd[4 * v].x,     qd[4 * v].y,     qd[4 * v + 1].x, qd[4 * v + 1].y,
+                                      qd[4 * v + 2].x, qd[4 * v + 2].y, qd[4 * v + 3].x, qd[4 * v + 3].y};
+                    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[a][4 * b + v], bop, d, 0, 0, 0);
                 }
             }
             if (lj == q % 4) {
@@ -859,9 +907,11 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_mfma_kernel(const uint16_t *
         }
         // Row n's partial over the wave's groups: the four lane rows, then LDS.
         float part = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-        const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+        const auto s32 =
+            __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
         part = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
-        const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+        const auto s16 =
+            __builtin_amdgcn_permlane16_swap(__float_as_uint(part), __float_as_uint(part), false, false);
         part = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
         const int bt = (int)(it % kMfBatch);
         float *rb = red + ((it / kMfBatch) & 1) * (kMfBatch * WAVES * 16);
@@ -881,7 +931,23 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_mfma_kernel(const uint16_t *
                 if (row < N) y[row] = tot;
             }
         }
-    }
+    };
+    // Whole ring cycles in the loop, so its back edge always carries the same
+    // pending loads (exact waits); a ragged last cycle follows it.
+    int64_t it0 = 0;
+    for (; it0 + UT <= my_tiles; it0 += UT)
+        static_for<UT>([&](auto hc) __attribute__((always_inline)) { tile(it0, hc); });
+    static_for<UT - 1>([&](auto hc) __attribute__((always_inline)) {
+        if (it0 + decltype(hc)::value < my_tiles) tile(it0, hc);
+    });
+    // Slots whose loads (past the last tile) are still in flight at the loop's
+    // exit and that the ragged cycle does not read: held until here, so their
+    // registers are not reused -- which would first wait for those loads.
+    static_for<RS>([&ring](auto ic) __attribute__((always_inline)) {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (UT > 1 && i >= NS * (UT - 1) && i < AH)
+            asm volatile("" ::"v"(ring[i].a), "v"(ring[i].b), "v"(ring[i].c), "v"(ring[i].s));
+    });
 }
 
 // ----------------------------------------------- small-M matrix cores -----
@@ -1015,8 +1081,10 @@ __global__ __launch_bounds__(256) void qgemm_chunk_sum_kernel(const float *__res
 
 // x' with one exponent per (token, 8-group slice): unit (slice, m, gi, b) =
 // the 32 values of block b of group slice*8 + gi; the 32 units of a
-// (slice, m) are one half-wave.  Same layout as prep_x_kernel:
-// xq[((g*Mp + m)*4 + b)*4 + t]; xe[slice*Mp + m].
+// (slice, m) are one half-wave.  Stored as xq[((g*4 + t)*4 + b)*Mp + m]
+// (t: the MFMA of the block), xe[slice*Mp + m]: the batched kernels' lane
+// (m, b) = m + 16b reads xq[(g*4 + t)*64 + lane], so each of their operand
+// loads is one contiguous kilobyte.
 __global__ __launch_bounds__(256) void prep_x_slice_kernel(const uint16_t *__restrict__ x, uint4 *__restrict__ xq,
                                                            int16_t *__restrict__ xe, int M, int Mp, int64_t K,
                                                            int S) {
@@ -1042,9 +1110,9 @@ __global__ __launch_bounds__(256) void prep_x_slice_kernel(const uint16_t *__res
     const int e = m < M ? group_exponent(mx) : 0;
     uint32_t out[16];
     convert_block(xb, e, out);
-    uint4 *dst = xq + ((((int64_t)g * Mp + m) * 4 + b) * 4);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dst[i] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
+    for (int i = 0; i < 4; ++i)
+        xq[(((int64_t)g * 4 + i) * 4 + b) * Mp + m] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
     if (gi == 0 && b == 0) xe[(int64_t)sl * Mp + m] = (int16_t)e;
 }
 
@@ -1117,7 +1185,7 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_mt_kernel(const uint4 *__res
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             xa[gi][u] = h8_t{0, 0, 0, 0, 0, 0, 0, 0};
-            if (n < M) xa[gi][u] = __builtin_bit_cast(h8_t, xq[(((int64_t)(g0 + gi) * Mp + n) * 4 + j) * 4 + u]);
+            if (n < M) xa[gi][u] = __builtin_bit_cast(h8_t, xq[(((int64_t)(g0 + gi) * 4 + u) * 4 + j) * Mp + n]);
         }
     }
     // One activation exponent per (token, slice): D rows 4j..4j+3 are tokens.
@@ -1224,17 +1292,29 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_mr_kernel(const uint4 *__res
     const int64_t W = (int64_t)G * kWordsPerGroup;
     float *y = out + (int64_t)chunk * out_chunk;
 
-    // Activations first (L2-resident), then the ring, so the first wait for
-    // the ring counts exactly the ring's loads.
+    // The slice's 16 activation exponents (one per token) through the scalar
+    // unit: they stay out of the vector memory counter, whose waits in the
+    // loop count the ring's loads exactly.  Lane row j scales tokens 4j..4j+3.
+    int et[4];
+    {
+        const int *xs = reinterpret_cast<const int *>(xe + (int64_t)(g0 / 8) * Mp);
+        int ew[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ew[i] = xs[i];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int w0 = j == 0 ? ew[r / 2] : j == 1 ? ew[2 + r / 2] : j == 2 ? ew[4 + r / 2] : ew[6 + r / 2];
+            et[r] = (r & 1) ? (w0 >> 16) : (int)(int16_t)(w0 & 0xFFFF);
+        }
+    }
+    // Activations first (L2-resident), then the ring: the loop's waits for
+    // the ring count exactly.
     h8_t xa[8][4];
 #pragma unroll
     for (int gi = 0; gi < 8; ++gi)
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-            xa[gi][u] = __builtin_bit_cast(h8_t, xq[(((int64_t)(g0 + gi) * Mp + n) * 4 + j) * 4 + u]);
-    int et[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) et[r] = xe[(int64_t)(g0 / 8) * Mp + 4 * j + r];
+            xa[gi][u] = __builtin_bit_cast(h8_t, xq[(((int64_t)(g0 + gi) * 4 + u) * 4 + j) * Mp + n]);
     // Unconditional loads: tiles past the last re-read it, rows past N read row N - 1.
     auto load = [&](int64_t t, int q, MrSlot &sl) {
         t = t < my_tiles ? t : my_tiles - 1;
@@ -1256,12 +1336,15 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_mr_kernel(const uint4 *__res
     __builtin_amdgcn_sched_barrier(0);
     const uint32_t magic = magic_vgpr();
     f4_t acc = {0.f, 0.f, 0.f, 0.f};
-    for (int64_t c0 = 0;; c0 += 2) {  // two tiles (four super-steps) per pass: the ring index is static
+    // Tile c0 + h: ring steps u = 2h + q.  Two tiles are one ring cycle, so
+    // the loop runs whole cycles (its back edge always carries the same
+    // pending loads, and the waits stay exact) and an odd last tile follows.
+    auto tile = [&](int64_t c0, auto hc) __attribute__((always_inline)) {
+        constexpr int h = decltype(hc)::value;
+        const int64_t t = c0 + h;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int q = u & 1;
-            const int64_t t = c0 + (u >> 1);
-            if (q == 0 && t >= my_tiles) return;  // workgroup-uniform; the last batch was stored
+        for (int q = 0; q < 2; ++q) {
+            const int u = 2 * h + q;
             load(c0 + ((u + 3) >> 1), (u + 3) & 1, ring[(u + 3) & 3]);
             __builtin_amdgcn_sched_barrier(0);
             const MrSlot &sl = ring[u];
@@ -1324,7 +1407,17 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_mr_kernel(const uint4 *__res
                 }
             }
         }
+    };
+    int64_t c0 = 0;
+    for (; c0 + 2 <= my_tiles; c0 += 2) {
+        tile(c0, std::integral_constant<int, 0>{});
+        tile(c0, std::integral_constant<int, 1>{});
     }
+    if (c0 < my_tiles) tile(c0, std::integral_constant<int, 0>{});
+    // Ring slot 2 is still loading (past the last tile) when an odd last tile
+    // runs: held until here, so its registers are not reused -- which would
+    // first wait for that load.
+    asm volatile("" ::"v"(ring[2].w[0]), "v"(ring[2].w[1]), "v"(ring[2].w[2]), "v"(ring[2].s));
 }
 
 // --------------------------------------------------- prefill (large M) tiles --
@@ -1795,6 +1888,57 @@ qw3_status cu_count(int *out) {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Device workspace of the batched-decode and prefill paths (converted
+// activations, K-chunk partial sums): one buffer per (device, stream), kept
+// until the process ends and grown to the largest request.  Work on one
+// stream runs in order, so the calls on that stream share its buffer; other
+// streams get their own.  A stream-ordered allocation and release per call
+// measured several microseconds per call; this costs nothing after the first
+// call of a size.  Growing synchronizes the stream first (the old buffer may
+// still be read by queued work), so under graph capture make one call of the
+// same size beforehand.
+struct Workspace {
+    int dev;
+    hipStream_t stream;
+    void *ptr;
+    size_t bytes;
+};
+std::mutex g_ws_mutex;
+std::vector<Workspace> g_ws;
+
+qw3_status workspace(hipStream_t stream, size_t bytes, void **out) {
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return hip_fail(err);
+    bytes = (bytes + (size_t(1) << 20) - 1) & ~((size_t(1) << 20) - 1);  // whole MiB: fewer regrowths
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    Workspace *w = nullptr;
+    for (auto &e : g_ws)
+        if (e.dev == dev && e.stream == stream) w = &e;
+    if (w && w->bytes >= bytes) {
+        *out = w->ptr;
+        return QW3_OK;
+    }
+    if (w) {
+        err = hipStreamSynchronize(stream);
+        if (err == hipSuccess) err = hipFree(w->ptr);
+        if (err != hipSuccess) return hip_fail(err);
+        w->ptr = nullptr;
+        w->bytes = 0;
+    } else {
+        g_ws.push_back(Workspace{dev, stream, nullptr, 0});
+        w = &g_ws.back();
+    }
+    err = hipMalloc(&w->ptr, bytes);
+    if (err != hipSuccess) {
+        w->ptr = nullptr;
+        return hip_fail(err);
+    }
+    w->bytes = bytes;
+    *out = w->ptr;
+    return QW3_OK;
+}
+
 qw3_status fill_zero(float *y, int64_t n, hipStream_t stream) {
     if (n == 0) return QW3_OK;
     hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, stream, y, n);
@@ -1924,7 +2068,7 @@ qw3_status launch_gemv_mfma(const uint16_t *x, GemvSegs sg, int count, hipStream
     for (int i = 0; i < kMaxSegs; ++i) {
         int64_t b = 0;
         if (tiles[i] > 0) {
-            b = (int64_t)cus * tiles[i] / tot;
+            b = (int64_t)kMfPerCu * cus * tiles[i] / tot;
             b = b < 1 ? 1 : (b > tiles[i] ? tiles[i] : b);
         }
         blocks += b;
@@ -2015,8 +2159,10 @@ qw3_status launch_gemm_tile(const uint16_t *x, const uint32_t *packed, const uin
     const size_t xq_bytes = (size_t)Mp * (size_t)K * 2;
     const size_t xe_bytes = (size_t)Mp * sizeof(int);
     void *scratch = nullptr;
-    hipError_t err = hipMallocAsync(&scratch, xq_bytes + xe_bytes, stream);
-    if (err != hipSuccess) return hip_fail(err);
+    {
+        const qw3_status ws = workspace(stream, xq_bytes + xe_bytes, &scratch);
+        if (ws != QW3_OK) return ws;
+    }
     uint32_t *xq = reinterpret_cast<uint32_t *>(scratch);
     int *xe = reinterpret_cast<int *>(static_cast<char *>(scratch) + xq_bytes);
     hipLaunchKernelGGL(prep_tile_x_kernel, dim3((unsigned)Mp), dim3(256), 0, stream, x, xq, xe, (int)M, K);
@@ -2027,8 +2173,6 @@ qw3_status launch_gemm_tile(const uint16_t *x, const uint32_t *packed, const uin
                            scales, y, (int)M, MT, N, G);
         st = check_launch();
     }
-    err = hipFreeAsync(scratch, stream);
-    if (st == QW3_OK && err != hipSuccess) st = hip_fail(err);
     return st;
 }
 
@@ -2050,8 +2194,10 @@ qw3_status launch_gemm_pf(const uint16_t *x, const uint32_t *packed, const uint1
     const size_t xe_bytes = ((size_t)Mp * sizeof(int) + 255) / 256 * 256;
     const size_t part_bytes = C > 1 ? (size_t)C * (size_t)M * (size_t)N * sizeof(float) : 0;
     void *scratch = nullptr;
-    hipError_t err = hipMallocAsync(&scratch, xq_bytes + xe_bytes + part_bytes, stream);
-    if (err != hipSuccess) return hip_fail(err);
+    {
+        const qw3_status ws = workspace(stream, xq_bytes + xe_bytes + part_bytes, &scratch);
+        if (ws != QW3_OK) return ws;
+    }
     uint32_t *xq = reinterpret_cast<uint32_t *>(scratch);
     int *xe = reinterpret_cast<int *>(static_cast<char *>(scratch) + xq_bytes);
     float *part = reinterpret_cast<float *>(static_cast<char *>(scratch) + xq_bytes + xe_bytes);
@@ -2069,8 +2215,6 @@ qw3_status launch_gemm_pf(const uint16_t *x, const uint32_t *packed, const uint1
                            count, C, count);
         st = check_launch();
     }
-    err = hipFreeAsync(scratch, stream);
-    if (st == QW3_OK && err != hipSuccess) st = hip_fail(err);
     return st;
 }
 
@@ -2099,8 +2243,10 @@ qw3_status launch_gemm_mt(const uint16_t *x, const uint32_t *packed, const uint1
                   : blocks_per_cu(reinterpret_cast<const void *>(&qgemm_mt_kernel<WAVES>), 64 * WAVES, 0, &per_cu);
     if (st != QW3_OK) return st;
     void *scratch = nullptr;
-    hipError_t err = hipMallocAsync(&scratch, xq_bytes + xe_bytes + part_bytes, stream);
-    if (err != hipSuccess) return hip_fail(err);
+    {
+        const qw3_status ws = workspace(stream, xq_bytes + xe_bytes + part_bytes, &scratch);
+        if (ws != QW3_OK) return ws;
+    }
     uint4 *xq = reinterpret_cast<uint4 *>(scratch);
     int16_t *xe = reinterpret_cast<int16_t *>(static_cast<char *>(scratch) + xq_bytes);
     float *part = reinterpret_cast<float *>(static_cast<char *>(scratch) + xq_bytes + xe_bytes);
@@ -2129,8 +2275,6 @@ qw3_status launch_gemm_mt(const uint16_t *x, const uint32_t *packed, const uint1
                            y + m0 * N, count, C, (int64_t)Mp * N);
         st = check_launch();
     }
-    err = hipFreeAsync(scratch, stream);
-    if (st == QW3_OK && err != hipSuccess) st = hip_fail(err);
     return st;
 }
 
@@ -2150,8 +2294,10 @@ qw3_status launch_gemm_small(const uint16_t *x, const uint32_t *packed, const ui
     const size_t xq_bytes = (size_t)mchunk * (size_t)K * 2;
     const size_t xe_bytes = (size_t)G * mchunk * sizeof(int16_t);
     void *scratch = nullptr;
-    hipError_t err = hipMallocAsync(&scratch, xq_bytes + xe_bytes, stream);
-    if (err != hipSuccess) return hip_fail(err);
+    {
+        const qw3_status ws = workspace(stream, xq_bytes + xe_bytes, &scratch);
+        if (ws != QW3_OK) return ws;
+    }
     uint4 *xq = reinterpret_cast<uint4 *>(scratch);
     int16_t *xe = reinterpret_cast<int16_t *>(static_cast<char *>(scratch) + xq_bytes);
     qw3_status st = QW3_OK;
@@ -2171,8 +2317,6 @@ qw3_status launch_gemm_small(const uint16_t *x, const uint32_t *packed, const ui
                                y + m0 * N, mc, mchunk, N, G, N);
         st = check_launch();
     }
-    err = hipFreeAsync(scratch, stream);
-    if (st == QW3_OK && err != hipSuccess) st = hip_fail(err);
     return st;
 }
 

@@ -134,11 +134,16 @@ qw3_status qgemv_w3g128_multi(const uint16_t *x, int32_t count, const int32_t *c
  * Any M >= 0 is accepted.  M == 1 runs the batch-1 kernel; small M streams
  * the weights once for the whole batch through bf16-exact fp16 matrix-core
  * products; large M (prefill) runs a tiled matrix-core kernel.  For M > 1 the
- * call borrows a temporary device buffer from the stream-ordered allocator of
- * `hip_stream` and releases it on the same stream: the activations converted
- * to fp16 (2 bytes per element, M rounded up to 16 or 256) plus, when K is
- * split across workgroups, fp32 partial sums (4 bytes per output element and
- * K chunk).  Same accuracy bound as qgemv_w3g128.
+ * call uses a device workspace that the library keeps per (device, stream):
+ * the activations converted to fp16 (2 bytes per element, M rounded up to 16
+ * or 256) plus, when K is split across workgroups, fp32 partial sums (4 bytes
+ * per output element and K chunk).  It is allocated (hipMalloc) by the first
+ * call on a stream, grown -- after synchronizing that stream -- when a later
+ * call needs more, and held until the process ends.  Calls on one stream run
+ * in order and share it; calls on different streams use different buffers.
+ * Under graph capture, make one call of the same size on the stream first, so
+ * that nothing is allocated while capturing.  Same accuracy bound as
+ * qgemv_w3g128.
  */
 qw3_status qgemm_w3g128_smallM(const uint16_t *x, const int32_t *packed,
                                const uint16_t *scales, float *y, int64_t M, int64_t N,
