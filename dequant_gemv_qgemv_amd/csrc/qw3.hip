@@ -1258,12 +1258,17 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_mt_kernel(const uint4 *__res
 // tokens' activations in VGPRs; lane (n, j) loads group g0 + 4q + j of row n
 // and a 4 x 4 block transpose gives it block j of each of the four groups --
 // walked as 4-group super-steps (two per 16-row tile) through a ring of four
-// register slots, the loads of a super-step issued three ahead.  The partial
+// register slots, the loads of a super-step issued two ahead (three ahead,
+// with two waves per SIMD, put more bytes in flight than the memory system
+// serves well and measured about 3 % slower).  The partial
 // sums of a tile (token 4j + r, row n in lane (n, j), register r) go to LDS;
 // every kMrBatch tiles one barrier lets the workgroup add its waves' partials
 // in wave order and store them.  Scale rows must be 8-byte aligned (one
 // 8-byte load per lane and super-step).
-constexpr int kMrBatch = 4;
+#ifndef QW3_MR_BATCH
+#define QW3_MR_BATCH 4
+#endif
+constexpr int kMrBatch = QW3_MR_BATCH;
 template <int WAVES>
 constexpr size_t mr_lds() { return (size_t)2 * kMrBatch * WAVES * 64 * 16; }
 struct MrSlot {
@@ -1332,8 +1337,7 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_mr_kernel(const uint4 *__res
     __builtin_amdgcn_sched_barrier(0);
     load(0, 1, ring[1]);
     __builtin_amdgcn_sched_barrier(0);
-    load(1, 0, ring[2]);
-    __builtin_amdgcn_sched_barrier(0);
+
     const uint32_t magic = magic_vgpr();
     f4_t acc = {0.f, 0.f, 0.f, 0.f};
     // Tile c0 + h: ring steps u = 2h + q.  Two tiles are one ring cycle, so
@@ -1345,7 +1349,7 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_mr_kernel(const uint4 *__res
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             const int u = 2 * h + q;
-            load(c0 + ((u + 3) >> 1), (u + 3) & 1, ring[(u + 3) & 3]);
+            load(c0 + ((u + 2) >> 1), (u + 2) & 1, ring[(u + 2) & 3]);
             __builtin_amdgcn_sched_barrier(0);
             const MrSlot &sl = ring[u];
             uint32_t blk[4][3];
@@ -1414,10 +1418,6 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_mr_kernel(const uint4 *__res
         tile(c0, std::integral_constant<int, 1>{});
     }
     if (c0 < my_tiles) tile(c0, std::integral_constant<int, 0>{});
-    // Ring slot 2 is still loading (past the last tile) when an odd last tile
-    // runs: held until here, so its registers are not reused -- which would
-    // first wait for that load.
-    asm volatile("" ::"v"(ring[2].w[0]), "v"(ring[2].w[1]), "v"(ring[2].w[2]), "v"(ring[2].s));
 }
 
 // --------------------------------------------------- prefill (large M) tiles --
