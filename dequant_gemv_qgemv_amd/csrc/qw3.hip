@@ -754,9 +754,6 @@ __device__ __forceinline__ void static_for(F &&f) {
 constexpr int kMfBatch = QW3_MF_BATCH;  // tiles per cross-wave reduction
 constexpr int kMfRing = QW3_MF_RING;    // register ring slots (one super-step each)
 constexpr int kMfAhead = QW3_MF_AHEAD;  // super-steps loaded ahead of the one decoded
-#ifndef QW3_MF_NT
-#define QW3_MF_NT 0
-#endif
 #ifndef QW3_MF_PER_CU
 #define QW3_MF_PER_CU 1
 #endif
@@ -816,20 +813,11 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_mfma_kernel(const uint16_t *
         r = r < N ? r : N - 1;
         const u32x4v_t *p =
             reinterpret_cast<const u32x4v_t *>(packed + r * W + (mf_group<GPW, WAVES>(w, q) + lj) * kWordsPerGroup);
-#if QW3_MF_NT
-        sl.a = __builtin_nontemporal_load(p);
-        sl.b = __builtin_nontemporal_load(p + 1);
-        sl.c = __builtin_nontemporal_load(p + 2);
-        if (q % 4 == 0)
-            sl.s = __builtin_nontemporal_load(
-                reinterpret_cast<const u32x2v_t *>(scales + r * G + mf_group<GPW, WAVES>(w, q + lj)));
-#else
         sl.a = p[0];
         sl.b = p[1];
         sl.c = p[2];
         if (q % 4 == 0)
             sl.s = *reinterpret_cast<const u32x2v_t *>(scales + r * G + mf_group<GPW, WAVES>(w, q + lj));
-#endif
     };
     // Steps are numbered s = NS * tile + q; step s lives in ring slot s % RS.
     // The body covers UT tiles, a whole number of ring cycles, so every slot
