@@ -1743,16 +1743,29 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     // 64 copy instructions per group, 8 per wave: instruction blk fills LDS
     // bytes [1024 blk, +1024) = rows 4 blk + lane/16, physical chunk lane%16.
+    // The 8 copies go through a buffer descriptor over this tile's 256 token
+    // rows of x' (256 K / 2 words, at most 32 MiB): each lane's byte offset is
+    // fixed for the whole kernel and the group's is a scalar, so no vector
+    // address register is written per copy.  (With 64-bit addresses the
+    // compiler reused one address register for all 8 copies and, before
+    // writing it again, waited for all of them.)
+    const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint32_t *>(xq + (int64_t)m0 * (K / 2)), (short)0, (int)(kPfBM * K * 2), 0x00020000);
+    uint32_t dma_off[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int blk = 8 * wave + i;
+        const int r = 4 * blk + (lane >> 4);
+        const int c = (lane & 15) ^ (r & 15);
+        dma_off[i] = (uint32_t)((r * (K / 2) + 4 * c) * 4);
+    }
     auto dma_a = [&](int g, int buf) {
         unsigned char *base = lds + (size_t)buf * kPfStage;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int blk = 8 * wave + i;
-            const int r = 4 * blk + (lane >> 4);
-            const int c = (lane & 15) ^ (r & 15);
-            const uint32_t *src = xq + (int64_t)(m0 + r) * (K / 2) + (int64_t)g * 64 + 4 * c;
-            __builtin_amdgcn_global_load_lds((pf_gbl_void_t *)src, (pf_lds_void_t *)(base + (size_t)blk * 1024), 16,
-                                             0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (pf_lds_void_t *)(base + (size_t)blk * 1024), 16, dma_off[i],
+                                                     g * 256, 0, 0);
         }
     };
     uint32_t wcur[NI][3], wnext[NI][3], scur[NI], snext[NI];
@@ -1780,15 +1793,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int g = gbeg; g < gbeg + Gc; ++g) {
         const int buf = (g - gbeg) & 1;
         const int gn = g + 1 < gbeg + Gc ? g + 1 : g;
-        if (g + 1 < gbeg + Gc) dma_a(gn, buf ^ 1);
-        load_w(gn, wnext, snext);
-        const unsigned char *abuf = lds + (size_t)buf * kPfStage;
+        // This group's scales first: converting them after the next group's
+        // loads are issued made the compiler drain those loads first.
         h2_t sc2[NI];
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const _Float16 sv = (_Float16)ldexpf(bf16_to_f32(scur[i]), -en[i]);
             sc2[i] = h2_t{sv, sv};
+            asm volatile("" : "+v"(sc2[i]));  // computed here, not sunk past the copies
         }
+        __builtin_amdgcn_sched_barrier(0);
+        if (g + 1 < gbeg + Gc) dma_a(gn, buf ^ 1);
+        load_w(gn, wnext, snext);
+        const unsigned char *abuf = lds + (size_t)buf * kPfStage;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             h8_t a[8];
@@ -1815,6 +1832,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         lds_barrier();
+        // the copies' lane offsets stay in their registers for the next group
+#pragma unroll
+        for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(dma_off[i]));
     }
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
