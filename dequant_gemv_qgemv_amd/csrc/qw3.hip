@@ -1658,11 +1658,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // of row n of each 16-row sub-tile, exactly (c-4) * 2^p, times the
 // row-normalised scale s * 2^-E[n] (exact in fp16) -- so only the activations
 // go through LDS: each group's 256 x 128
-// fp16 tile is copied in by global_load_lds_dwordx4 one group ahead (XOR-
-// swizzled rows, double buffered).  The A operands are read by asm blocks
-// that wait for themselves (the compiler would drain the copies in flight
-// before every compiler-visible LDS read).  K may be split into C chunks
-// whose partial sums are added by qgemm_chunk_sum_kernel.
+// fp16 tile is copied in by buffer loads to LDS one group ahead (XOR-swizzled
+// rows, double buffered in two separate arrays, two groups per loop
+// iteration, so the compiler can tell that the copy in flight and the reads
+// of the other stage are disjoint and overlaps the reads with the MFMAs).
+// K may be split into C chunks whose partial sums are added by
+// qgemm_chunk_sum_kernel.
 // s_waitcnt immediate that constrains vmcnt only (gfx9 encoding: vmcnt in
 // bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
@@ -1672,42 +1673,19 @@ constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) 
 #endif
 constexpr int kPfBM = 256, kPfBN = 256;
 constexpr size_t kPfStage = (size_t)kPfBM * kTileRow;  // 64 KB of activations per group
-constexpr size_t kPfLds = 2 * kPfStage;
 
 typedef unsigned u32x3_t __attribute__((ext_vector_type(3)));
 typedef __attribute__((address_space(3))) void pf_lds_void_t;
-typedef __attribute__((address_space(1))) const void pf_gbl_void_t;
-
-__device__ __forceinline__ uint32_t pf_lds_addr(const void *p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char *)p;
-}
-
-// A operands of one k-step for 8 token sub-tiles (rows r0 + 16 mi + lr).
-__device__ __forceinline__ void pf_read_a(const unsigned char *buf, int r0, int lr, int chunk, h8_t (&a)[8]) {
-    uint32_t ad[8];
-#pragma unroll
-    for (int mi = 0; mi < 8; ++mi) ad[mi] = pf_lds_addr(buf + tile_off(r0 + 16 * mi + lr, chunk));
-    asm volatile(
-        "ds_read_b128 %0, %8\n\t"
-        "ds_read_b128 %1, %9\n\t"
-        "ds_read_b128 %2, %10\n\t"
-        "ds_read_b128 %3, %11\n\t"
-        "ds_read_b128 %4, %12\n\t"
-        "ds_read_b128 %5, %13\n\t"
-        "ds_read_b128 %6, %14\n\t"
-        "ds_read_b128 %7, %15\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]), "=&v"(a[5]), "=&v"(a[6]), "=&v"(a[7])
-        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7])
-        : "memory");
-}
 
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void qgemm_pf_kernel(
     const uint32_t *__restrict__ xq, const int *__restrict__ xe, const uint32_t *__restrict__ packed,
     const uint16_t *__restrict__ scales, float *__restrict__ out, int M, int MT, int64_t N, int G, int C,
     int64_t out_chunk) {
     constexpr int NI = 4;  // 16-row sub-tiles per wave
-    extern __shared__ __align__(16) unsigned char lds[];
+    // The two activation stages as separate arrays: the copy into one and the
+    // reads from the other are then provably disjoint, so the compiler neither
+    // drains the copy before a read nor needs the reads hidden in asm.
+    __shared__ __align__(16) unsigned char stage_a[kPfStage], stage_b[kPfStage];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1759,8 +1737,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int c = (lane & 15) ^ (r & 15);
         dma_off[i] = (uint32_t)((r * (K / 2) + 4 * c) * 4);
     }
-    auto dma_a = [&](int g, int buf) {
-        unsigned char *base = lds + (size_t)buf * kPfStage;
+    auto dma_a = [&](int g, unsigned char *base) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int blk = 8 * wave + i;
@@ -1786,13 +1763,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int i = 0; i < NI; ++i) acc[mi][i] = f4_t{0.f, 0.f, 0.f, 0.f};
     const uint32_t magic = magic_vgpr();
 
-    dma_a(gbeg, 0);
-    load_w(gbeg, wcur, scur);
-    __builtin_amdgcn_s_waitcnt(0);
-    lds_barrier();
-    for (int g = gbeg; g < gbeg + Gc; ++g) {
-        const int buf = (g - gbeg) & 1;
-        const int gn = g + 1 < gbeg + Gc ? g + 1 : g;
+    // Group g: A from `abuf`; the next group's copies go to `nbuf`.
+    auto group = [&](int g, const unsigned char *abuf, unsigned char *nbuf) __attribute__((always_inline)) {
+        const bool more = g + 1 < gbeg + Gc;
+        const int gn = more ? g + 1 : g;
         // This group's scales first: converting them after the next group's
         // loads are issued made the compiler drain those loads first.
         h2_t sc2[NI];
@@ -1803,13 +1777,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             asm volatile("" : "+v"(sc2[i]));  // computed here, not sunk past the copies
         }
         __builtin_amdgcn_sched_barrier(0);
-        if (g + 1 < gbeg + Gc) dma_a(gn, buf ^ 1);
+        if (more) dma_a(gn, nbuf);
         load_w(gn, wnext, snext);
-        const unsigned char *abuf = lds + (size_t)buf * kPfStage;
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             h8_t a[8];
-            pf_read_a(abuf, wm * 128, lr, 4 * lc + u, a);
+#pragma unroll
+            for (int mi = 0; mi < 8; ++mi)
+                a[mi] = *reinterpret_cast<const h8_t *>(abuf + tile_off(wm * 128 + 16 * mi + lr, 4 * lc + u));
             h8_t bop[NI];
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
@@ -1830,11 +1806,22 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
             for (int d = 0; d < 3; ++d) wcur[i][d] = wnext[i][d];
         }
+        // the next group's copies have landed and every wave is done with abuf
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         lds_barrier();
         // the copies' lane offsets stay in their registers for the next group
 #pragma unroll
         for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(dma_off[i]));
+    };
+
+    dma_a(gbeg, stage_a);
+    load_w(gbeg, wcur, scur);
+    __builtin_amdgcn_s_waitcnt(0);
+    lds_barrier();
+    // two groups per iteration, so each one's stage is a fixed array
+    for (int g = gbeg; g < gbeg + Gc; g += 2) {
+        group(g, stage_a, stage_b);
+        if (g + 1 < gbeg + Gc) group(g + 1, stage_b, stage_a);
     }
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -2213,7 +2200,7 @@ qw3_status launch_gemm_pf(const uint16_t *x, const uint32_t *packed, const uint1
     st = check_launch();
     if (st == QW3_OK) {
         float *dst = C > 1 ? part : y;
-        hipLaunchKernelGGL(qgemm_pf_kernel, dim3((unsigned)(NT * MT * C)), dim3(512), kPfLds, stream, xq, xe, packed,
+        hipLaunchKernelGGL(qgemm_pf_kernel, dim3((unsigned)(NT * MT * C)), dim3(512), 0, stream, xq, xe, packed,
                            scales, dst, (int)M, MT, N, G, C, (int64_t)M * N);
         st = check_launch();
     }
