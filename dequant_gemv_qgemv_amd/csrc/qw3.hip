@@ -1630,6 +1630,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
 #undef QW3_TILE_STEP
 
+    // the exponents of the lane's 16 tokens, loaded together (past M: the last)
+    int xt[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int tok = m0 + wm * 64 + 16 * i + 4 * lc + r;
+            xt[i][r] = xe[tok < M ? tok : M - 1];
+        }
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
         const int nl = wn * 64 + 16 * jj + lr;
@@ -1640,7 +1649,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int tok = m0 + wm * 64 + 16 * i + 4 * lc + r;
-                if (tok < M && row < N) y[(int64_t)tok * N + row] = ldexpf(acc[i][jj][r], en + xe[tok]);
+                if (tok < M && row < N) y[(int64_t)tok * N + row] = ldexpf(acc[i][jj][r], en + xt[i][r]);
             }
         }
     }
@@ -1823,6 +1832,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         group(g, stage_a, stage_b);
         if (g + 1 < gbeg + Gc) group(g + 1, stage_b, stage_a);
     }
+    // The exponents of the lane's 32 tokens, loaded together (tokens past M
+    // read the last one): loaded next to each store, every store waited for
+    // its own load.
+    int xt[8][4];
+#pragma unroll
+    for (int mi = 0; mi < 8; ++mi)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int tok = m0 + wm * 128 + 16 * mi + 4 * lc + r;
+            xt[mi][r] = xe[tok < M ? tok : M - 1];
+        }
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
         const int64_t row = n0 + wn * 16 * NI + 16 * i + lr;
@@ -1831,7 +1851,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int tok = m0 + wm * 128 + 16 * mi + 4 * lc + r;
-                if (tok < M && row < N) y[(int64_t)tok * N + row] = ldexpf(acc[mi][i][r], en[i] + xe[tok]);
+                if (tok < M && row < N) y[(int64_t)tok * N + row] = ldexpf(acc[mi][i][r], en[i] + xt[mi][r]);
             }
         }
     }
