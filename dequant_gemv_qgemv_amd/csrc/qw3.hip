@@ -1257,22 +1257,27 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_mt_kernel(const uint4 *__res
 #define QW3_MR_BATCH 4
 #endif
 constexpr int kMrBatch = QW3_MR_BATCH;
-template <int WAVES>
-constexpr size_t mr_lds() { return (size_t)2 * kMrBatch * WAVES * 64 * 16; }
+// TS sets of 16 tokens share each decoded block (TS = 2: 17..32 tokens in one
+// pass over the weights); a wave then owns 8 / TS groups.
+template <int WAVES, int TS>
+constexpr size_t mr_lds() { return (size_t)2 * kMrBatch * WAVES * TS * 64 * 16; }
 struct MrSlot {
     u32x4v_t w[3];  // group g0 + 4q + j of row n: 12 words
     u32x2v_t s;     // bf16 scales of groups g0 + 4q .. g0 + 4q + 3 of row n
 };
 
-template <int WAVES>
+template <int WAVES, int TS>
 __global__ __launch_bounds__(64 * WAVES) void qgemm_mr_kernel(const uint4 *__restrict__ xq,
                                                             const int16_t *__restrict__ xe,
                                                             const uint32_t *__restrict__ packed,
                                                             const uint16_t *__restrict__ scales,
                                                             float *__restrict__ out, int M, int64_t N, int G, int C,
                                                             int64_t out_chunk) {
-    constexpr int Mp = 16;
-    extern __shared__ __align__(16) unsigned char lds[];  // [2][kMrBatch][WAVES][64 lanes] x f4
+    constexpr int Mp = 16 * TS;
+    constexpr int GW = 8 / TS;   // groups per wave
+    constexpr int NS = GW / 4;   // 4-group super-steps per tile
+    constexpr int UT = 4 / NS;   // tiles per ring cycle (4 slots)
+    extern __shared__ __align__(16) unsigned char lds[];  // [2][kMrBatch][WAVES][TS][64 lanes] x f4
     f4_t *red = reinterpret_cast<f4_t *>(lds);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1280,34 +1285,41 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_mr_kernel(const uint4 *__res
     const int j = lane >> 4;
     const int chunk = (int)(blockIdx.x % C);
     const int64_t tb = blockIdx.x / C, TB = gridDim.x / C;
-    const int g0 = (chunk * WAVES + wave) * 8;  // the wave's 8 groups
+    const int g0 = (chunk * WAVES + wave) * GW;  // the wave's groups
     const int64_t my_tiles = (((N + 15) >> 4) - tb + TB - 1) / TB;  // >= 1: at most one tile block per tile
     const int64_t W = (int64_t)G * kWordsPerGroup;
     float *y = out + (int64_t)chunk * out_chunk;
 
-    // The slice's 16 activation exponents (one per token) through the scalar
-    // unit: they stay out of the vector memory counter, whose waits in the
-    // loop count the ring's loads exactly.  Lane row j scales tokens 4j..4j+3.
-    int et[4];
+    // The slice's activation exponents (one per token; the wave's groups lie
+    // in one 8-group slice) through the scalar unit: they stay out of the
+    // vector memory counter, whose waits in the loop count the ring's loads
+    // exactly.  Lane row j scales tokens 16 ts + 4j .. 16 ts + 4j + 3.
+    int et[TS][4];
     {
         const int *xs = reinterpret_cast<const int *>(xe + (int64_t)(g0 / 8) * Mp);
-        int ew[8];
+        int ew[8 * TS];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) ew[i] = xs[i];
+        for (int i = 0; i < 8 * TS; ++i) ew[i] = xs[i];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int w0 = j == 0 ? ew[r / 2] : j == 1 ? ew[2 + r / 2] : j == 2 ? ew[4 + r / 2] : ew[6 + r / 2];
-            et[r] = (r & 1) ? (w0 >> 16) : (int)(int16_t)(w0 & 0xFFFF);
-        }
+        for (int ts = 0; ts < TS; ++ts)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int b = 8 * ts + r / 2;
+                const int w0 = j == 0 ? ew[b] : j == 1 ? ew[b + 2] : j == 2 ? ew[b + 4] : ew[b + 6];
+                et[ts][r] = (r & 1) ? (w0 >> 16) : (int)(int16_t)(w0 & 0xFFFF);
+            }
     }
     // Activations first (L2-resident), then the ring: the loop's waits for
     // the ring count exactly.
-    h8_t xa[8][4];
+    h8_t xa[GW][TS][4];
 #pragma unroll
-    for (int gi = 0; gi < 8; ++gi)
+    for (int gi = 0; gi < GW; ++gi)
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-            xa[gi][u] = __builtin_bit_cast(h8_t, xq[(((int64_t)(g0 + gi) * 4 + u) * 4 + j) * Mp + n]);
+        for (int ts = 0; ts < TS; ++ts)
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                xa[gi][ts][u] =
+                    __builtin_bit_cast(h8_t, xq[(((int64_t)(g0 + gi) * 4 + u) * 4 + j) * Mp + 16 * ts + n]);
     // Unconditional loads: tiles past the last re-read it, rows past N read row N - 1.
     auto load = [&](int64_t t, int q, MrSlot &sl) {
         t = t < my_tiles ? t : my_tiles - 1;
@@ -1323,21 +1335,23 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_mr_kernel(const uint4 *__res
     __builtin_amdgcn_sched_barrier(0);
     load(0, 0, ring[0]);
     __builtin_amdgcn_sched_barrier(0);
-    load(0, 1, ring[1]);
+    load(1 / NS, 1 % NS, ring[1]);
     __builtin_amdgcn_sched_barrier(0);
 
     const uint32_t magic = magic_vgpr();
-    f4_t acc = {0.f, 0.f, 0.f, 0.f};
-    // Tile c0 + h: ring steps u = 2h + q.  Two tiles are one ring cycle, so
+    f4_t acc[TS];
+#pragma unroll
+    for (int ts = 0; ts < TS; ++ts) acc[ts] = f4_t{0.f, 0.f, 0.f, 0.f};
+    // Tile c0 + h: ring steps u = NS h + q.  UT tiles are one ring cycle, so
     // the loop runs whole cycles (its back edge always carries the same
-    // pending loads, and the waits stay exact) and an odd last tile follows.
+    // pending loads, and the waits stay exact) and a ragged last cycle follows.
     auto tile = [&](int64_t c0, auto hc) __attribute__((always_inline)) {
         constexpr int h = decltype(hc)::value;
         const int64_t t = c0 + h;
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int u = 2 * h + q;
-            load(c0 + ((u + 2) >> 1), (u + 2) & 1, ring[(u + 2) & 3]);
+        for (int q = 0; q < NS; ++q) {
+            const int u = NS * h + q;
+            load(c0 + (u + 2) / NS, (u + 2) % NS, ring[(u + 2) & 3]);
             __builtin_amdgcn_sched_barrier(0);
             const MrSlot &sl = ring[u];
             uint32_t blk[4][3];
@@ -1353,46 +1367,55 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_mr_kernel(const uint4 *__res
             for (int k = 0; k < 4; ++k) {
                 h2_t qd[16];
                 decode_block(blk[k][0], blk[k][1], blk[k][2], magic, qd);
-                f4_t d = {0.f, 0.f, 0.f, 0.f};
+                f4_t d[TS];
+#pragma unroll
+                for (int ts = 0; ts < TS; ++ts) d[ts] = f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const h8_t bop = {qd[4 * v].x,     qd[4 * v].y,     qd[4 * v + 1].x, qd[4 * v + 1].y,
                                       qd[4 * v + 2].x, qd[4 * v + 2].y, qd[4 * v + 3].x, qd[4 * v + 3].y};
-                    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[4 * q + k][v], bop, d, 0, 0, 0);
+#pragma unroll
+                    for (int ts = 0; ts < TS; ++ts)
+                        d[ts] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[4 * q + k][ts][v], bop, d[ts], 0, 0, 0);
                 }
                 const uint32_t sw = scw[k >> 1];
                 const float sv = __uint_as_float((k & 1) ? (sw & 0xFFFF0000u) : (sw << 16));
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[r] = fmaf(d[r], sv, acc[r]);
-            }
-            if (q == 1) {
-                // Tile t done: its partials (times the activation exponents) to LDS.
+                for (int ts = 0; ts < TS; ++ts)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[r] = ldexpf(acc[r], et[r]);
+                    for (int r = 0; r < 4; ++r) acc[ts][r] = fmaf(d[ts][r], sv, acc[ts][r]);
+            }
+            if (q == NS - 1) {
+                // Tile t done: its partials (times the activation exponents) to LDS.
                 const int bt = (int)(t % kMrBatch);
-                f4_t *rb = red + ((t / kMrBatch) & 1) * (kMrBatch * WAVES * 64);
-                rb[(bt * WAVES + wave) * 64 + lane] = acc;
-                acc = f4_t{0.f, 0.f, 0.f, 0.f};
+                f4_t *rb = red + ((t / kMrBatch) & 1) * (kMrBatch * WAVES * TS * 64);
+#pragma unroll
+                for (int ts = 0; ts < TS; ++ts) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[ts][r] = ldexpf(acc[ts][r], et[ts][r]);
+                    rb[((bt * WAVES + wave) * TS + ts) * 64 + lane] = acc[ts];
+                    acc[ts] = f4_t{0.f, 0.f, 0.f, 0.f};
+                }
                 if (bt == kMrBatch - 1 || t == my_tiles - 1) {
                     // One barrier per batch; the other half of `red` is written
                     // next, and the loads in flight stay in flight.
                     lds_barrier();
-                    // (tile, lane, r) outputs, a fixed number of passes: a
-                    // data-dependent store count would leave the compiler
-                    // unsure of the memory counter and make it over-wait.
-                    const int outs = (bt + 1) * 256;
-                    constexpr int kPasses = (kMrBatch * 256 + 64 * WAVES - 1) / (64 * WAVES);
+                    // (tile, token set, lane, r) outputs, a fixed number of
+                    // passes: a data-dependent store count would leave the
+                    // compiler unsure of the memory counter and make it over-wait.
+                    const int outs = (bt + 1) * 256 * TS;
+                    constexpr int kPasses = (kMrBatch * 256 * TS + 64 * WAVES - 1) / (64 * WAVES);
 #pragma unroll
                     for (int ps = 0; ps < kPasses; ++ps) {
                         const int i = threadIdx.x + ps * 64 * WAVES;
-                        const int tt = i >> 8, l = (i >> 2) & 63, r = i & 3;
-                        const int tok = 4 * (l >> 4) + r;
+                        const int tt = i / (256 * TS), ts = (i >> 8) % TS, l = (i >> 2) & 63, r = i & 3;
+                        const int tok = 16 * ts + 4 * (l >> 4) + r;
                         const int64_t row = (tb + (t - bt + tt) * TB) * 16 + (l & 15);
                         if (i < outs && tok < M && row < N) {
-                            const float *src = reinterpret_cast<const float *>(rb + tt * WAVES * 64 + l) + r;
+                            const float *src = reinterpret_cast<const float *>(rb + (tt * WAVES * TS + ts) * 64 + l) + r;
                             float tot = src[0];
 #pragma unroll
-                            for (int w = 1; w < WAVES; ++w) tot += src[w * 64 * 4];
+                            for (int w = 1; w < WAVES; ++w) tot += src[w * TS * 64 * 4];
                             y[(int64_t)tok * N + row] = tot;
                         }
                     }
@@ -1401,11 +1424,10 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_mr_kernel(const uint4 *__res
         }
     };
     int64_t c0 = 0;
-    for (; c0 + 2 <= my_tiles; c0 += 2) {
-        tile(c0, std::integral_constant<int, 0>{});
-        tile(c0, std::integral_constant<int, 1>{});
-    }
-    if (c0 < my_tiles) tile(c0, std::integral_constant<int, 0>{});
+    for (; c0 + UT <= my_tiles; c0 += UT) static_for<UT>([&](auto hc) __attribute__((always_inline)) { tile(c0, hc); });
+    static_for<UT - 1>([&](auto hc) __attribute__((always_inline)) {
+        if (c0 + decltype(hc)::value < my_tiles) tile(c0, hc);
+    });
 }
 
 // --------------------------------------------------- prefill (large M) tiles --
@@ -2238,24 +2260,27 @@ qw3_status launch_gemm_pf(const uint16_t *x, const uint32_t *packed, const uint1
 #ifndef QW3_MT_RING
 #define QW3_MT_RING 1
 #endif
-template <int WAVES>
+// TS = 1: passes of up to 16 tokens, through the ring kernel when the scale
+// rows are 8-byte aligned (it reads 8 bytes of scales at a time), else
+// through qgemm_mt_kernel (2 bytes at a time).  TS = 2: 17..32 tokens in one
+// pass of the ring kernel (two sets of 16 per decoded block, 4 groups per
+// wave), scale rows 8-byte aligned.
+template <int WAVES, int TS>
 qw3_status launch_gemm_mt(const uint16_t *x, const uint32_t *packed, const uint16_t *scales, float *y, int64_t M,
                           int64_t N, int64_t K, hipStream_t stream) {
-    constexpr int Mp = 16;
     const int G = (int)(K / kGroup);
-    const int C = G / (8 * WAVES);
+    const bool ring = TS == 2 || (QW3_MT_RING && aligned(scales, 8));
+    constexpr int Mp = 16 * TS;
+    const int C = G / ((8 / TS) * WAVES);
     const size_t xq_bytes = (size_t)Mp * (size_t)K * 2;
     const size_t xe_bytes = ((size_t)(G / 8) * Mp * sizeof(int16_t) + 255) / 256 * 256;
     const size_t part_bytes = C > 1 ? (size_t)C * Mp * (size_t)N * sizeof(float) : 0;
-    // The ring kernel needs 8-byte aligned scale rows; the other reads its
-    // scales two bytes at a time.
-    const bool ring = QW3_MT_RING && aligned(scales, 8);
+    const void *kern = ring ? reinterpret_cast<const void *>(&qgemm_mr_kernel<WAVES, TS>)
+                            : reinterpret_cast<const void *>(&qgemm_mt_kernel<WAVES>);
+    const size_t lds = ring ? mr_lds<WAVES, TS>() : 0;
     int cus = 0, per_cu = 0;
     qw3_status st = cu_count(&cus);
-    if (st == QW3_OK)
-        st = ring ? blocks_per_cu(reinterpret_cast<const void *>(&qgemm_mr_kernel<WAVES>), 64 * WAVES, mr_lds<WAVES>(),
-                                  &per_cu)
-                  : blocks_per_cu(reinterpret_cast<const void *>(&qgemm_mt_kernel<WAVES>), 64 * WAVES, 0, &per_cu);
+    if (st == QW3_OK) st = blocks_per_cu(kern, 64 * WAVES, lds, &per_cu);
     if (st != QW3_OK) return st;
     void *scratch = nullptr;
     {
@@ -2278,8 +2303,8 @@ qw3_status launch_gemm_mt(const uint16_t *x, const uint32_t *packed, const uint1
         if (st != QW3_OK) break;
         float *dst = C > 1 ? part : y + m0 * N;
         if (ring)
-            hipLaunchKernelGGL(qgemm_mr_kernel<WAVES>, dim3((unsigned)(tb * C)), dim3(64 * WAVES), mr_lds<WAVES>(),
-                               stream, xq, xe, packed, scales, dst, mc, N, G, C, (int64_t)Mp * N);
+            hipLaunchKernelGGL((qgemm_mr_kernel<WAVES, TS>), dim3((unsigned)(tb * C)), dim3(64 * WAVES), lds, stream,
+                               xq, xe, packed, scales, dst, mc, N, G, C, (int64_t)Mp * N);
         else
             hipLaunchKernelGGL(qgemm_mt_kernel<WAVES>, dim3((unsigned)(tb * C)), dim3(64 * WAVES), 0, stream, xq, xe,
                                packed, scales, dst, mc, N, G, C, (int64_t)Mp * N);
@@ -2302,9 +2327,13 @@ qw3_status launch_gemm_small(const uint16_t *x, const uint32_t *packed, const ui
         if (M >= QW3_PF_MIN_M) return launch_gemm_pf(x, packed, scales, y, M, N, K, stream);
         return launch_gemm_tile(x, packed, scales, y, M, N, K, stream);
     }
-    // Batched decode: chunks of 8 waves x 8 groups (or 7 x 8 when K = 28672).
-    if (G % 64 == 0) return launch_gemm_mt<8>(x, packed, scales, y, M, N, K, stream);
-    if (G % 56 == 0) return launch_gemm_mt<7>(x, packed, scales, y, M, N, K, stream);
+    // Batched decode: 17..32 tokens in one pass when the scale rows allow the
+    // ring kernel (chunks of 8 waves x 4 groups); otherwise passes of up to
+    // 16 tokens in chunks of 8 waves x 8 groups (or 7 x 8 when K = 28672).
+    if (M > 16 && QW3_MT_RING && aligned(scales, 8) && G % 32 == 0)
+        return launch_gemm_mt<8, 2>(x, packed, scales, y, M, N, K, stream);
+    if (G % 64 == 0) return launch_gemm_mt<8, 1>(x, packed, scales, y, M, N, K, stream);
+    if (G % 56 == 0) return launch_gemm_mt<7, 1>(x, packed, scales, y, M, N, K, stream);
     const int mchunk = M > 16 ? 32 : 16;
     const size_t xq_bytes = (size_t)mchunk * (size_t)K * 2;
     const size_t xe_bytes = (size_t)G * mchunk * sizeof(int16_t);

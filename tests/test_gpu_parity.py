@@ -389,9 +389,13 @@ def test_qgemm_parity(m, n, k):
     assert_close(y, yr, a, "qgemm M=%d %dx%d" % (m, n, k))
 
 
-@pytest.mark.parametrize("m,n,k", [(5, 48, 16384), (16, 40, 7168), (9, 33, 57344)])
+@pytest.mark.parametrize("m,n,k", [(5, 48, 16384), (16, 40, 7168), (9, 33, 57344),
+                                   (24, 48, 16384), (20, 33, 57344), (32, 40, 4096), (17, 30, 7168)])
 def test_qgemm_chunked_k(m, n, k):
-    # K split over several workgroup chunks (partial sums added in a second pass)
+    # K split over several workgroup chunks (partial sums added in a second
+    # pass); 17..32 tokens take one pass of two token sets when K / 128 is a
+    # multiple of 32 (16384: 4 chunks, 57344: 14, 4096: 1) and passes of 16
+    # otherwise (7168)
     say("qgemm chunked", m, n, k)
     c = synth.codes_all8(4300 + k, n, k)
     s = synth.scales(4400 + k, n, k // 128, sigma=0.02, eps=1e-3)
@@ -413,11 +417,13 @@ def test_qgemm_large_m_tiles(m, n, k):
     assert_close(y, yr, a, "qgemm large M=%d %dx%d" % (m, n, k))
 
 
+@pytest.mark.parametrize("m", [6, 24])
 @pytest.mark.parametrize("off", [1, 4])
-def test_qgemm_scales_view_not_16_byte_aligned(off):
-    """Scale views 2-byte aligned (read two bytes at a time) and 8-byte aligned
-    but not 16 (the ring kernel's 8-byte loads)."""
-    m, n, k = 6, 40, 8192
+def test_qgemm_scales_view_not_16_byte_aligned(off, m):
+    """Scale views 2-byte aligned (read two bytes at a time: passes of 16
+    tokens) and 8-byte aligned but not 16 (the ring kernel's 8-byte loads;
+    24 tokens in one pass)."""
+    n, k = 40, 8192
     c = synth.codes_all8(4600, n, k)
     s = synth.scales(4601, n, k // 128, sigma=0.02, eps=1e-3)
     x = synth.activations(4602, m, k)
