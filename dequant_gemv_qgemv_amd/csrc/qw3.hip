@@ -1049,8 +1049,19 @@ __global__ __launch_bounds__(256) void qgemm_chunk_sum_kernel(const float *__res
                                                             int64_t count, int C, int64_t chunk_stride) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= count) return;
-    float tot = part[i];
-    for (int c = 1; c < C; ++c) tot += part[(int64_t)c * chunk_stride + i];
+    // Up to 8 chunks' loads in flight before their adds (a plain loop waits
+    // for each load in turn); the adds stay in chunk order.
+    constexpr int kBatch = 8;
+    float tot = 0.f;
+    for (int c0 = 0; c0 < C; c0 += kBatch) {
+        float v[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k)
+            if (c0 + k < C) v[k] = part[(int64_t)(c0 + k) * chunk_stride + i];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k)
+            if (c0 + k < C) tot = c0 + k == 0 ? v[k] : tot + v[k];
+    }
     y[i] = tot;
 }
 
