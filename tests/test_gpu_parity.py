@@ -453,16 +453,20 @@ def test_qgemm_m1_is_gemv_and_rows_repeat():
     assert_close(yr[0], ref[0], a[0], "repeated row")
 
 
-def test_qgemm_deterministic():
-    n, k, m = 512, 8192, 16
+# One pass of 16 tokens; 32 tokens in one pass with K in two chunks; seven
+# K chunks (K = 28672); the prefill tiles with K split.
+@pytest.mark.parametrize("m,n,k", [(16, 512, 8192), (32, 512, 8192), (24, 64, 28672), (300, 256, 4096)])
+def test_qgemm_deterministic(m, n, k):
     c = synth.codes(81, n, k)
     s = synth.scales(82, n, k // 128)
     x = synth.activations(83, m, k)
     packed, sd, xd = gpu_pack(c), dev(s), dev(x)
-    say("qgemm determinism")
+    say("qgemm determinism", m, n, k)
     y1 = host(q().qgemm_w3g128_smallM(xd, packed, sd))
     y2 = host(q().qgemm_w3g128_smallM(xd, packed, sd))
     assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+    ref, a = oracle.gemm(x, oracle.pack(c), s, k)
+    assert_close(y1, ref, a, "determinism case")
 
 
 # --------------------------------------------- full 70B-layer shapes -------
