@@ -1321,16 +1321,19 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_mr_kernel(const uint4 *__res
             }
     }
     // Activations first (L2-resident), then the ring: the loop's waits for
-    // the ring count exactly.
+    // the ring count exactly.  Token slots past M read slot M - 1 again (their
+    // rows of D are never stored), so a load touches only the lines of the M
+    // real tokens.
     h8_t xa[GW][TS][4];
 #pragma unroll
-    for (int gi = 0; gi < GW; ++gi)
+    for (int ts = 0; ts < TS; ++ts) {
+        const int m = 16 * ts + n < M ? 16 * ts + n : M - 1;
 #pragma unroll
-        for (int ts = 0; ts < TS; ++ts)
+        for (int gi = 0; gi < GW; ++gi)
 #pragma unroll
             for (int u = 0; u < 4; ++u)
-                xa[gi][ts][u] =
-                    __builtin_bit_cast(h8_t, xq[(((int64_t)(g0 + gi) * 4 + u) * 4 + j) * Mp + 16 * ts + n]);
+                xa[gi][ts][u] = __builtin_bit_cast(h8_t, xq[(((int64_t)(g0 + gi) * 4 + u) * 4 + j) * Mp + m]);
+    }
     // Unconditional loads: tiles past the last re-read it, rows past N read row N - 1.
     auto load = [&](int64_t t, int q, MrSlot &sl) {
         t = t < my_tiles ? t : my_tiles - 1;
