@@ -931,11 +931,12 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_mfma_kernel(const uint16_t *
     // Slots whose loads (past the last tile) are still in flight at the loop's
     // exit and that the ragged cycle does not read: held until here, so their
     // registers are not reused -- which would first wait for those loads.
-    static_for<RS>([&ring](auto ic) __attribute__((always_inline)) {
-        constexpr int i = decltype(ic)::value;
-        if constexpr (UT > 1 && i >= NS * (UT - 1) && i < AH)
-            asm volatile("" ::"v"(ring[i].a), "v"(ring[i].b), "v"(ring[i].c), "v"(ring[i].s));
-    });
+    if constexpr (UT > 1)
+        static_for<RS>([&ring](auto ic) __attribute__((always_inline)) {
+            constexpr int i = decltype(ic)::value;
+            if constexpr (i >= NS * (UT - 1) && i < AH)
+                asm volatile("" ::"v"(ring[i].a), "v"(ring[i].b), "v"(ring[i].c), "v"(ring[i].s));
+        });
 }
 
 // ----------------------------------------------- small-M matrix cores -----
