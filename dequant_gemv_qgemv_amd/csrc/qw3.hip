@@ -1445,6 +1445,149 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_mr_kernel(const uint4 *__res
     });
 }
 
+// ------------------------------------- batched decode, up to four tokens ----
+// The batch-1 matrix-core layout with the four tokens in place of its four
+// super-step slots.  In super-step q lane (n, j) decodes group g0 + 4q + j of
+// row n straight into the B operand (k chunk j), as in qgemv_mfma_kernel, so
+// no transpose across lanes is needed.  A-operand set q has row m = 4t + j'
+// carrying token t's activations of group g0 + 4q + j' in k chunk j' and zero
+// elsewhere, so after the super-step's 16 MFMAs rows 4t .. 4t + 3 -- lane row
+// t's registers -- hold token t's partial sums of the four groups, exactly
+// apart.  A wave owns the 8 groups of one activation slice (two sets, 128
+// VGPRs) and walks 16-row tiles through the ring of qgemm_mr_kernel; the
+// waves' partials meet in LDS every kMrBatch tiles and are added in wave
+// order.  Activations come from prep_x_slice_kernel with 8 token slots:
+// slots 4 .. 7 are zero, and the lanes whose rows carry nothing read slot 4
+// (the 8 slots of a 16-byte fragment share one 128-byte line).
+template <int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void qgemm_m4_kernel(const uint4 *__restrict__ xq,
+                                                            const int16_t *__restrict__ xe,
+                                                            const uint32_t *__restrict__ packed,
+                                                            const uint16_t *__restrict__ scales,
+                                                            float *__restrict__ out, int M, int64_t N, int G, int C,
+                                                            int64_t out_chunk) {
+    constexpr int Mp = 8, GW = 8, NS = 2, UT = 2;
+    extern __shared__ __align__(16) unsigned char lds[];  // [2][kMrBatch][WAVES][64 lanes] floats
+    float *red = reinterpret_cast<float *>(lds);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n = lane & 15;
+    const int j = lane >> 4;
+    const int chunk = (int)(blockIdx.x % C);
+    const int64_t tb = blockIdx.x / C, TB = gridDim.x / C;
+    const int g0 = (chunk * WAVES + wave) * GW;
+    const int64_t my_tiles = (((N + 15) >> 4) - tb + TB - 1) / TB;
+    const int64_t W = (int64_t)G * kWordsPerGroup;
+    float *y = out + (int64_t)chunk * out_chunk;
+
+    // Lane row j accumulates token j: its slice exponent, through the scalar
+    // unit (out of the vector memory counter that the ring's waits count).
+    int et;
+    {
+        const int *xs = reinterpret_cast<const int *>(xe + (int64_t)(g0 / 8) * Mp);
+        const int e01 = xs[0], e23 = xs[1];
+        const int w0 = j < 2 ? e01 : e23;
+        et = (j & 1) ? (w0 >> 16) : (int)(int16_t)(w0 & 0xFFFF);
+    }
+    // A operands, loaded as they are used: row n = 4t + j' of lane row j holds
+    // token t's fragment when j' = j and the zero slot 4 otherwise (tokens
+    // past M read token M - 1; their outputs are not stored).
+    h8_t xa[NS][16];
+    {
+        const int tok = (n & 3) != j ? 4 : (n >> 2) < M ? (n >> 2) : M - 1;
+#pragma unroll
+        for (int q = 0; q < NS; ++q)
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    xa[q][4 * b + v] =
+                        __builtin_bit_cast(h8_t, xq[(((int64_t)(g0 + 4 * q + j) * 4 + v) * 4 + b) * Mp + tok]);
+    }
+    // Unconditional loads: tiles past the last re-read it, rows past N read row N - 1.
+    auto load = [&](int64_t t, int q, MrSlot &sl) {
+        t = t < my_tiles ? t : my_tiles - 1;
+        int64_t row = (tb + t * TB) * 16 + n;
+        row = row < N ? row : N - 1;
+        const u32x4v_t *p = reinterpret_cast<const u32x4v_t *>(packed + row * W + (int64_t)(g0 + 4 * q + j) * kWordsPerGroup);
+        sl.w[0] = p[0];
+        sl.w[1] = p[1];
+        sl.w[2] = p[2];
+        sl.s = *reinterpret_cast<const u32x2v_t *>(scales + row * G + g0 + 4 * q);
+    };
+    MrSlot ring[4];
+    __builtin_amdgcn_sched_barrier(0);
+    load(0, 0, ring[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    load(0, 1, ring[1]);
+    __builtin_amdgcn_sched_barrier(0);
+
+    const uint32_t magic = magic_vgpr();
+    float acc = 0.f;
+    // Tile c0 + h: ring steps u = 2h + q (UT tiles are one ring cycle).
+    auto tile = [&](int64_t c0, auto hc) __attribute__((always_inline)) {
+        constexpr int h = decltype(hc)::value;
+        const int64_t t = c0 + h;
+#pragma unroll
+        for (int q = 0; q < NS; ++q) {
+            const int u = NS * h + q;
+            load(c0 + (u + 2) / NS, (u + 2) % NS, ring[(u + 2) & 3]);
+            __builtin_amdgcn_sched_barrier(0);
+            const MrSlot &sl = ring[u];
+            const uint32_t wd[12] = {sl.w[0].x, sl.w[0].y, sl.w[0].z, sl.w[0].w, sl.w[1].x, sl.w[1].y,
+                                     sl.w[1].z, sl.w[1].w, sl.w[2].x, sl.w[2].y, sl.w[2].z, sl.w[2].w};
+            f4_t d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                h2_t qd[16];
+                decode_block(wd[3 * b], wd[3 * b + 1], wd[3 * b + 2], magic, qd);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const h8_t bop = {qd[4 * v].x,     qd[4 * v].y,     qd[4 * v + 1].x, qd[4 * v + 1].y,
+                                      qd[4 * v + 2].x, qd[4 * v + 2].y, qd[4 * v + 3].x, qd[4 * v + 3].y};
+                    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[q][4 * b + v], bop, d, 0, 0, 0);
+                }
+            }
+            // d[r]: token j, group g0 + 4q + r of row n
+            acc = fmaf(d[0], bf16_to_f32(sl.s.x & 0xFFFFu), acc);
+            acc = fmaf(d[1], __uint_as_float(sl.s.x & 0xFFFF0000u), acc);
+            acc = fmaf(d[2], bf16_to_f32(sl.s.y & 0xFFFFu), acc);
+            acc = fmaf(d[3], __uint_as_float(sl.s.y & 0xFFFF0000u), acc);
+            if (q == NS - 1) {
+                const int bt = (int)(t % kMrBatch);
+                float *rb = red + ((t / kMrBatch) & 1) * (kMrBatch * WAVES * 64);
+                rb[(bt * WAVES + wave) * 64 + lane] = ldexpf(acc, et);
+                acc = 0.f;
+                if (bt == kMrBatch - 1 || t == my_tiles - 1) {
+                    lds_barrier();
+                    // (tile, lane) outputs in a fixed number of passes
+                    const int outs = (bt + 1) * 64;
+                    constexpr int kPasses = (kMrBatch * 64 + 64 * WAVES - 1) / (64 * WAVES);
+#pragma unroll
+                    for (int ps = 0; ps < kPasses; ++ps) {
+                        const int i = threadIdx.x + ps * 64 * WAVES;
+                        const int tt = i >> 6, l = i & 63;
+                        const int tok = l >> 4;
+                        const int64_t row = (tb + (t - bt + tt) * TB) * 16 + (l & 15);
+                        if (i < outs && tok < M && row < N) {
+                            const float *src = rb + tt * WAVES * 64 + l;
+                            float tot = src[0];
+#pragma unroll
+                            for (int w = 1; w < WAVES; ++w) tot += src[w * 64];
+                            y[(int64_t)tok * N + row] = tot;
+                        }
+                    }
+                }
+            }
+        }
+    };
+    int64_t c0 = 0;
+    for (; c0 + UT <= my_tiles; c0 += UT) static_for<UT>([&](auto hc) __attribute__((always_inline)) { tile(c0, hc); });
+    if (c0 < my_tiles) tile(c0, std::integral_constant<int, 0>{});
+}
+template <int WAVES>
+constexpr size_t m4_lds() { return (size_t)2 * kMrBatch * WAVES * 64 * sizeof(float); }
+
 // --------------------------------------------------- prefill (large M) tiles --
 // Many tokens: an MFMA GEMM whose B tiles are decoded on the fly.  Because a
 // decoded weight is reused by every token of the tile, the group scale is
@@ -2333,6 +2476,51 @@ qw3_status launch_gemm_mt(const uint16_t *x, const uint32_t *packed, const uint1
     return st;
 }
 
+// Up to four tokens: qgemm_m4_kernel, WAVES x 8 groups per K chunk (scale
+// rows 8-byte aligned).
+#ifndef QW3_GEMM_M4
+#define QW3_GEMM_M4 1
+#endif
+template <int WAVES>
+qw3_status launch_gemm_m4(const uint16_t *x, const uint32_t *packed, const uint16_t *scales, float *y, int64_t M,
+                          int64_t N, int64_t K, hipStream_t stream) {
+    constexpr int Mp = 8;  // tokens 0..3 and zero slots 4..7
+    const int G = (int)(K / kGroup);
+    const int C = G / (8 * WAVES);
+    const size_t xq_bytes = (size_t)Mp * (size_t)K * 2;
+    const size_t xe_bytes = ((size_t)(G / 8) * Mp * sizeof(int16_t) + 255) / 256 * 256;
+    const size_t part_bytes = C > 1 ? (size_t)C * Mp * (size_t)N * sizeof(float) : 0;
+    const size_t lds = m4_lds<WAVES>();
+    int cus = 0, per_cu = 0;
+    qw3_status st = cu_count(&cus);
+    if (st == QW3_OK) st = blocks_per_cu(reinterpret_cast<const void *>(&qgemm_m4_kernel<WAVES>), 64 * WAVES, lds,
+                                         &per_cu);
+    if (st != QW3_OK) return st;
+    void *scratch = nullptr;
+    st = workspace(stream, xq_bytes + xe_bytes + part_bytes, &scratch);
+    if (st != QW3_OK) return st;
+    uint4 *xq = reinterpret_cast<uint4 *>(scratch);
+    int16_t *xe = reinterpret_cast<int16_t *>(static_cast<char *>(scratch) + xq_bytes);
+    float *part = reinterpret_cast<float *>(static_cast<char *>(scratch) + xq_bytes + xe_bytes);
+    const int64_t tiles = ceil_div(N, 16);
+    int64_t tb = (int64_t)cus * per_cu / C;
+    if (tb < 1) tb = 1;
+    if (tb > tiles) tb = tiles;
+    const int64_t units = (int64_t)(G / 8) * Mp * 32;
+    hipLaunchKernelGGL(prep_x_slice_kernel, dim3((unsigned)ceil_div(units, 256)), dim3(256), 0, stream, x, xq, xe,
+                       (int)M, Mp, K, G / 8);
+    st = check_launch();
+    if (st != QW3_OK) return st;
+    hipLaunchKernelGGL(qgemm_m4_kernel<WAVES>, dim3((unsigned)(tb * C)), dim3(64 * WAVES), lds, stream, xq, xe,
+                       packed, scales, C > 1 ? part : y, (int)M, N, G, C, (int64_t)Mp * N);
+    st = check_launch();
+    if (st != QW3_OK || C == 1) return st;
+    const int64_t count = M * N;
+    hipLaunchKernelGGL(qgemm_chunk_sum_kernel, dim3((unsigned)ceil_div(count, 256)), dim3(256), 0, stream, part, y,
+                       count, C, (int64_t)Mp * N);
+    return check_launch();
+}
+
 // Small-M path: convert x once into scratch, then one streaming pass over W
 // per chunk of up to 32 tokens.
 qw3_status launch_gemm_small(const uint16_t *x, const uint32_t *packed, const uint16_t *scales, float *y,
@@ -2345,6 +2533,10 @@ qw3_status launch_gemm_small(const uint16_t *x, const uint32_t *packed, const ui
     // Batched decode: 17..32 tokens in one pass when the scale rows allow the
     // ring kernel (chunks of 8 waves x 4 groups); otherwise passes of up to
     // 16 tokens in chunks of 8 waves x 8 groups (or 7 x 8 when K = 28672).
+    if (M <= 4 && QW3_GEMM_M4 && aligned(scales, 8)) {
+        if (G % 64 == 0) return launch_gemm_m4<8>(x, packed, scales, y, M, N, K, stream);
+        if (G % 56 == 0) return launch_gemm_m4<7>(x, packed, scales, y, M, N, K, stream);
+    }
     if (M > 16 && QW3_MT_RING && aligned(scales, 8) && G % 32 == 0)
         return launch_gemm_mt<8, 2>(x, packed, scales, y, M, N, K, stream);
     if (G % 64 == 0) return launch_gemm_mt<8, 1>(x, packed, scales, y, M, N, K, stream);

@@ -390,12 +390,14 @@ def test_qgemm_parity(m, n, k):
 
 
 @pytest.mark.parametrize("m,n,k", [(5, 48, 16384), (16, 40, 7168), (9, 33, 57344),
-                                   (24, 48, 16384), (20, 33, 57344), (32, 40, 4096), (17, 30, 7168)])
+                                   (24, 48, 16384), (20, 33, 57344), (32, 40, 4096), (17, 30, 7168),
+                                   (4, 48, 16384), (3, 33, 57344), (2, 40, 7168), (4, 24, 28672)])
 def test_qgemm_chunked_k(m, n, k):
     # K split over several workgroup chunks (partial sums added in a second
     # pass); 17..32 tokens take one pass of two token sets when K / 128 is a
     # multiple of 32 (16384: 4 chunks, 57344: 14, 4096: 1) and passes of 16
-    # otherwise (7168)
+    # otherwise (7168); up to 4 tokens take the four-token kernel in chunks of
+    # 64 groups (16384: 2, 57344: 7) or 56 (7168: 1, 28672: 4)
     say("qgemm chunked", m, n, k)
     c = synth.codes_all8(4300 + k, n, k)
     s = synth.scales(4400 + k, n, k // 128, sigma=0.02, eps=1e-3)
@@ -417,12 +419,12 @@ def test_qgemm_large_m_tiles(m, n, k):
     assert_close(y, yr, a, "qgemm large M=%d %dx%d" % (m, n, k))
 
 
-@pytest.mark.parametrize("m", [6, 24])
+@pytest.mark.parametrize("m", [3, 6, 24])
 @pytest.mark.parametrize("off", [1, 4])
 def test_qgemm_scales_view_not_16_byte_aligned(off, m):
     """Scale views 2-byte aligned (read two bytes at a time: passes of 16
-    tokens) and 8-byte aligned but not 16 (the ring kernel's 8-byte loads;
-    24 tokens in one pass)."""
+    tokens) and 8-byte aligned but not 16 (the 8-byte scale loads of the
+    ring and four-token kernels; 24 tokens in one pass)."""
     n, k = 40, 8192
     c = synth.codes_all8(4600, n, k)
     s = synth.scales(4601, n, k // 128, sigma=0.02, eps=1e-3)
