@@ -377,7 +377,7 @@ def test_qgemv_multi_qkv_full_size():
 
 # ------------------------------------------------------------- small M ----
 
-@pytest.mark.parametrize("m", [2, 3, 4, 8, 16, 17, 31, 32, 33, 64, 100])
+@pytest.mark.parametrize("m", [2, 3, 4, 5, 7, 8, 16, 17, 31, 32, 33, 64, 100])
 @pytest.mark.parametrize("n,k", [(200, 1024), (70, 8192), (24, 28672)])
 def test_qgemm_parity(m, n, k):
     say("qgemm", m, n, k)
@@ -391,13 +391,15 @@ def test_qgemm_parity(m, n, k):
 
 @pytest.mark.parametrize("m,n,k", [(5, 48, 16384), (16, 40, 7168), (9, 33, 57344),
                                    (24, 48, 16384), (20, 33, 57344), (32, 40, 4096), (17, 30, 7168),
-                                   (4, 48, 16384), (3, 33, 57344), (2, 40, 7168), (4, 24, 28672)])
+                                   (4, 48, 16384), (3, 33, 57344), (2, 40, 7168), (4, 24, 28672),
+                                   (6, 48, 16384), (8, 33, 57344), (7, 40, 4096)])
 def test_qgemm_chunked_k(m, n, k):
     # K split over several workgroup chunks (partial sums added in a second
     # pass); 17..32 tokens take one pass of two token sets when K / 128 is a
     # multiple of 32 (16384: 4 chunks, 57344: 14, 4096: 1) and passes of 16
-    # otherwise (7168); up to 4 tokens take the four-token kernel in chunks of
-    # 64 groups (16384: 2, 57344: 7) or 56 (7168: 1, 28672: 4)
+    # otherwise (7168, and 5..16 tokens); up to 4 tokens take the four-token
+    # kernel in chunks of 64 groups (16384: 2, 57344: 7) or 56 (7168: 1,
+    # 28672: 4)
     say("qgemm chunked", m, n, k)
     c = synth.codes_all8(4300 + k, n, k)
     s = synth.scales(4400 + k, n, k // 128, sigma=0.02, eps=1e-3)
