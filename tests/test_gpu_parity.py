@@ -440,6 +440,36 @@ def test_qgemm_scales_view_not_16_byte_aligned(off, m):
     assert_close(y, yr, a, "qgemm scales view")
 
 
+def _random_shapes(count, seed):
+    """Seeded (M, N, K) across every dispatch rule: M = 1, up to 4 tokens,
+    passes of 16 and 32, the 128-row tiles and the prefill tiles; K / 128 a
+    multiple of 64, 56 or 32, or none of them; ragged N.  N shrinks so that
+    the oracle's M N K stays near 3e8 multiply-adds."""
+    rng = np.random.default_rng(seed)
+    ms = [1, 2, 3, 4, 5, 8, 11, 16, 17, 23, 32, 33, 70, 129, 160]
+    gs = [1, 2, 3, 7, 8, 28, 32, 56, 64, 96, 112, 128, 224]
+    out = []
+    for _ in range(count):
+        m = int(rng.choice(ms))
+        k = 128 * int(rng.choice(gs))
+        n = int(rng.integers(1, 600))
+        n = max(1, min(n, int(3e8 // (m * k))))
+        out.append((m, n, k))
+    return out
+
+
+@pytest.mark.parametrize("m,n,k", _random_shapes(48, 20261203))
+def test_qgemm_random_shapes(m, n, k):
+    seed = m * 1000003 + n * 131 + k
+    c = synth.codes_all8(seed, n, k)
+    s = synth.scales(seed + 1, n, k // 128, sigma=0.02, eps=1e-3)
+    x = synth.activations(seed + 2, m, k)
+    say("qgemm random shape", m, n, k)
+    y = host(q().qgemm_w3g128_smallM(dev(x), gpu_pack(c), dev(s)))
+    yr, a = oracle.gemm(x, oracle.pack(c), s, k)
+    assert_close(y, yr, a, "random shape M=%d %dx%d" % (m, n, k))
+
+
 def test_qgemm_m1_is_gemv_and_rows_repeat():
     n, k = 100, 2048
     c = synth.codes(71, n, k)
