@@ -1456,20 +1456,15 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_mr_kernel(const uint4 *__res
 // apart.  A wave owns the 8 groups of one activation slice (two sets, 128
 // VGPRs) and walks 16-row tiles through the ring of qgemm_mr_kernel; the
 // waves' partials meet in LDS every kMrBatch tiles and are added in wave
-// order.  XIN: the kernel converts the activations itself (one exponent per
-// token over the wave's slice), with no conversion launch.  Otherwise they
-// come from prep_x_slice_kernel with 8 token slots: slots 4 .. 7 are zero,
-// and the lanes whose rows carry nothing read slot 4 (the 8 slots of a
-// 16-byte fragment share one 128-byte line).
-template <int WAVES, bool XIN>
-__global__ __launch_bounds__(64 * WAVES) void qgemm_m4_kernel(const uint4 *__restrict__ xq,
-                                                            const int16_t *__restrict__ xe,
-                                                            const uint16_t *__restrict__ x,
+// order.  The kernel converts the activations itself, with one exponent per
+// token over the wave's slice (a conversion launch in front measured slower).
+template <int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void qgemm_m4_kernel(const uint16_t *__restrict__ x,
                                                             const uint32_t *__restrict__ packed,
                                                             const uint16_t *__restrict__ scales,
                                                             float *__restrict__ out, int M, int64_t N, int G, int C,
                                                             int64_t out_chunk) {
-    constexpr int Mp = 8, GW = 8, NS = 2, UT = 2;
+    constexpr int GW = 8, NS = 2, UT = 2;
     extern __shared__ __align__(16) unsigned char lds[];  // [2][kMrBatch][WAVES][64 lanes] floats
     float *red = reinterpret_cast<float *>(lds);
     const int lane = threadIdx.x & 63;
@@ -1483,42 +1478,20 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_m4_kernel(const uint4 *__res
     const int64_t W = (int64_t)G * kWordsPerGroup;
     float *y = out + (int64_t)chunk * out_chunk;
 
+    // The bf16 activations straight from x, before the ring's loads: lane
+    // (n, j) reads all of group g0 + 4q + j of token n / 4 (the four lanes of
+    // a token and group share the addresses; tokens past M read token M - 1,
+    // whose rows of D are not stored).
     int et;
     h8_t xa[NS][16];
-    [[maybe_unused]] uint4 xb[NS][4][4];
-    if constexpr (XIN) {
-        // The bf16 activations straight from x: lane (n, j) reads all of
-        // group g0 + 4q + j of token n / 4 (the four lanes of a token and
-        // group share the addresses), before the ring's loads.
+    uint4 xb[NS][4][4];
+    {
         const int64_t K = (int64_t)G * kGroup;
         const int t = (n >> 2) < M ? (n >> 2) : M - 1;
 #pragma unroll
         for (int q = 0; q < NS; ++q)
 #pragma unroll
             for (int b = 0; b < 4; ++b) load_x32(x + t * K + (int64_t)(g0 + 4 * q + j) * kGroup + 32 * b, xb[q][b]);
-    } else {
-    // Lane row j accumulates token j: its slice exponent, through the scalar
-    // unit (out of the vector memory counter that the ring's waits count).
-    {
-        const int *xs = reinterpret_cast<const int *>(xe + (int64_t)(g0 / 8) * Mp);
-        const int e01 = xs[0], e23 = xs[1];
-        const int w0 = j < 2 ? e01 : e23;
-        et = (j & 1) ? (w0 >> 16) : (int)(int16_t)(w0 & 0xFFFF);
-    }
-    // A operands, loaded as they are used: row n = 4t + j' of lane row j holds
-    // token t's fragment when j' = j and the zero slot 4 otherwise (tokens
-    // past M read token M - 1; their outputs are not stored).
-    {
-        const int tok = (n & 3) != j ? 4 : (n >> 2) < M ? (n >> 2) : M - 1;
-#pragma unroll
-        for (int q = 0; q < NS; ++q)
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    xa[q][4 * b + v] =
-                        __builtin_bit_cast(h8_t, xq[(((int64_t)(g0 + 4 * q + j) * 4 + v) * 4 + b) * Mp + tok]);
-    }
     }
     // Unconditional loads: tiles past the last re-read it, rows past N read row N - 1.
     auto load = [&](int64_t t, int q, MrSlot &sl) {
@@ -1537,7 +1510,7 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_m4_kernel(const uint4 *__res
     __builtin_amdgcn_sched_barrier(0);
     load(0, 1, ring[1]);
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (XIN) {
+    {
         // One exponent per token over the wave's slice: the largest |x| over
         // the token's 16 lanes (lane ^ 17 and lane ^ 34 keep n / 4) maps to
         // [2^14, 2^15).  Lane row j accumulates token j, held by lane 4j.
@@ -2524,47 +2497,32 @@ qw3_status launch_gemm_mt(const uint16_t *x, const uint32_t *packed, const uint1
 #ifndef QW3_GEMM_M4
 #define QW3_GEMM_M4 1
 #endif
-#ifndef QW3_M4_XIN
-#define QW3_M4_XIN 1
-#endif
-constexpr bool kM4Xin = QW3_M4_XIN;  // the four-token kernel converts x itself
 template <int WAVES>
 qw3_status launch_gemm_m4(const uint16_t *x, const uint32_t *packed, const uint16_t *scales, float *y, int64_t M,
                           int64_t N, int64_t K, hipStream_t stream) {
-    constexpr int Mp = 8;  // tokens 0..3 and zero slots 4..7
+    constexpr int Mp = 4;  // token slots of the partial sums
     const int G = (int)(K / kGroup);
     const int C = G / (8 * WAVES);
-    const size_t xq_bytes = kM4Xin ? 0 : (size_t)Mp * (size_t)K * 2;
-    const size_t xe_bytes = kM4Xin ? 0 : ((size_t)(G / 8) * Mp * sizeof(int16_t) + 255) / 256 * 256;
     const size_t part_bytes = C > 1 ? (size_t)C * Mp * (size_t)N * sizeof(float) : 0;
     const size_t lds = m4_lds<WAVES>();
     int cus = 0, per_cu = 0;
     qw3_status st = cu_count(&cus);
     if (st == QW3_OK)
-        st = blocks_per_cu(reinterpret_cast<const void *>(&qgemm_m4_kernel<WAVES, kM4Xin>), 64 * WAVES, lds,
-                           &per_cu);
+        st = blocks_per_cu(reinterpret_cast<const void *>(&qgemm_m4_kernel<WAVES>), 64 * WAVES, lds, &per_cu);
     if (st != QW3_OK) return st;
-    void *scratch = nullptr;
-    if (xq_bytes + xe_bytes + part_bytes > 0) {
-        st = workspace(stream, xq_bytes + xe_bytes + part_bytes, &scratch);
+    float *part = nullptr;
+    if (part_bytes > 0) {
+        void *scratch = nullptr;
+        st = workspace(stream, part_bytes, &scratch);
         if (st != QW3_OK) return st;
+        part = static_cast<float *>(scratch);
     }
-    uint4 *xq = reinterpret_cast<uint4 *>(scratch);
-    int16_t *xe = reinterpret_cast<int16_t *>(static_cast<char *>(scratch) + xq_bytes);
-    float *part = reinterpret_cast<float *>(static_cast<char *>(scratch) + xq_bytes + xe_bytes);
     const int64_t tiles = ceil_div(N, 16);
     int64_t tb = (int64_t)cus * per_cu / C;
     if (tb < 1) tb = 1;
     if (tb > tiles) tb = tiles;
-    if (!kM4Xin) {
-        const int64_t units = (int64_t)(G / 8) * Mp * 32;
-        hipLaunchKernelGGL(prep_x_slice_kernel, dim3((unsigned)ceil_div(units, 256)), dim3(256), 0, stream, x, xq,
-                           xe, (int)M, Mp, K, G / 8);
-        st = check_launch();
-        if (st != QW3_OK) return st;
-    }
-    hipLaunchKernelGGL((qgemm_m4_kernel<WAVES, kM4Xin>), dim3((unsigned)(tb * C)), dim3(64 * WAVES), lds, stream,
-                       xq, xe, x, packed, scales, C > 1 ? part : y, (int)M, N, G, C, (int64_t)Mp * N);
+    hipLaunchKernelGGL(qgemm_m4_kernel<WAVES>, dim3((unsigned)(tb * C)), dim3(64 * WAVES), lds, stream, x, packed,
+                       scales, C > 1 ? part : y, (int)M, N, G, C, (int64_t)Mp * N);
     st = check_launch();
     if (st != QW3_OK || C == 1) return st;
     const int64_t count = M * N;
