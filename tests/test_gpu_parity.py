@@ -440,6 +440,20 @@ def test_qgemm_scales_view_not_16_byte_aligned(off, m):
     assert_close(y, yr, a, "qgemm scales view")
 
 
+@pytest.mark.parametrize("m", [3, 9, 20, 40, 130])
+def test_qgemm_max_k(m):
+    """K = 131072, the largest accepted: 16, 32 or more K chunks on the
+    batched paths, 1024 groups per row on the tile and prefill paths."""
+    n, k = 24, 131072
+    c = synth.codes_all8(4900 + m, n, k)
+    s = synth.scales(4901, n, k // 128, sigma=0.02, eps=1e-3)
+    x = synth.activations(4902 + m, m, k)
+    say("qgemm K = %d, M = %d" % (k, m))
+    y = host(q().qgemm_w3g128_smallM(dev(x), gpu_pack(c), dev(s)))
+    yr, a = oracle.gemm(x, oracle.pack(c), s, k)
+    assert_close(y, yr, a, "qgemm max K M=%d" % m)
+
+
 def _random_shapes(count, seed):
     """Seeded (M, N, K) across every dispatch rule: M = 1, up to 4 tokens,
     passes of 16 and 32, the 128-row tiles and the prefill tiles; K / 128 a
