@@ -574,3 +574,60 @@ def test_prefill_m512_full_size(name):
     rows = sample_rows(n, count=24, seed=5)
     yr, a = oracle.gemm(x, oracle.pack(c[rows]), s[rows], k)
     assert_close(y[:, rows], yr, a, "prefill %s" % name)
+
+
+# ------------------------------------------------------- graph capture ----
+
+def test_graph_capture_replays_match_eager():
+    """The product calls captured in a HIP graph on a user stream (after one
+    call of each size on that stream, so nothing is allocated while
+    capturing), replayed three times with new activations copied into the
+    captured buffers between replays: every replay equals the eager calls
+    bit for bit.  Covers batch 1, up to 4 tokens, 16 and 32 tokens (K in two
+    chunks plus the chunk sum) and the prefill tiles."""
+    n, k = 96, 8192
+    c = synth.codes_all8(8100, n, k)
+    s = synth.scales(8101, n, k // 128, sigma=0.02, eps=1e-3)
+    packed, sd = gpu_pack(c), dev(s)
+    ms = [1, 3, 16, 32, 300]
+    say("graph capture", ms)
+    xs = [torch.zeros((m, k), dtype=torch.int16, device="cuda") for m in ms]
+    ys = [torch.zeros((m, n), dtype=torch.float32, device="cuda") for m in ms]
+
+    def calls():
+        for x, y in zip(xs, ys):
+            if x.shape[0] == 1:
+                q().qgemv_w3g128(x.view(-1), packed, sd, out=y.view(-1))
+            else:
+                q().qgemm_w3g128_smallM(x, packed, sd, out=y)
+
+    def load(seed):
+        for i, (x, m) in enumerate(zip(xs, ms)):
+            x.copy_(dev(synth.activations(seed + i, m, k)))
+
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        load(8200)
+        calls()  # sizes the workspace of this stream before capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        calls()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        seed = 8300 + 10 * rep
+        with torch.cuda.stream(stream):
+            load(seed)
+            calls()
+        torch.cuda.synchronize()
+        eager = [host(y).copy() for y in ys]
+        for y in ys:
+            y.fill_(float("nan"))
+        with torch.cuda.stream(stream):
+            load(seed)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for m, y, e in zip(ms, ys, eager):
+            assert np.array_equal(host(y).view(np.uint32), e.view(np.uint32)), \
+                "graph replay %d differs from the eager call at M=%d" % (rep, m)
