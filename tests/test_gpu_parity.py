@@ -631,3 +631,35 @@ def test_graph_capture_replays_match_eager():
         for m, y, e in zip(ms, ys, eager):
             assert np.array_equal(host(y).view(np.uint32), e.view(np.uint32)), \
                 "graph replay %d differs from the eager call at M=%d" % (rep, m)
+
+
+def test_streams_have_their_own_workspace():
+    """Batched calls queued on two streams at once (different M, so the
+    workspaces differ in size and layout, K split so partial sums are
+    staged) give the same results as calls made one at a time; a later,
+    larger call on one stream grows only that stream's workspace."""
+    n, k = 200, 16384
+    c = synth.codes_all8(8500, n, k)
+    s = synth.scales(8501, n, k // 128, sigma=0.02, eps=1e-3)
+    packed, sd = gpu_pack(c), dev(s)
+    say("two streams")
+    cases = [(16, 8502), (32, 8503), (9, 8504), (24, 8505)]
+    xs = [dev(synth.activations(seed, m, k)) for m, seed in cases]
+    ref = [host(q().qgemm_w3g128_smallM(x, packed, sd)) for x in xs]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda") for m, _ in cases]
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for i, (x, y) in enumerate(zip(xs, outs)):
+            with torch.cuda.stream(streams[i % 2]):
+                q().qgemm_w3g128_smallM(x, packed, sd, out=y)
+        torch.cuda.synchronize()
+        for i, (y, r) in enumerate(zip(outs, ref)):
+            assert np.array_equal(host(y).view(np.uint32), r.view(np.uint32)), "stream case %d, pass %d" % (i, rep)
+            y.fill_(float("nan"))
+    big = dev(synth.activations(8506, 300, k))
+    with torch.cuda.stream(streams[0]):
+        yb = q().qgemm_w3g128_smallM(big, packed, sd)
+    torch.cuda.synchronize()
+    yr, a = oracle.gemm(synth.activations(8506, 300, k), oracle.pack(c), s, k)
+    assert_close(host(yb), yr, a, "grown workspace")
