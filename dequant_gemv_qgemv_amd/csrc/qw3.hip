@@ -1478,20 +1478,18 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_m4_kernel(const uint16_t *__
     const int64_t W = (int64_t)G * kWordsPerGroup;
     float *y = out + (int64_t)chunk * out_chunk;
 
-    // The bf16 activations straight from x, before the ring's loads: lane
-    // (n, j) reads all of group g0 + 4q + j of token n / 4 (the four lanes of
-    // a token and group share the addresses; tokens past M read token M - 1,
-    // whose rows of D are not stored).
+    // The bf16 activations straight from x, before the ring's loads: the
+    // four lanes n = 4t .. 4t + 3 of lane row j share token t and group
+    // g0 + 4q + j, and lane n reads block n % 4 of it (tokens past M read
+    // token M - 1, whose rows of D are not stored).
     int et;
     h8_t xa[NS][16];
-    uint4 xb[NS][4][4];
+    uint4 xb[NS][4];
     {
         const int64_t K = (int64_t)G * kGroup;
         const int t = (n >> 2) < M ? (n >> 2) : M - 1;
 #pragma unroll
-        for (int q = 0; q < NS; ++q)
-#pragma unroll
-            for (int b = 0; b < 4; ++b) load_x32(x + t * K + (int64_t)(g0 + 4 * q + j) * kGroup + 32 * b, xb[q][b]);
+        for (int q = 0; q < NS; ++q) load_x32(x + t * K + (int64_t)(g0 + 4 * q + j) * kGroup + 32 * (n & 3), xb[q]);
     }
     // Unconditional loads: tiles past the last re-read it, rows past N read row N - 1.
     auto load = [&](int64_t t, int q, MrSlot &sl) {
@@ -1512,29 +1510,35 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_m4_kernel(const uint16_t *__
     __builtin_amdgcn_sched_barrier(0);
     {
         // One exponent per token over the wave's slice: the largest |x| over
-        // the token's 16 lanes (lane ^ 17 and lane ^ 34 keep n / 4) maps to
-        // [2^14, 2^15).  Lane row j accumulates token j, held by lane 4j.
+        // the token's 4 x 4 lanes (the quad: the group's blocks; lane ^ 16
+        // and lane ^ 32: its groups) maps to [2^14, 2^15).  Each lane
+        // converts its block; the quad then hands all four blocks to its lane
+        // n % 4 = j (a DPP broadcast per dword), the only one whose row takes
+        // k chunk j: the other rows are zero.  Lane row j accumulates token
+        // j, held by lane 4j.
         uint32_t mx = 0;
 #pragma unroll
-        for (int q = 0; q < NS; ++q)
-#pragma unroll
-            for (int b = 0; b < 4; ++b) mx = max(mx, absmax32(xb[q][b]));
-        mx = max(mx, (uint32_t)__shfl_xor((int)mx, 17));
-        mx = max(mx, (uint32_t)__shfl_xor((int)mx, 34));
+        for (int q = 0; q < NS; ++q) mx = max(mx, absmax32(xb[q]));
+        mx = max(mx, dpp_u32<kDppQuadXor1>(mx));
+        mx = max(mx, dpp_u32<kDppQuadXor2>(mx));
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, 16));
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32));
         const int e = group_exponent(mx);
         const bool on = (n & 3) == j;
 #pragma unroll
-        for (int q = 0; q < NS; ++q)
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                uint32_t o[16];
-                convert_block(xb[q][b], e, o);
+        for (int q = 0; q < NS; ++q) {
+            uint32_t o[16];
+            convert_block(xb[q], e, o);
+            static_for<4>([&](auto bc) __attribute__((always_inline)) {
+                constexpr int b = decltype(bc)::value;
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    const h8_t a = __builtin_bit_cast(h8_t, make_uint4(o[4 * v], o[4 * v + 1], o[4 * v + 2], o[4 * v + 3]));
-                    xa[q][4 * b + v] = on ? a : h8_t{0, 0, 0, 0, 0, 0, 0, 0};
+                    const uint4 f = make_uint4(dpp_u32<0x55 * b>(o[4 * v]), dpp_u32<0x55 * b>(o[4 * v + 1]),
+                                               dpp_u32<0x55 * b>(o[4 * v + 2]), dpp_u32<0x55 * b>(o[4 * v + 3]));
+                    xa[q][4 * b + v] = on ? __builtin_bit_cast(h8_t, f) : h8_t{0, 0, 0, 0, 0, 0, 0, 0};
                 }
-            }
+            });
+        }
         et = __shfl(e, 4 * j);
     }
 
