@@ -1278,9 +1278,10 @@ struct MrSlot {
     u32x2v_t s;     // bf16 scales of groups g0 + 4q .. g0 + 4q + 3 of row n
 };
 
-template <int WAVES, int TS>
+template <int WAVES, int TS, bool XH>
 __global__ __launch_bounds__(64 * WAVES) void qgemm_mr_kernel(const uint4 *__restrict__ xq,
                                                             const int16_t *__restrict__ xe,
+                                                            const uint16_t *__restrict__ x,
                                                             const uint32_t *__restrict__ packed,
                                                             const uint16_t *__restrict__ scales,
                                                             float *__restrict__ out, int M, int64_t N, int G, int C,
@@ -1302,38 +1303,52 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_mr_kernel(const uint4 *__res
     const int64_t W = (int64_t)G * kWordsPerGroup;
     float *y = out + (int64_t)chunk * out_chunk;
 
-    // The slice's activation exponents (one per token; the wave's groups lie
-    // in one 8-group slice) through the scalar unit: they stay out of the
-    // vector memory counter, whose waits in the loop count the ring's loads
-    // exactly.  Lane row j scales tokens 16 ts + 4j .. 16 ts + 4j + 3.
     int et[TS][4];
-    {
-        const int *xs = reinterpret_cast<const int *>(xe + (int64_t)(g0 / 8) * Mp);
-        int ew[8 * TS];
-#pragma unroll
-        for (int i = 0; i < 8 * TS; ++i) ew[i] = xs[i];
-#pragma unroll
-        for (int ts = 0; ts < TS; ++ts)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int b = 8 * ts + r / 2;
-                const int w0 = j == 0 ? ew[b] : j == 1 ? ew[b + 2] : j == 2 ? ew[b + 4] : ew[b + 6];
-                et[ts][r] = (r & 1) ? (w0 >> 16) : (int)(int16_t)(w0 & 0xFFFF);
-            }
-    }
-    // Activations first (L2-resident), then the ring: the loop's waits for
-    // the ring count exactly.  Token slots past M read slot M - 1 again (their
-    // rows of D are never stored), so a load touches only the lines of the M
-    // real tokens.
     h8_t xa[GW][TS][4];
+    [[maybe_unused]] uint4 xh[4][4];
+    if constexpr (XH) {
+        // Up to 8 tokens (TS = 1): the activations straight from x.  Lane
+        // (n, j) reads block j of groups g0 + 4(n / 8) .. + 3 of token n % 8
+        // (tokens past M read token M - 1; rows 8..15 of D are never stored),
+        // so lanes n and n + 8 share the wave's 8 groups of one token.
+        static_assert(!XH || TS == 1, "in-kernel conversion for one token set");
+        const int64_t K = (int64_t)G * kGroup;
+        const int t = (n & 7) < M ? (n & 7) : M - 1;
 #pragma unroll
-    for (int ts = 0; ts < TS; ++ts) {
-        const int m = 16 * ts + n < M ? 16 * ts + n : M - 1;
+        for (int k = 0; k < 4; ++k)
+            load_x32(x + t * K + (int64_t)(g0 + 4 * (n >> 3) + k) * kGroup + 32 * j, xh[k]);
+    } else {
+        // The slice's activation exponents (one per token; the wave's groups lie
+        // in one 8-group slice) through the scalar unit: they stay out of the
+        // vector memory counter, whose waits in the loop count the ring's loads
+        // exactly.  Lane row j scales tokens 16 ts + 4j .. 16 ts + 4j + 3.
+        {
+            const int *xs = reinterpret_cast<const int *>(xe + (int64_t)(g0 / 8) * Mp);
+            int ew[8 * TS];
 #pragma unroll
-        for (int gi = 0; gi < GW; ++gi)
+            for (int i = 0; i < 8 * TS; ++i) ew[i] = xs[i];
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
-                xa[gi][ts][u] = __builtin_bit_cast(h8_t, xq[(((int64_t)(g0 + gi) * 4 + u) * 4 + j) * Mp + m]);
+            for (int ts = 0; ts < TS; ++ts)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int b = 8 * ts + r / 2;
+                    const int w0 = j == 0 ? ew[b] : j == 1 ? ew[b + 2] : j == 2 ? ew[b + 4] : ew[b + 6];
+                    et[ts][r] = (r & 1) ? (w0 >> 16) : (int)(int16_t)(w0 & 0xFFFF);
+                }
+        }
+        // Activations first (L2-resident), then the ring: the loop's waits for
+        // the ring count exactly.  Token slots past M read slot M - 1 again (their
+        // rows of D are never stored), so a load touches only the lines of the M
+        // real tokens.
+#pragma unroll
+        for (int ts = 0; ts < TS; ++ts) {
+            const int m = 16 * ts + n < M ? 16 * ts + n : M - 1;
+#pragma unroll
+            for (int gi = 0; gi < GW; ++gi)
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    xa[gi][ts][u] = __builtin_bit_cast(h8_t, xq[(((int64_t)(g0 + gi) * 4 + u) * 4 + j) * Mp + m]);
+        }
     }
     // Unconditional loads: tiles past the last re-read it, rows past N read row N - 1.
     auto load = [&](int64_t t, int q, MrSlot &sl) {
@@ -1352,6 +1367,35 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_mr_kernel(const uint4 *__res
     __builtin_amdgcn_sched_barrier(0);
     load(1 / NS, 1 % NS, ring[1]);
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (XH) {
+        // One exponent per token over the slice (the largest |x| over lanes
+        // n, n + 8 and the four lane rows).  Each lane converts its 4 groups;
+        // a DPP row rotation by 8 brings the other 4 from lane n ^ 8, so
+        // every lane holds all 8 groups of token n % 8.
+        uint32_t mx = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) mx = max(mx, absmax32(xh[k]));
+        mx = max(mx, dpp_u32<0x128>(mx));
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, 16));
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32));
+        const int e = group_exponent(mx);
+        const bool lo = n < 8;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            uint32_t o[16];
+            convert_block(xh[k], e, o);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint4 own = make_uint4(o[4 * u], o[4 * u + 1], o[4 * u + 2], o[4 * u + 3]);
+                const uint4 oth = make_uint4(dpp_u32<0x128>(o[4 * u]), dpp_u32<0x128>(o[4 * u + 1]),
+                                             dpp_u32<0x128>(o[4 * u + 2]), dpp_u32<0x128>(o[4 * u + 3]));
+                xa[k][0][u] = __builtin_bit_cast(h8_t, lo ? own : oth);
+                xa[4 + k][0][u] = __builtin_bit_cast(h8_t, lo ? oth : own);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) et[0][r] = __shfl(e, 4 * j + r);
+    }
 
     const uint32_t magic = magic_vgpr();
     f4_t acc[TS];
@@ -2438,6 +2482,9 @@ qw3_status launch_gemm_pf(const uint16_t *x, const uint32_t *packed, const uint1
 #ifndef QW3_MT_RING
 #define QW3_MT_RING 1
 #endif
+#ifndef QW3_MR_XH
+#define QW3_MR_XH 1
+#endif
 // TS = 1: passes of up to 16 tokens, through the ring kernel when the scale
 // rows are 8-byte aligned (it reads 8 bytes of scales at a time), else
 // through qgemm_mt_kernel (2 bytes at a time).  TS = 2: 17..32 tokens in one
@@ -2453,8 +2500,12 @@ qw3_status launch_gemm_mt(const uint16_t *x, const uint32_t *packed, const uint1
     const size_t xq_bytes = (size_t)Mp * (size_t)K * 2;
     const size_t xe_bytes = ((size_t)(G / 8) * Mp * sizeof(int16_t) + 255) / 256 * 256;
     const size_t part_bytes = C > 1 ? (size_t)C * Mp * (size_t)N * sizeof(float) : 0;
-    const void *kern = ring ? reinterpret_cast<const void *>(&qgemm_mr_kernel<WAVES, TS>)
-                            : reinterpret_cast<const void *>(&qgemm_mt_kernel<WAVES>);
+    // Up to 6 tokens: the ring kernel converts the activations itself (at 8
+    // it measured the same as the conversion launch).
+    const bool xh = QW3_MR_XH && ring && TS == 1 && M <= 6;
+    const void *kern = xh     ? reinterpret_cast<const void *>(&qgemm_mr_kernel<WAVES, TS, TS == 1>)
+                       : ring ? reinterpret_cast<const void *>(&qgemm_mr_kernel<WAVES, TS, false>)
+                              : reinterpret_cast<const void *>(&qgemm_mt_kernel<WAVES>);
     const size_t lds = ring ? mr_lds<WAVES, TS>() : 0;
     int cus = 0, per_cu = 0;
     qw3_status st = cu_count(&cus);
@@ -2474,15 +2525,20 @@ qw3_status launch_gemm_mt(const uint16_t *x, const uint32_t *packed, const uint1
     if (tb > tiles) tb = tiles;
     for (int64_t m0 = 0; m0 < M && st == QW3_OK; m0 += Mp) {
         const int mc = (int)(M - m0 < Mp ? M - m0 : Mp);
-        const int64_t units = (int64_t)(G / 8) * Mp * 32;
-        hipLaunchKernelGGL(prep_x_slice_kernel, dim3((unsigned)ceil_div(units, 256)), dim3(256), 0, stream,
-                           x + m0 * K, xq, xe, mc, Mp, K, G / 8);
-        st = check_launch();
-        if (st != QW3_OK) break;
+        if (!xh) {
+            const int64_t units = (int64_t)(G / 8) * Mp * 32;
+            hipLaunchKernelGGL(prep_x_slice_kernel, dim3((unsigned)ceil_div(units, 256)), dim3(256), 0, stream,
+                               x + m0 * K, xq, xe, mc, Mp, K, G / 8);
+            st = check_launch();
+            if (st != QW3_OK) break;
+        }
         float *dst = C > 1 ? part : y + m0 * N;
-        if (ring)
-            hipLaunchKernelGGL((qgemm_mr_kernel<WAVES, TS>), dim3((unsigned)(tb * C)), dim3(64 * WAVES), lds, stream,
-                               xq, xe, packed, scales, dst, mc, N, G, C, (int64_t)Mp * N);
+        if (xh)
+            hipLaunchKernelGGL((qgemm_mr_kernel<WAVES, TS, TS == 1>), dim3((unsigned)(tb * C)), dim3(64 * WAVES), lds,
+                               stream, xq, xe, x + m0 * K, packed, scales, dst, mc, N, G, C, (int64_t)Mp * N);
+        else if (ring)
+            hipLaunchKernelGGL((qgemm_mr_kernel<WAVES, TS, false>), dim3((unsigned)(tb * C)), dim3(64 * WAVES), lds,
+                               stream, xq, xe, x + m0 * K, packed, scales, dst, mc, N, G, C, (int64_t)Mp * N);
         else
             hipLaunchKernelGGL(qgemm_mt_kernel<WAVES>, dim3((unsigned)(tb * C)), dim3(64 * WAVES), 0, stream, xq, xe,
                                packed, scales, dst, mc, N, G, C, (int64_t)Mp * N);
