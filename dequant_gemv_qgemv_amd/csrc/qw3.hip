@@ -2497,12 +2497,12 @@ qw3_status launch_gemm_mt(const uint16_t *x, const uint32_t *packed, const uint1
     const bool ring = TS == 2 || (QW3_MT_RING && aligned(scales, 8));
     constexpr int Mp = 16 * TS;
     const int C = G / ((8 / TS) * WAVES);
-    const size_t xq_bytes = (size_t)Mp * (size_t)K * 2;
-    const size_t xe_bytes = ((size_t)(G / 8) * Mp * sizeof(int16_t) + 255) / 256 * 256;
-    const size_t part_bytes = C > 1 ? (size_t)C * Mp * (size_t)N * sizeof(float) : 0;
     // Up to 6 tokens: the ring kernel converts the activations itself (at 8
     // it measured the same as the conversion launch).
     const bool xh = QW3_MR_XH && ring && TS == 1 && M <= 6;
+    const size_t xq_bytes = xh ? 0 : (size_t)Mp * (size_t)K * 2;
+    const size_t xe_bytes = xh ? 0 : ((size_t)(G / 8) * Mp * sizeof(int16_t) + 255) / 256 * 256;
+    const size_t part_bytes = C > 1 ? (size_t)C * Mp * (size_t)N * sizeof(float) : 0;
     const void *kern = xh     ? reinterpret_cast<const void *>(&qgemm_mr_kernel<WAVES, TS, TS == 1>)
                        : ring ? reinterpret_cast<const void *>(&qgemm_mr_kernel<WAVES, TS, false>)
                               : reinterpret_cast<const void *>(&qgemm_mt_kernel<WAVES>);
@@ -2512,7 +2512,7 @@ qw3_status launch_gemm_mt(const uint16_t *x, const uint32_t *packed, const uint1
     if (st == QW3_OK) st = blocks_per_cu(kern, 64 * WAVES, lds, &per_cu);
     if (st != QW3_OK) return st;
     void *scratch = nullptr;
-    {
+    if (xq_bytes + xe_bytes + part_bytes > 0) {
         const qw3_status ws = workspace(stream, xq_bytes + xe_bytes + part_bytes, &scratch);
         if (ws != QW3_OK) return ws;
     }

@@ -133,13 +133,13 @@ qw3_status qgemv_w3g128_multi(const uint16_t *x, int32_t count, const int32_t *c
  *   y [M, N] float32, written: y[m][n] = sum_k x[m][k] * scales[n][k/128] * (c[n][k] - 4)
  * Any M >= 0 is accepted.  M == 1 runs the batch-1 kernel; small M streams
  * the weights once for the whole batch through bf16-exact fp16 matrix-core
- * products; large M (prefill) runs a tiled matrix-core kernel.  For M > 4
+ * products; large M (prefill) runs a tiled matrix-core kernel.  For M > 6
  * the call uses a device workspace that the library keeps per (device,
  * stream): the activations converted to fp16 (2 bytes per element, M rounded
  * up to 16 or 32, or to whole 128- or 256-token tiles) plus, when K is split
  * across workgroups, fp32 partial sums (4 bytes per output element and K
- * chunk).  For 2 <= M <= 4 the kernel converts the activations itself and the
- * workspace holds only partial sums, when K is split (K = 28672, for one).  It is allocated (hipMalloc) by the first
+ * chunk).  For 2 <= M <= 6 the kernels convert the activations themselves and
+ * the workspace holds only partial sums, when K is split (K = 28672, for one).  It is allocated (hipMalloc) by the first
  * call on a stream, grown -- after synchronizing that stream -- when a later
  * call needs more, and held until the process ends.  Calls on one stream run
  * in order and share it; calls on different streams use different buffers.
