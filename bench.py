@@ -275,12 +275,31 @@ def dense_branch(torch, q, name, n, k, rot, fused_ms):
             "gemm_TFLOP/s": round(2.0 * m * n * k / ms_mm / 1e9, 2)}
 
 
+CEILING_SRC = os.path.join(ROOT, "bench_ceiling.hip")
+CEILING_LIB = os.path.join(ROOT, "bench_ceiling.so")
+
+
+def build_ceiling() -> str:
+    """Compile the streaming-read probe (bench_ceiling.hip, a measurement tool
+    beside this script; the product library does not contain it) with the
+    library's own hipcc flags."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "qw3_build_step", os.path.join(ROOT, "dequant_gemv_qgemv_amd", "_build.py"))
+    step = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(step)
+    step.compile_hip(CEILING_SRC, CEILING_LIB)
+    return CEILING_LIB
+
+
 def read_sweep_ceiling(torch):
-    """A plain streaming-read kernel (libqw3_ceiling.so) over slices of a 1 GiB
+    """A plain streaming-read kernel (bench_ceiling.so) over slices of a 1 GiB
     buffer the size of the gate_proj weights + scales, rotated so no slice is
     cache resident: the read rate HBM gives a kernel on this part."""
     import ctypes
-    lib = ctypes.CDLL(os.path.join(ROOT, "dequant_gemv_qgemv_amd", "libqw3_ceiling.so"))
+    if not os.path.exists(CEILING_LIB):
+        raise SystemExit("bench_ceiling.so is not built: run __graft_entry__.build() first")
+    lib = ctypes.CDLL(CEILING_LIB)
     lib.qw3_read_sweep.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
                                    ctypes.c_void_p]
     lib.qw3_read_sweep.restype = ctypes.c_int

@@ -1,6 +1,7 @@
 // Streaming-read ceiling: the HBM read rate a plain kernel reaches on this
 // part, the reference beside which bench.py --ceiling reports the GEMV.
-// Measurement tool only (libqw3_ceiling.so); the product library does not use it.
+// Measurement tool only (bench_ceiling.so, built beside bench.py); the
+// product library does not contain or use it.
 //
 // Every workgroup reads 16-byte chunks in a grid-stride loop, four loads in
 // flight per lane, and folds them with XOR; the result is stored only if it

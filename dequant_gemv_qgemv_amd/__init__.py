@@ -36,11 +36,12 @@ __all__ = [
     "QW3_ERR_SHAPE",
     "QW3_ERR_ALIGN",
     "QW3_ERR_HIP",
+    "QW3_ERR_CAPTURE",
     "QW3_MAX_K",
     "QW3_MAX_MULTI",
 ]
 
-QW3_OK, QW3_ERR_NULL, QW3_ERR_SHAPE, QW3_ERR_ALIGN, QW3_ERR_HIP = 0, -1, -2, -3, -4
+QW3_OK, QW3_ERR_NULL, QW3_ERR_SHAPE, QW3_ERR_ALIGN, QW3_ERR_HIP, QW3_ERR_CAPTURE = 0, -1, -2, -3, -4, -5
 QW3_MAX_K = 131072
 QW3_MAX_MULTI = 4
 GROUP = 128

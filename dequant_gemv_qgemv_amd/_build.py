@@ -8,9 +8,6 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "qw3.hip")
 LIB = os.path.join(HERE, "libqw3.so")
-# measurement tool beside the product: the streaming-read ceiling of bench.py --ceiling
-CEILING_SRC = os.path.join(HERE, "csrc", "ceiling.hip")
-CEILING_LIB = os.path.join(HERE, "libqw3_ceiling.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 HIP_FLAGS = [
@@ -26,7 +23,8 @@ HIP_FLAGS = [
 ]
 
 
-def _compile(src: str, lib: str, extra_flags) -> None:
+def compile_hip(src: str, lib: str, extra_flags=None) -> None:
+    """hipcc `src` (gfx950, the flags above) into the shared library `lib`."""
     tmp = lib + ".tmp%d" % os.getpid()
     cmd = [HIPCC] + HIP_FLAGS + list(extra_flags or []) + ["-o", tmp, src]
     subprocess.run(cmd, check=True)
@@ -34,9 +32,8 @@ def _compile(src: str, lib: str, extra_flags) -> None:
 
 
 def build(extra_flags=None) -> str:
-    """Always recompiles both libraries; returns the path of the product library."""
-    _compile(SRC, LIB, extra_flags)
-    _compile(CEILING_SRC, CEILING_LIB, extra_flags)
+    """Always recompiles the library; returns its path."""
+    compile_hip(SRC, LIB, extra_flags)
     return LIB
 
 

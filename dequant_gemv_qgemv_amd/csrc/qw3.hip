@@ -22,13 +22,27 @@
 // as long as the activations are paired the same way, so activations are
 // converted once into the same pairing (kPairs below).
 //
-// Activations.  x is bf16; the products use fp16 operands, so each group of
-// 128 activations is scaled by a power of two 2^-e that brings its largest
-// magnitude into [2^14, 2^15), and each element by its slot's 2^-p, and is
-// then rounded to fp16.  bf16 has 8 significant bits and fp16 11, so this is
-// exact for every element within 2^24 of the group's largest; 2^e is
-// multiplied back in fp32 together with the weight scale.  Every product is
-// then exact and only the fp32 accumulation rounds.
+// Activations.  x is bf16; the products use fp16 operands, so each exponent
+// set (a group of 128 activations at batch 1, an 8-group slice of a token in
+// batched decode, a whole token in the tile kernels) is scaled by a power of
+// two 2^-e that brings its largest magnitude into [2^14, 2^15), each element
+// by its slot's 2^-p (p <= 7), and rounded to fp16.  bf16 has 8 significant
+// bits and fp16 11, so every element of magnitude at least 2^(e-7) lands in
+// the fp16 normal range and converts exactly; 2^e is multiplied back in fp32
+// together with the weight scale.  Those products are exact and only the fp32
+// accumulation rounds.
+//
+// Exactness guard.  Smaller elements (about 2^21 or more below the largest of
+// their set) may be rounded or flushed.  The conversion sums their magnitudes
+// per (token, group) into D, which bounds what they can change in any output:
+// |sum_k w_k (x_k - x'_k)| <= 4 sum_g |s_g| D_g.  When some D is non-zero a
+// pass after the fast loop (fixup_outputs) evaluates that bound for every
+// output the workgroup wrote and recomputes in fp32 the ones above 2^-21, so
+// each output meets |y - y_exact| <= 1e-4 sum_k |w_k x_k| + 1e-6 whatever the
+// spread of x.  The tile kernels also fold the group scale into the fp16
+// weight, exact while every scale of the row lies within 2^21 of its largest;
+// other rows are recomputed by the same pass.  The fast loops are unchanged:
+// the pass costs nothing when every D is zero and every row folds exactly.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -233,6 +247,54 @@ __device__ __forceinline__ int group_exponent(uint32_t absmax_bits) {
     return __builtin_amdgcn_frexp_expf(bf16_to_f32(absmax_bits)) - 15;
 }
 
+// Largest magnitude and smallest non-zero magnitude (0x10000 when all are
+// zero) of 32 bf16 values, as bf16 magnitude bit patterns; packed 16-bit max
+// and min, one of each per two values.
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void block_stats(const uint4 (&xb)[4], uint32_t &mx, uint32_t &mn) {
+    u16x2_t vmax = {0, 0}, vmin = {0xFFFF, 0xFFFF};
+    const u16x2_t one = {1, 1};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t d[4] = {xb[i].x, xb[i].y, xb[i].z, xb[i].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const u16x2_t v = __builtin_bit_cast(u16x2_t, d[j] & 0x7FFF7FFFu);
+            vmax = __builtin_elementwise_max(vmax, v);
+            vmin = __builtin_elementwise_min(vmin, v - one);  // zero wraps to 0xFFFF
+        }
+    }
+    mx = max((uint32_t)vmax.x, (uint32_t)vmax.y);
+    mn = min((uint32_t)vmin.x, (uint32_t)vmin.y) + 1u;
+}
+
+// bf16 magnitude bits of 2^(e-7): elements at least this large convert to
+// fp16 normals exactly under exponent e for every slot offset p <= 7.
+__device__ __forceinline__ uint32_t exact_floor_bits(int e) {
+    const int b = e + 120;  // biased bf16 exponent of 2^(e-7)
+    if (b >= 1) return (uint32_t)min(b, 255) << 7;
+    if (b >= -6) return 1u << (b + 6);  // a bf16 subnormal
+    return 0u;
+}
+
+// Sum of |x| over the elements of the block below 2^(e-7) (the ones whose
+// fp16 form may be rounded or flushed), in fp32.
+__device__ __forceinline__ float small_mass(const uint4 (&xb)[4], int e) {
+    const uint32_t fl = exact_floor_bits(e);
+    float d = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t w[4] = {xb[i].x, xb[i].y, xb[i].z, xb[i].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t lo = w[j] & 0x7FFFu, hi = (w[j] >> 16) & 0x7FFFu;
+            if (lo < fl) d += bf16_to_f32(lo);
+            if (hi < fl) d += bf16_to_f32(hi);
+        }
+    }
+    return d;
+}
+
 // 32 bf16 values -> x * 2^-(e + slot offset) as fp16, arranged as the 16
 // pairs of a block (kPairs order).
 __device__ __forceinline__ void convert_block(const uint4 (&xb)[4], int e, uint32_t (&out)[16]) {
@@ -257,6 +319,144 @@ __device__ __forceinline__ void load_x32(const uint16_t *src, uint4 (&xb)[4]) {
     const uint4 *s = reinterpret_cast<const uint4 *>(src);
 #pragma unroll
     for (int i = 0; i < 4; ++i) xb[i] = s[i];
+}
+
+// ------------------------------------------------------- exact fixup pass --
+// Outputs whose bound 4 sum_g |s_g| D_g exceeds kFixBudget are recomputed by
+// exact_output.  The budget leaves half of the 1e-6 absolute term of the
+// accuracy bound for the fast path's own fp32 rounding.
+constexpr float kFixBudget = 0x1p-21f;
+constexpr int kNzCap = 128;  // compacted list of groups with a non-zero D
+
+// sum_{g0 <= g < g1} s[g] * sum_{k in g} (c_k - 4) x_k in fp32 by one thread,
+// read the plain way: code i of a 32-code block is bits [3i, 3i + 3) of its
+// three little-endian words.  Each product (c - 4) x is exact in fp32; a
+// group's 128 products are added in order, the group sums (times their
+// scale) in runs of 32 groups, the runs in order.
+__device__ __noinline__ float exact_output(const uint16_t *__restrict__ xrow, const uint32_t *__restrict__ wrow,
+                                           const uint16_t *__restrict__ srow, int g0, int g1) {
+    float tot = 0.f;
+    for (int gb = g0; gb < g1; gb += 32) {
+        const int ge = min(gb + 32, g1);
+        float run = 0.f;
+        for (int g = gb; g < ge; ++g) {
+            const uint32_t *gw = wrow + (int64_t)g * kWordsPerGroup;
+            float acc = 0.f;
+            for (int b = 0; b < 4; ++b) {
+                const uint32_t w[4] = {gw[3 * b], gw[3 * b + 1], gw[3 * b + 2], 0u};
+                uint4 xb[4];
+                load_x32(xrow + (int64_t)g * kGroup + 32 * b, xb);
+                const uint32_t xw[16] = {xb[0].x, xb[0].y, xb[0].z, xb[0].w, xb[1].x, xb[1].y, xb[1].z, xb[1].w,
+                                         xb[2].x, xb[2].y, xb[2].z, xb[2].w, xb[3].x, xb[3].y, xb[3].z, xb[3].w};
+#pragma unroll
+                for (int i = 0; i < 32; ++i) {
+                    const int bit = 3 * i;
+                    const uint32_t c = __builtin_amdgcn_alignbit(w[(bit >> 5) + 1], w[bit >> 5], bit & 31) & 7u;
+                    const float xv = bf16_to_f32((i & 1) ? (xw[i >> 1] >> 16) : (xw[i >> 1] & 0xFFFFu));
+                    acc = fmaf((float)((int)c - 4), xv, acc);
+                }
+            }
+            run = fmaf(acc, bf16_to_f32(srow[g]), run);
+        }
+        tot += run;
+    }
+    return tot;
+}
+
+// Whether folding the scales of row srow[g0..g1) into fp16 weights as
+// s * 2^-E, E chosen so that the largest maps to [8, 16), is inexact for some
+// non-zero scale: exact iff s * 2^-E >= 2^-17 (8 significant bits then sit at
+// or above fp16's smallest subnormal, and so do the products with (c-4) 2^p).
+__device__ __forceinline__ bool fold_inexact(const uint16_t *__restrict__ srow, int g0, int g1) {
+    uint32_t mx = 0, mn = 0x10000u;
+    for (int g = g0; g < g1; ++g) {
+        const uint32_t b = srow[g] & 0x7FFFu;
+        mx = max(mx, b);
+        if (b) mn = min(mn, b);
+    }
+    if (mx == 0) return false;
+    const int E = __builtin_amdgcn_frexp_expf(bf16_to_f32(mx)) - 4;
+    return bf16_to_f32(mn) < ldexpf(1.0f, E - 17);
+}
+
+// The rows a workgroup wrote: blocks blk, blk + nblk, blk + 2 nblk, ... of R
+// consecutive rows each, rows past N dropped.
+struct BlockRows {
+    int64_t blk, nblk, R, N;
+    __device__ int64_t count() const {
+        const int64_t nb = (N + R - 1) / R;
+        return blk < nb ? ((nb - blk + nblk - 1) / nblk) * R : 0;
+    }
+    __device__ int64_t row(int64_t i) const {
+        const int64_t r = (blk + (i / R) * nblk) * R + i % R;
+        return r < N ? r : -1;
+    }
+};
+
+// Wave 0 lists in nz[0..) the groups g in [g0, g1) with any_d(g); nz[kNzCap]
+// receives their count (which may exceed kNzCap).  All threads of the
+// workgroup call it (it ends with a barrier).
+template <class AnyD>
+__device__ __noinline__ int build_nz(int g0, int g1, AnyD any_d, int *nz) {
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        int cnt = 0;
+        for (int base = g0; base < g1; base += 64) {
+            const int g = base + lane;
+            const bool f = g < g1 && any_d(g);
+            const uint64_t bal = __ballot(f);
+            const int pos = cnt + __popcll(bal & ((uint64_t(1) << lane) - 1));
+            if (f && pos < kNzCap) nz[pos] = g;
+            cnt += __popcll(bal);
+        }
+        if (lane == 0) nz[kNzCap] = cnt;
+    }
+    __syncthreads();
+    return nz[kNzCap];
+}
+
+// The fixup pass over the outputs out[m * ldo + r] (tokens m < Mt, x row m at
+// x + m * ldx; rows r of `rows`) computed over the groups [g0, g1): with D(m, g)
+// = d_at(m, g), the outputs whose bound exceeds kFixBudget -- and, with `fold`,
+// every output of a row whose scales do not fold exactly -- are recomputed by
+// exact_output.  nz / nnz list the groups with a non-zero D (nz == nullptr or
+// nnz > kNzCap: every group of the range).  Threads tid, tid + nthr, ... take
+// one row each.  The caller orders the fast path's stores before this pass.
+template <int TB, class DAt>
+__device__ __noinline__ void fixup_outputs(const uint16_t *__restrict__ x, int64_t ldx, int Mt,
+                              const uint32_t *__restrict__ packed, const uint16_t *__restrict__ scales, int G,
+                              int g0, int g1, const BlockRows &rows, DAt d_at, const int *nz, int nnz, bool fold,
+                              float *__restrict__ out, int64_t ldo, int tid, int nthr) {
+    const int64_t W = (int64_t)G * kWordsPerGroup;
+    const bool dense = nz == nullptr || nnz > kNzCap;
+    const int ne = dense ? g1 - g0 : nnz;
+    const int64_t nrows = rows.count();
+    for (int64_t i = tid; i < nrows; i += nthr) {
+        const int64_t r = rows.row(i);
+        if (r < 0) continue;
+        const uint16_t *srow = scales + r * G;
+        const bool all = fold && fold_inexact(srow, g0, g1);
+        for (int m0 = 0; m0 < Mt; m0 += TB) {
+            float b[TB];
+#pragma unroll
+            for (int t = 0; t < TB; ++t) b[t] = 0.f;
+            if (!all) {
+                for (int e = 0; e < ne; ++e) {
+                    const int g = dense ? g0 + e : nz[e];
+                    const float s = fabsf(bf16_to_f32(srow[g]));
+#pragma unroll
+                    for (int t = 0; t < TB; ++t)
+                        if (m0 + t < Mt) b[t] = fmaf(s, d_at(m0 + t, g), b[t]);
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < TB; ++t) {
+                const int m = m0 + t;
+                if (m < Mt && (all || !(4.0f * b[t] <= kFixBudget)))
+                    out[(int64_t)m * ldo + r] = exact_output(x + (int64_t)m * ldx, packed + r * W, srow, g0, g1);
+            }
+        }
+    }
 }
 
 // ------------------------------------------------------------- qpack -------
@@ -382,19 +582,8 @@ __global__ __launch_bounds__(256) void qdequant_kernel(const uint32_t *__restric
 // memory system always holds D rows per team (the GEMV is latency-bound
 // without it).  Partial sums are reduced in a fixed order (DPP inside a wave,
 // then LDS across waves), so results are run-to-run identical.
-#ifndef QW3_GEMV_DEPTH
-#define QW3_GEMV_DEPTH 3
-#endif
-constexpr int kGemvDepth = QW3_GEMV_DEPTH;
-#ifndef QW3_GEMV_WGS
-#define QW3_GEMV_WGS 256
-#endif
-constexpr int kGemvWGS = QW3_GEMV_WGS;  // threads per workgroup, teams of T <= 64
-#ifdef QW3_GEMV_WAVES
-#define QW3_GEMV_OCC __attribute__((amdgpu_waves_per_eu(QW3_GEMV_WAVES)))
-#else
-#define QW3_GEMV_OCC
-#endif
+constexpr int kGemvDepth = 3;    // rows in flight per team
+constexpr int kGemvWGS = 256;     // threads per workgroup, teams of T <= 64
 constexpr size_t kMaxLdsX = 64 * 1024;
 
 struct RowBuf {
@@ -408,19 +597,8 @@ struct RowBuf {
 // the compiler can wait for exactly the loads a step needs (s_waitcnt vmcnt(n))
 // instead of draining every load in flight.  The extra rows are never stored
 // and the extra groups meet zero activations.
-#ifndef QW3_GEMV_NT
-#define QW3_GEMV_NT 0
-#endif
 typedef unsigned u32x4v_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint4 load_words16(const uint32_t *p) {
-#if QW3_GEMV_NT
-    // Streaming data, read once: non-temporal loads keep it out of the caches.
-    const u32x4v_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4v_t *>(p));
-    return make_uint4(v.x, v.y, v.z, v.w);
-#else
-    return *reinterpret_cast<const uint4 *>(p);
-#endif
-}
+__device__ __forceinline__ uint4 load_words16(const uint32_t *p) { return *reinterpret_cast<const uint4 *>(p); }
 
 __device__ __forceinline__ void load_row(const uint32_t *__restrict__ packed, const uint16_t *__restrict__ scales,
                                          int64_t r, int64_t N, int64_t W, int G, int g_load, RowBuf &rb) {
@@ -464,28 +642,52 @@ __device__ __forceinline__ void xstage_issue(const uint16_t *__restrict__ x, int
 // LDS layout of the converted activations: xs4[q][g] holds pairs 4q..4q+3 of
 // group g (16 bytes), q = 0..15, so that when lane g fetches its group the 64
 // lanes of each ds_read_b128 touch 64 consecutive 16-byte chunks (no bank
-// conflicts); exponents follow as int[G].
+// conflicts); exponents follow as int[G].  Each group's error mass D goes to
+// xd[g].  Returns whether this thread saw an element below its group's exact
+// range (D non-zero).
 template <int U>
-__device__ __forceinline__ void xstage_convert(const XStage<U> &st, int G, uint32_t *smem) {
+__device__ __forceinline__ bool xstage_convert(const XStage<U> &st, int G, uint32_t *smem, float *xd) {
     uint4 *xs4 = reinterpret_cast<uint4 *>(smem);                // [16][G]
     int *xe = reinterpret_cast<int *>(smem + (size_t)G * 64);  // [G]
+    bool small = false;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int idx = threadIdx.x + u * blockDim.x;  // quads share validity: 4G and blockDim are multiples of 4
-        uint32_t m = absmax32(st.raw[u]);
+        uint32_t m, mn;
+        block_stats(st.raw[u], m, mn);
         m = max(m, dpp_u32<kDppQuadXor1>(m));
         m = max(m, dpp_u32<kDppQuadXor2>(m));
+        const int eg = group_exponent(m);
+        float d = 0.f;
+        if (idx < 4 * G && mn < exact_floor_bits(eg)) d = small_mass(st.raw[u], eg);  // rare
+        small |= d != 0.f;
+        d += dpp_f32<kDppQuadXor1>(d);
+        d += dpp_f32<kDppQuadXor2>(d);
         if (idx < 4 * G) {
             const int g = idx >> 2, blk = idx & 3;
-            const int eg = group_exponent(m);
             uint32_t out[16];
             convert_block(st.raw[u], eg, out);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 xs4[(size_t)(4 * blk + i) * G + g] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
-            if (blk == 0) xe[g] = eg;
+            if (blk == 0) {
+                xe[g] = eg;
+                xd[g] = d;
+            }
         }
     }
+    return small;
+}
+
+// One word per wave in LDS: whether any lane of the wave passed `mine`.
+__device__ __forceinline__ void publish_flag(bool mine, uint32_t *flags) {
+    const uint64_t bal = __ballot(mine);
+    if ((threadIdx.x & 63) == 0) flags[threadIdx.x >> 6] = bal != 0 ? 1u : 0u;
+}
+__device__ __forceinline__ bool any_flag(const uint32_t *flags) {
+    uint32_t f = 0;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) f |= flags[w];
+    return f != 0;
 }
 
 // After a barrier: this lane's pairs and exponent (zeros for lanes without a group).
@@ -506,28 +708,35 @@ __device__ __forceinline__ void xstage_fetch(const uint32_t *smem, int G, int gl
 }
 
 // Activation staging without LDS (very long rows): each lane converts its own
-// group in two passes (max, then convert).
-__device__ __forceinline__ void xstage_lane(const uint16_t *__restrict__ x, int gl, bool lane_on,
-                                            uint32_t (&xp)[64], int &e) {
+// group in two passes (max, then convert).  Returns the group's error mass D.
+__device__ __forceinline__ float xstage_lane(const uint16_t *__restrict__ x, int gl, bool lane_on,
+                                             uint32_t (&xp)[64], int &e) {
     const uint16_t *xg = x + (size_t)(lane_on ? gl : 0) * kGroup;
-    uint32_t m = 0;
+    uint32_t m = 0, mn = 0x10000u;
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk) {
         uint4 xb[4];
         load_x32(xg + blk * 32, xb);
-        m = max(m, absmax32(xb));
+        uint32_t bm, bn;
+        block_stats(xb, bm, bn);
+        m = max(m, bm);
+        mn = min(mn, bn);
     }
     e = group_exponent(m);
+    const bool small = lane_on && mn < exact_floor_bits(e);
+    float d = 0.f;
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk) {
         uint4 xb[4];
         load_x32(xg + blk * 32, xb);
         uint32_t out[16];
         convert_block(xb, e, out);
+        if (small) d += small_mass(xb, e);  // rare
 #pragma unroll
         for (int p = 0; p < 16; ++p) xp[blk * 16 + p] = lane_on ? out[p] : 0u;
     }
     if (!lane_on) e = 0;
+    return d;
 }
 
 // Up to 4 weight matrices with the same K that share one activation vector
@@ -551,11 +760,18 @@ __device__ __forceinline__ P seg_pick(const P (&v)[kMaxSegs], int k) {
 // Teams of T <= 64 lanes (T a power of two >= G): the reduction is DPP only.
 // Order of the prologue: activation loads, then the first D rows, then the
 // conversion (which waits only for the activation loads).
+// LDS words of the batch-1 staging for G groups: xs4 [16][G] x 16 B and xe [G],
+// then xd [G] (error masses), 16 wave flags and the fixup's group list.
+__host__ __device__ constexpr size_t stage_words(int G) { return (size_t)G * 66 + 16 + kNzCap + 1; }
+
 template <int T, bool MULTI, int D>
-__global__ __launch_bounds__(kGemvWGS) QW3_GEMV_OCC void qgemv_small_kernel(const uint16_t *__restrict__ x,
-                                                               const GemvSegs sg, int G, int lds_x) {
+__global__ __launch_bounds__(kGemvWGS) void qgemv_small_kernel(const uint16_t *__restrict__ x,
+                                                               const GemvSegs sg, int G) {
     constexpr int R = kGemvWGS / T;
     extern __shared__ uint32_t smem[];
+    float *xd = reinterpret_cast<float *>(smem + (size_t)G * 65);
+    uint32_t *flags = smem + (size_t)G * 66;
+    int *nz = reinterpret_cast<int *>(flags + 16);
     // This workgroup's matrix (workgroup-uniform) and its place among the
     // workgroups of that matrix.
     int kseg = 0, blk = blockIdx.x, nblk = gridDim.x;
@@ -586,18 +802,14 @@ __global__ __launch_bounds__(kGemvWGS) QW3_GEMV_OCC void qgemv_small_kernel(cons
     uint32_t xp[64];
     int e = 0;
     RowBuf ring[E];
-    if (lds_x) {
+    {
         XStage<1> st;  // 4G <= 256 <= blockDim: one block per thread
         xstage_issue<1>(x, G, st);
 #pragma unroll
         for (int d = 0; d < D; ++d) load(row0 + d * stride, ring[d]);
-        xstage_convert<1>(st, G, smem);
+        publish_flag(xstage_convert<1>(st, G, smem, xd), flags);
         __syncthreads();
         xstage_fetch(smem, G, gl, lane_on, xp, e);
-    } else {
-#pragma unroll
-        for (int d = 0; d < D; ++d) load(row0 + d * stride, ring[d]);
-        xstage_lane(x, gl, lane_on, xp, e);
     }
     const uint32_t magic = magic_vgpr();
 
@@ -611,6 +823,12 @@ __global__ __launch_bounds__(kGemvWGS) QW3_GEMV_OCC void qgemv_small_kernel(cons
             const float tot = segment_sum<T>(part);
             if (gl == T - 1 && r < N) y[r] = tot;
         }
+    }
+    if (any_flag(flags)) {  // workgroup-uniform, rare
+        __syncthreads();
+        const int nnz = build_nz(0, G, [&](int g) { return xd[g] != 0.f; }, nz);
+        fixup_outputs<1>(x, 0, 1, packed, scales, G, 0, G, BlockRows{blk, nblk, R, N},
+                         [&](int, int g) { return xd[g]; }, nz, nnz, false, y, 0, threadIdx.x, blockDim.x);
     }
 }
 
@@ -627,12 +845,21 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // LDS_X: the converted activations fit in LDS (K <= 32768); otherwise each
 // lane converts its own group.  A template parameter, so that one prologue
 // reaches the loop and the loop's waits are exact.
+constexpr int kBigRedWords = 256;  // half-sum slots of qgemv_big_kernel: 2 (E <= 4) x E x (<= 32 halves)
+// LDS words of qgemv_big_kernel: the staging (LDS_X) or the half sums, then
+// xd [G], 16 wave flags and the fixup's group list.
+__host__ __device__ constexpr size_t big_xd_at(int G, bool lds_x) { return lds_x ? (size_t)G * 65 : kBigRedWords; }
+__host__ __device__ constexpr size_t big_words(int G, bool lds_x) { return big_xd_at(G, lds_x) + G + 16 + kNzCap + 1; }
+
 template <int MAXWGS, int D, bool LDS_X>
-__global__ __launch_bounds__(MAXWGS) QW3_GEMV_OCC void qgemv_big_kernel(const uint16_t *__restrict__ x,
+__global__ __launch_bounds__(MAXWGS) void qgemv_big_kernel(const uint16_t *__restrict__ x,
                                                          const uint32_t *__restrict__ packed,
                                                          const uint16_t *__restrict__ scales,
                                                          float *__restrict__ y, int64_t N, int G, int T) {
     extern __shared__ uint32_t smem[];
+    float *xd = reinterpret_cast<float *>(smem + big_xd_at(G, LDS_X));
+    uint32_t *flags = smem + big_xd_at(G, LDS_X) + G;
+    int *nz = reinterpret_cast<int *>(flags + 16);
     const int tid = threadIdx.x;
     const int wgs = blockDim.x;
     const int R = wgs / T;
@@ -647,6 +874,7 @@ __global__ __launch_bounds__(MAXWGS) QW3_GEMV_OCC void qgemv_big_kernel(const ui
 
     // Issue-first ring of E = D + 1 row buffers, as in qgemv_small_kernel.
     constexpr int E = D + 1;
+    static_assert(2 * E * 32 <= kBigRedWords, "half-sum slots");
     uint32_t xp[64];
     int e = 0;
     RowBuf ring[E];
@@ -659,7 +887,7 @@ __global__ __launch_bounds__(MAXWGS) QW3_GEMV_OCC void qgemv_big_kernel(const ui
             load_row(packed, scales, row0 + d * stride, N, W, G, g_load, ring[d]);
         }
         __builtin_amdgcn_sched_barrier(0);
-        xstage_convert<4>(st, G, smem);
+        publish_flag(xstage_convert<4>(st, G, smem, xd), flags);
         __syncthreads();
         xstage_fetch(smem, G, gl, lane_on, xp, e);
         __syncthreads();  // LDS is reused for the half sums below
@@ -670,7 +898,9 @@ __global__ __launch_bounds__(MAXWGS) QW3_GEMV_OCC void qgemv_big_kernel(const ui
             load_row(packed, scales, row0 + d * stride, N, W, G, g_load, ring[d]);
         }
         __builtin_amdgcn_sched_barrier(0);
-        xstage_lane(x, gl, lane_on, xp, e);
+        const float dg = xstage_lane(x, gl, lane_on, xp, e);
+        if (team == 0 && lane_on) xd[gl] = dg;  // seen after the loop's first barrier
+        publish_flag(dg != 0.f, flags);
     }
     const uint32_t magic = magic_vgpr();
 
@@ -703,6 +933,12 @@ __global__ __launch_bounds__(MAXWGS) QW3_GEMV_OCC void qgemv_big_kernel(const ui
             }
         }
         parity ^= 1;
+    }
+    if (any_flag(flags)) {  // workgroup-uniform, rare
+        __syncthreads();
+        const int nnz = build_nz(0, G, [&](int g) { return xd[g] != 0.f; }, nz);
+        fixup_outputs<1>(x, 0, 1, packed, scales, G, 0, G, BlockRows{(int64_t)blockIdx.x, (int64_t)gridDim.x, R, N},
+                         [&](int, int g) { return xd[g]; }, nz, nnz, false, y, 0, tid, wgs);
     }
 }
 
@@ -739,29 +975,16 @@ __device__ __forceinline__ void static_for(F &&f) {
 // are summed across lane rows with permlane swaps and across the four waves
 // through LDS, in a fixed order, once per batch of tiles.  Loads run three
 // super-steps ahead in a register ring, as in qgemv_small_kernel.
-#ifndef QW3_MF_BATCH
-#define QW3_MF_BATCH 8
-#endif
-#ifndef QW3_MF_ILV
-#define QW3_MF_ILV 1
-#endif
-#ifndef QW3_MF_RING
-#define QW3_MF_RING 4
-#endif
-#ifndef QW3_MF_AHEAD
-#define QW3_MF_AHEAD 3
-#endif
-constexpr int kMfBatch = QW3_MF_BATCH;  // tiles per cross-wave reduction
-constexpr int kMfRing = QW3_MF_RING;    // register ring slots (one super-step each)
-constexpr int kMfAhead = QW3_MF_AHEAD;  // super-steps loaded ahead of the one decoded
-#ifndef QW3_MF_PER_CU
-#define QW3_MF_PER_CU 1
-#endif
-constexpr int kMfPerCu = QW3_MF_PER_CU;  // workgroups per CU
-// LDS: the converted activations, then the partial sums [2][kMfBatch][WAVES][16].
+constexpr int kMfBatch = 8;  // tiles per cross-wave reduction
+constexpr int kMfRing = 4;   // register ring slots (one super-step each)
+constexpr int kMfAhead = 3;  // super-steps loaded ahead of the one decoded
+// LDS: the converted activations (xs4, xe), the partial sums
+// [2][kMfBatch][WAVES][16], then xd [G], 16 wave flags and the fixup's list.
+template <int WAVES>
+constexpr size_t mf_red_words() { return (size_t)2 * kMfBatch * WAVES * 16; }
 template <int GPW, int WAVES>
 constexpr size_t mf_lds() {
-    return (size_t)GPW * WAVES * 64 * 4 + (size_t)GPW * WAVES * 4 + 2 * kMfBatch * WAVES * 16 * sizeof(float);
+    return ((size_t)GPW * WAVES * 66 + mf_red_words<WAVES>() + 16 + kNzCap + 1) * 4;
 }
 typedef unsigned u32x2v_t __attribute__((ext_vector_type(2)));
 struct MfSlot {
@@ -773,7 +996,7 @@ struct MfSlot {
 // super-step q.
 template <int GPW, int WAVES>
 __device__ __forceinline__ int mf_group(int w, int q) {
-    return QW3_MF_ILV ? 4 * WAVES * q + 4 * w : GPW * w + 4 * q;
+    return 4 * WAVES * q + 4 * w;
 }
 
 // GPW groups per wave: 16 (K = 8192, 4 waves) or 32 (K = 28672, 7 waves).  A
@@ -790,6 +1013,9 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_mfma_kernel(const uint16_t *
     static_assert(NS % 4 == 0, "whole A-operand sets");
     extern __shared__ uint32_t smem[];
     float *red = reinterpret_cast<float *>(smem + G * 64 + G);  // [2][kMfBatch][WAVES][16 rows]
+    float *xd = reinterpret_cast<float *>(smem + G * 65 + mf_red_words<WAVES>());
+    uint32_t *flags = smem + G * 66 + mf_red_words<WAVES>();
+    int *nz = reinterpret_cast<int *>(flags + 16);
     int kseg = 0, blk = blockIdx.x, nblk = gridDim.x;
     if constexpr (MULTI) {
         kseg = ((int)blockIdx.x >= sg.blk_end[0]) + ((int)blockIdx.x >= sg.blk_end[1]) +
@@ -834,7 +1060,7 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_mfma_kernel(const uint16_t *
         load(s / NS, s % NS, ring[s % RS]);
         __builtin_amdgcn_sched_barrier(0);
     }
-    xstage_convert<XU>(st, G, smem);
+    publish_flag(xstage_convert<XU>(st, G, smem, xd), flags);
     __syncthreads();
     h8_t xa[AS][16];  // step t = 4 * block + u: pairs 4u .. 4u + 3 of 32-code block `block`
     float fe[AS][4];  // 2^e of the groups whose partials this lane scales (lane row lj of each set)
@@ -937,6 +1163,12 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_mfma_kernel(const uint16_t *
             if constexpr (i >= NS * (UT - 1) && i < AH)
                 asm volatile("" ::"v"(ring[i].a), "v"(ring[i].b), "v"(ring[i].c), "v"(ring[i].s));
         });
+    if (any_flag(flags)) {  // workgroup-uniform, rare
+        __syncthreads();
+        const int nnz = build_nz(0, G, [&](int g) { return xd[g] != 0.f; }, nz);
+        fixup_outputs<1>(x, 0, 1, packed, scales, G, 0, G, BlockRows{blk, nblk, 16, N},
+                         [&](int, int g) { return xd[g]; }, nz, nnz, false, y, 0, threadIdx.x, blockDim.x);
+    }
 }
 
 // ----------------------------------------------- small-M matrix cores -----
@@ -944,10 +1176,12 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_mfma_kernel(const uint16_t *
 // operand order of the 16x16x32 MFMA: for group g, token m and 32-code block
 // j, 16 fp16 pairs in decode pair order (64 bytes).  Tokens m in [M, Mp) are
 // zero.  One thread per (g, m, j); the four blocks of a group form a quad.
+// xe[g][m] = 2 e + (1 if the group's error mass is non-zero), the mass itself
+// in xd[g][m].
 __global__ __launch_bounds__(256) void prep_x_kernel(const uint16_t *__restrict__ x,
                                                      uint4 *__restrict__ xq,
-                                                     int16_t *__restrict__ xe, int M, int Mp,
-                                                     int64_t K, int G) {
+                                                     int16_t *__restrict__ xe, float *__restrict__ xd, int M,
+                                                     int Mp, int64_t K, int G) {
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t units = (int64_t)G * Mp * 4;
     if (idx >= units) return;  // units is a multiple of 4: whole quads exit together
@@ -957,22 +1191,30 @@ __global__ __launch_bounds__(256) void prep_x_kernel(const uint16_t *__restrict_
     const int g = (int)(gm / Mp);
     uint32_t out[16];
     int eg = 0;
+    float d = 0.f;
     if (m < M) {
         uint4 xb[4];
         load_x32(x + (int64_t)m * K + (int64_t)g * kGroup + j * 32, xb);
-        uint32_t mx = absmax32(xb);
+        uint32_t mx, mn;
+        block_stats(xb, mx, mn);
         mx = max(mx, dpp_u32<kDppQuadXor1>(mx));
         mx = max(mx, dpp_u32<kDppQuadXor2>(mx));
         eg = group_exponent(mx);
+        if (mn < exact_floor_bits(eg)) d = small_mass(xb, eg);  // rare
         convert_block(xb, eg, out);
     } else {
 #pragma unroll
         for (int i = 0; i < 16; ++i) out[i] = 0;
     }
+    d += dpp_f32<kDppQuadXor1>(d);
+    d += dpp_f32<kDppQuadXor2>(d);
     uint4 *dst = xq + idx * 4;
 #pragma unroll
     for (int i = 0; i < 4; ++i) dst[i] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
-    if (j == 0) xe[(int64_t)g * Mp + m] = (int16_t)eg;
+    if (j == 0) {
+        xe[(int64_t)g * Mp + m] = (int16_t)(2 * eg + (d != 0.f ? 1 : 0));
+        xd[(int64_t)g * Mp + m] = d;
+    }
 }
 
 // Streaming small-M product on v_mfma_f32_16x16x32_f16.  One wave owns 16
@@ -985,12 +1227,15 @@ __global__ __launch_bounds__(256) void prep_x_kernel(const uint16_t *__restrict_
 template <int MT>
 __global__ __launch_bounds__(256) void qgemm_mfma_kernel(const uint4 *__restrict__ xq,
                                                          const int16_t *__restrict__ xe,
+                                                         const float *__restrict__ xd,
+                                                         const uint16_t *__restrict__ x,
                                                          const uint32_t *__restrict__ packed,
                                                          const uint16_t *__restrict__ scales,
                                                          float *__restrict__ y, int M, int Mp,
                                                          int64_t N, int G, int64_t y_ld) {
     const int lane = threadIdx.x & 63;
-    const int64_t n0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 16;
+    const int64_t wblk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t n0 = wblk * 16;
     if (n0 >= N) return;  // whole wave
     const int nl = lane & 15;
     const int jq = lane >> 4;
@@ -1004,6 +1249,7 @@ __global__ __launch_bounds__(256) void qgemm_mfma_kernel(const uint4 *__restrict
 #pragma unroll
     for (int t = 0; t < MT; ++t) acc[t] = f4_t{0.f, 0.f, 0.f, 0.f};
     const uint32_t magic = magic_vgpr();
+    int small = 0;
 
     for (int g = 0; g < G; ++g) {
         const uint32_t *wp = wrow + (int64_t)g * kWordsPerGroup;
@@ -1032,17 +1278,28 @@ __global__ __launch_bounds__(256) void qgemm_mfma_kernel(const uint4 *__restrict
             for (int t = 0; t < 4; ++t) d = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop[t], bop[t], d, 0, 0, 0);
             const int16_t *ep = xe + (int64_t)g * Mp + mt * 16 + 4 * jq;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[mt][r] += ldexpf(d[r], (int)ep[r]) * s;
+            for (int r = 0; r < 4; ++r) {
+                const int ev = ep[r];
+                small |= ev & 1;
+                acc[mt][r] += ldexpf(d[r], ev >> 1) * s;
+            }
         }
     }
-    if (n >= N) return;
+    const bool fix = __ballot(small != 0) != 0;  // wave-uniform, rare
+    if (n < N) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int m = mt * 16 + 4 * jq + r;
-            if (m < M) y[(int64_t)m * y_ld + n] = acc[mt][r];
-        }
+            for (int r = 0; r < 4; ++r) {
+                const int m = mt * 16 + 4 * jq + r;
+                if (m < M) y[(int64_t)m * y_ld + n] = acc[mt][r];
+            }
+    }
+    if (fix) {
+        __threadfence_block();  // this wave's stores above land before the fixup's
+        fixup_outputs<4>(x, (int64_t)G * kGroup, M, packed, scales, G, 0, G, BlockRows{wblk, (N + 15) / 16, 16, N},
+                         [&](int m, int g) { return xd[(int64_t)g * Mp + m]; }, nullptr, 0, false, y, y_ld, lane, 64);
+    }
 }
 
 // y[m][n] = sum over chunks c, in order, of part[c][m][n].
@@ -1084,10 +1341,11 @@ __global__ __launch_bounds__(256) void qgemm_chunk_sum_kernel(const float *__res
 // (slice, m) are one half-wave.  Stored as xq[((g*4 + t)*4 + b)*Mp + m]
 // (t: the MFMA of the block), xe[slice*Mp + m]: the batched kernels' lane
 // (m, b) = m + 16b reads xq[(g*4 + t)*64 + lane], so each of their operand
-// loads is one contiguous kilobyte.
+// loads is one contiguous kilobyte.  xe holds 2 e + (1 if some group of the
+// slice has a non-zero error mass for token m); the masses go to xd[g][m].
 __global__ __launch_bounds__(256) void prep_x_slice_kernel(const uint16_t *__restrict__ x, uint4 *__restrict__ xq,
-                                                           int16_t *__restrict__ xe, int M, int Mp, int64_t K,
-                                                           int S) {
+                                                           int16_t *__restrict__ xe, float *__restrict__ xd, int M,
+                                                           int Mp, int64_t K, int S) {
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t units = (int64_t)S * Mp * 32;
     if (idx >= units) return;  // units is a multiple of 32: whole half-waves exit together
@@ -1104,16 +1362,22 @@ __global__ __launch_bounds__(256) void prep_x_slice_kernel(const uint16_t *__res
 #pragma unroll
         for (int i = 0; i < 4; ++i) xb[i] = make_uint4(0, 0, 0, 0);
     }
-    uint32_t mx = absmax32(xb);
+    uint32_t mx, mn;
+    block_stats(xb, mx, mn);
 #pragma unroll
     for (int off = 1; off < 32; off <<= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 32));
     const int e = m < M ? group_exponent(mx) : 0;
+    float d = (m < M && mn < exact_floor_bits(e)) ? small_mass(xb, e) : 0.f;  // rare
+    const bool any = (__ballot(d != 0.f) >> (threadIdx.x & 32)) & 0xFFFFFFFFull;  // this half-wave
+    d += dpp_f32<kDppQuadXor1>(d);
+    d += dpp_f32<kDppQuadXor2>(d);
     uint32_t out[16];
     convert_block(xb, e, out);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         xq[(((int64_t)g * 4 + i) * 4 + b) * Mp + m] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
-    if (gi == 0 && b == 0) xe[(int64_t)sl * Mp + m] = (int16_t)e;
+    if (b == 0) xd[(int64_t)g * Mp + m] = d;
+    if (gi == 0 && b == 0) xe[(int64_t)sl * Mp + m] = (int16_t)(2 * e + (any ? 1 : 0));
 }
 
 // 4 x 4 transpose of 3-dword blocks across the lane rows j = l/16:
@@ -1143,12 +1407,16 @@ struct MtStage {
 template <int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void qgemm_mt_kernel(const uint4 *__restrict__ xq,
                                                             const int16_t *__restrict__ xe,
+                                                            const float *__restrict__ xd,
+                                                            const uint16_t *__restrict__ x,
                                                             const uint32_t *__restrict__ packed,
                                                             const uint16_t *__restrict__ scales,
                                                             float *__restrict__ out, int M, int64_t N, int G, int C,
                                                             int64_t out_chunk) {
     constexpr int Mp = 16;
     __shared__ __align__(16) unsigned char red[2][WAVES][64 * 16];
+    __shared__ uint32_t flags[16];
+    __shared__ int nz[kNzCap + 1];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15;
@@ -1189,9 +1457,15 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_mt_kernel(const uint4 *__res
         }
     }
     // One activation exponent per (token, slice): D rows 4j..4j+3 are tokens.
-    int et[4];
+    // The low bit of each entry flags a non-zero error mass.
+    int et[4], small = 0;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) et[r] = xe[(int64_t)(g0 / 8) * Mp + 4 * j + r];
+    for (int r = 0; r < 4; ++r) {
+        const int v = xe[(int64_t)(g0 / 8) * Mp + 4 * j + r];
+        small |= v & 1;
+        et[r] = v >> 1;
+    }
+    publish_flag(small != 0, flags);
     const uint32_t magic = magic_vgpr();
 
     auto tile = [&](int64_t t, const MtStage &st) {
@@ -1251,6 +1525,18 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_mt_kernel(const uint4 *__res
         __builtin_amdgcn_sched_barrier(0);
         tile(t + 1, ring1);
     }
+    if (any_flag(flags)) {  // workgroup-uniform (the loop's barriers published the flags), rare
+        __syncthreads();
+        const int gc0 = chunk * WAVES * 8, gc1 = gc0 + WAVES * 8;
+        auto d_at = [&](int m, int g) { return xd[(int64_t)g * Mp + m]; };
+        const int nnz = build_nz(gc0, gc1, [&](int g) {
+            bool f = false;
+            for (int m = 0; m < M; ++m) f |= d_at(m, g) != 0.f;
+            return f;
+        }, nz);
+        fixup_outputs<8>(x, (int64_t)G * kGroup, M, packed, scales, G, gc0, gc1, BlockRows{tb, TB, 16, N}, d_at, nz,
+                         nnz, false, y, N, threadIdx.x, blockDim.x);
+    }
 }
 
 // ----------------------- batched decode, a ring of 4-group steps (M <= 16) --
@@ -1265,14 +1551,16 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_mt_kernel(const uint4 *__res
 // every kMrBatch tiles one barrier lets the workgroup add its waves' partials
 // in wave order and store them.  Scale rows must be 8-byte aligned (one
 // 8-byte load per lane and super-step).
-#ifndef QW3_MR_BATCH
-#define QW3_MR_BATCH 4
-#endif
-constexpr int kMrBatch = QW3_MR_BATCH;
+constexpr int kMrBatch = 4;  // tiles per cross-wave reduction
 // TS sets of 16 tokens share each decoded block (TS = 2: 17..32 tokens in one
 // pass over the weights); a wave then owns 8 / TS groups.
+// LDS: the partial sums [2][kMrBatch][WAVES][TS][64 lanes] x f4, then the
+// guard's error masses of in-kernel conversion [8 tokens][WAVES * 8 groups],
+// 16 wave flags and the fixup's group list.
 template <int WAVES, int TS>
-constexpr size_t mr_lds() { return (size_t)2 * kMrBatch * WAVES * TS * 64 * 16; }
+constexpr size_t mr_red_bytes() { return (size_t)2 * kMrBatch * WAVES * TS * 64 * 16; }
+template <int WAVES, int TS>
+constexpr size_t mr_lds() { return mr_red_bytes<WAVES, TS>() + ((size_t)8 * WAVES * 8 + 16 + kNzCap + 1) * 4; }
 struct MrSlot {
     u32x4v_t w[3];  // group g0 + 4q + j of row n: 12 words
     u32x2v_t s;     // bf16 scales of groups g0 + 4q .. g0 + 4q + 3 of row n
@@ -1281,6 +1569,7 @@ struct MrSlot {
 template <int WAVES, int TS, bool XH>
 __global__ __launch_bounds__(64 * WAVES) void qgemm_mr_kernel(const uint4 *__restrict__ xq,
                                                             const int16_t *__restrict__ xe,
+                                                            const float *__restrict__ xd,
                                                             const uint16_t *__restrict__ x,
                                                             const uint32_t *__restrict__ packed,
                                                             const uint16_t *__restrict__ scales,
@@ -1290,8 +1579,12 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_mr_kernel(const uint4 *__res
     constexpr int GW = 8 / TS;   // groups per wave
     constexpr int NS = GW / 4;   // 4-group super-steps per tile
     constexpr int UT = 4 / NS;   // tiles per ring cycle (4 slots)
-    extern __shared__ __align__(16) unsigned char lds[];  // [2][kMrBatch][WAVES][TS][64 lanes] x f4
+    extern __shared__ __align__(16) unsigned char lds[];  // mr_lds()
     f4_t *red = reinterpret_cast<f4_t *>(lds);
+    float *xdl = reinterpret_cast<float *>(lds + mr_red_bytes<WAVES, TS>());  // [8][WAVES * 8]
+    uint32_t *flags = reinterpret_cast<uint32_t *>(xdl + 8 * WAVES * 8);
+    int *nz = reinterpret_cast<int *>(flags + 16);
+    int small = 0;  // some error mass of this lane's tokens and groups is non-zero
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15;
@@ -1333,7 +1626,9 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_mr_kernel(const uint4 *__res
                 for (int r = 0; r < 4; ++r) {
                     const int b = 8 * ts + r / 2;
                     const int w0 = j == 0 ? ew[b] : j == 1 ? ew[b + 2] : j == 2 ? ew[b + 4] : ew[b + 6];
-                    et[ts][r] = (r & 1) ? (w0 >> 16) : (int)(int16_t)(w0 & 0xFFFF);
+                    const int v = (r & 1) ? (w0 >> 16) : (int)(int16_t)(w0 & 0xFFFF);
+                    small |= v & 1;  // the low bit flags a non-zero error mass
+                    et[ts][r] = v >> 1;
                 }
         }
         // Activations first (L2-resident), then the ring: the loop's waits for
@@ -1372,13 +1667,27 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_mr_kernel(const uint4 *__res
         // n, n + 8 and the four lane rows).  Each lane converts its 4 groups;
         // a DPP row rotation by 8 brings the other 4 from lane n ^ 8, so
         // every lane holds all 8 groups of token n % 8.
-        uint32_t mx = 0;
+        uint32_t mx = 0, mnk[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) mx = max(mx, absmax32(xh[k]));
+        for (int k = 0; k < 4; ++k) {
+            uint32_t bm;
+            block_stats(xh[k], bm, mnk[k]);
+            mx = max(mx, bm);
+        }
         mx = max(mx, dpp_u32<0x128>(mx));
         mx = max(mx, (uint32_t)__shfl_xor((int)mx, 16));
         mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32));
         const int e = group_exponent(mx);
+        // Error masses of token n % 8, groups g0 + 4(n / 8) + k: the four
+        // lane rows' blocks summed, kept in LDS for the fixup pass.
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            float d = mnk[k] < exact_floor_bits(e) ? small_mass(xh[k], e) : 0.f;  // rare
+            small |= d != 0.f;
+            d += __shfl_xor(d, 16);
+            d += __shfl_xor(d, 32);
+            if (j == 0 && (n & 7) < M) xdl[(n & 7) * (WAVES * 8) + wave * 8 + 4 * (n >> 3) + k] = d;
+        }
         const bool lo = n < 8;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -1482,11 +1791,26 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_mr_kernel(const uint4 *__res
             }
         }
     };
+    publish_flag(small != 0, flags);  // read after the loop's barriers
     int64_t c0 = 0;
     for (; c0 + UT <= my_tiles; c0 += UT) static_for<UT>([&](auto hc) __attribute__((always_inline)) { tile(c0, hc); });
     static_for<UT - 1>([&](auto hc) __attribute__((always_inline)) {
         if (c0 + decltype(hc)::value < my_tiles) tile(c0, hc);
     });
+    if (any_flag(flags)) {  // workgroup-uniform, rare
+        __syncthreads();
+        const int gc0 = chunk * WAVES * GW, gc1 = gc0 + WAVES * GW;
+        auto d_at = [&](int m, int g) {
+            return XH ? xdl[m * (WAVES * 8) + (g - gc0)] : xd[(int64_t)g * Mp + m];
+        };
+        const int nnz = build_nz(gc0, gc1, [&](int g) {
+            bool f = false;
+            for (int m = 0; m < M; ++m) f |= d_at(m, g) != 0.f;
+            return f;
+        }, nz);
+        fixup_outputs<8>(x, (int64_t)G * kGroup, M, packed, scales, G, gc0, gc1, BlockRows{tb, TB, 16, N}, d_at, nz,
+                         nnz, false, y, N, threadIdx.x, blockDim.x);
+    }
 }
 
 // ------------------------------------- batched decode, up to four tokens ----
@@ -1509,8 +1833,11 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_m4_kernel(const uint16_t *__
                                                             float *__restrict__ out, int M, int64_t N, int G, int C,
                                                             int64_t out_chunk) {
     constexpr int GW = 8, NS = 2, UT = 2;
-    extern __shared__ __align__(16) unsigned char lds[];  // [2][kMrBatch][WAVES][64 lanes] floats
+    extern __shared__ __align__(16) unsigned char lds[];  // [2][kMrBatch][WAVES][64 lanes] floats, then the guard's
     float *red = reinterpret_cast<float *>(lds);
+    float *xdl = red + 2 * kMrBatch * WAVES * 64;                            // D [4 tokens][WAVES * GW groups]
+    uint32_t *flags = reinterpret_cast<uint32_t *>(xdl + 4 * WAVES * GW);  // per wave
+    int *nz = reinterpret_cast<int *>(flags + 16);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15;
@@ -1560,14 +1887,30 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_m4_kernel(const uint16_t *__
         // n % 4 = j (a DPP broadcast per dword), the only one whose row takes
         // k chunk j: the other rows are zero.  Lane row j accumulates token
         // j, held by lane 4j.
-        uint32_t mx = 0;
+        uint32_t mx = 0, mnq[NS];
 #pragma unroll
-        for (int q = 0; q < NS; ++q) mx = max(mx, absmax32(xb[q]));
+        for (int q = 0; q < NS; ++q) {
+            uint32_t bm;
+            block_stats(xb[q], bm, mnq[q]);
+            mx = max(mx, bm);
+        }
         mx = max(mx, dpp_u32<kDppQuadXor1>(mx));
         mx = max(mx, dpp_u32<kDppQuadXor2>(mx));
         mx = max(mx, (uint32_t)__shfl_xor((int)mx, 16));
         mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32));
         const int e = group_exponent(mx);
+        // Error masses of token n / 4, groups g0 + 4q + j (the quad's four
+        // blocks summed), kept in LDS for the fixup pass.
+        bool small = false;
+#pragma unroll
+        for (int q = 0; q < NS; ++q) {
+            float d = mnq[q] < exact_floor_bits(e) ? small_mass(xb[q], e) : 0.f;  // rare
+            small |= d != 0.f;
+            d += dpp_f32<kDppQuadXor1>(d);
+            d += dpp_f32<kDppQuadXor2>(d);
+            if ((n & 3) == 0 && (n >> 2) < M) xdl[(n >> 2) * (WAVES * GW) + wave * GW + 4 * q + j] = d;
+        }
+        publish_flag(small, flags);
         const bool on = (n & 3) == j;
 #pragma unroll
         for (int q = 0; q < NS; ++q) {
@@ -1648,9 +1991,23 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_m4_kernel(const uint16_t *__
     int64_t c0 = 0;
     for (; c0 + UT <= my_tiles; c0 += UT) static_for<UT>([&](auto hc) __attribute__((always_inline)) { tile(c0, hc); });
     if (c0 < my_tiles) tile(c0, std::integral_constant<int, 0>{});
+    if (any_flag(flags)) {  // workgroup-uniform (the loop's barriers published the flags), rare
+        __syncthreads();
+        const int gc0 = chunk * WAVES * GW, gc1 = gc0 + WAVES * GW;
+        auto d_at = [&](int m, int g) { return xdl[m * (WAVES * GW) + (g - gc0)]; };
+        const int nnz = build_nz(gc0, gc1, [&](int g) {
+            bool f = false;
+            for (int m = 0; m < M; ++m) f |= d_at(m, g) != 0.f;
+            return f;
+        }, nz);
+        fixup_outputs<4>(x, (int64_t)G * kGroup, M, packed, scales, G, gc0, gc1, BlockRows{tb, TB, 16, N}, d_at, nz,
+                         nnz, false, y, N, threadIdx.x, blockDim.x);
+    }
 }
 template <int WAVES>
-constexpr size_t m4_lds() { return (size_t)2 * kMrBatch * WAVES * 64 * sizeof(float); }
+constexpr size_t m4_lds() {
+    return (size_t)2 * kMrBatch * WAVES * 64 * sizeof(float) + ((size_t)4 * WAVES * 8 + 16 + kNzCap + 1) * 4;
+}
 
 // --------------------------------------------------- prefill (large M) tiles --
 // Many tokens: an MFMA GEMM whose B tiles are decoded on the fly.  Because a
@@ -1668,10 +2025,13 @@ constexpr size_t m4_lds() { return (size_t)2 * kMrBatch * WAVES * 64 * sizeof(fl
 // 16 consecutive rows hit 16 different bank groups.
 
 // Per token: E[m] and x' = x * 2^-(E[m] + p) in block pair order, zero rows
-// for m >= M.  One workgroup per token.
+// for m >= M; the error masses of the guard per group, xd[m][g], and their
+// sum over the token, dtot[m].  One workgroup per token.
 __global__ __launch_bounds__(256) void prep_tile_x_kernel(const uint16_t *__restrict__ x, uint32_t *__restrict__ xq,
-                                                          int *__restrict__ xe, int M, int64_t K) {
+                                                          int *__restrict__ xe, float *__restrict__ xd,
+                                                          float *__restrict__ dtot, int M, int64_t K) {
     __shared__ uint32_t wmax[4];
+    __shared__ float wsum[4];
     const int m = blockIdx.x;
     const int tid = threadIdx.x;
     const int64_t units = K / 32;
@@ -1682,7 +2042,10 @@ __global__ __launch_bounds__(256) void prep_tile_x_kernel(const uint16_t *__rest
 #pragma unroll
             for (int i = 0; i < 4; ++i) d4[i] = make_uint4(0, 0, 0, 0);
         }
-        if (tid == 0) xe[m] = 0;
+        if (tid == 0) {
+            xe[m] = 0;
+            dtot[m] = 0.f;
+        }
         return;
     }
     const uint16_t *src = x + (int64_t)m * K;
@@ -1697,23 +2060,47 @@ __global__ __launch_bounds__(256) void prep_tile_x_kernel(const uint16_t *__rest
     __syncthreads();
     mx = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
     const int e = group_exponent(mx);
-    for (int64_t u = tid; u < units; u += 256) {
+    const uint32_t floor_bits = exact_floor_bits(e);
+    float dsum = 0.f;
+    for (int64_t u = tid; u < units; u += 256) {  // units = 4 G: quads of threads are groups
         uint4 xb[4];
         load_x32(src + u * 32, xb);
+        uint32_t bm, bn;
+        block_stats(xb, bm, bn);
+        float d = bn < floor_bits ? small_mass(xb, e) : 0.f;  // rare
+        dsum += d;
+        d += dpp_f32<kDppQuadXor1>(d);
+        d += dpp_f32<kDppQuadXor2>(d);
+        if ((u & 3) == 0) xd[(int64_t)m * (K / kGroup) + (u >> 2)] = d;
         uint32_t out[16];
         convert_block(xb, e, out);
         uint4 *d4 = reinterpret_cast<uint4 *>(dst + u * 16);
 #pragma unroll
         for (int i = 0; i < 4; ++i) d4[i] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
     }
-    if (tid == 0) xe[m] = e;
+    for (int off = 32; off >= 1; off >>= 1) dsum += __shfl_xor(dsum, off);
+    if ((tid & 63) == 0) wsum[tid >> 6] = dsum;
+    __syncthreads();
+    if (tid == 0) {
+        xe[m] = e;
+        dtot[m] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+    }
+}
+
+// Whether the tile kernels' fast result may be outside the accuracy bound
+// for an output of row set / token set whose largest row exponent is en_max
+// (largest scale below 2^(en_max + 4)) and whose largest token error mass is
+// dmax: 4 s D > budget.
+__device__ __forceinline__ bool tile_coarse_flag(int en_max, float dmax) {
+    return dmax > 0.f && !(4.0f * ldexpf(dmax, en_max + 4) <= kFixBudget);
 }
 
 constexpr int kTileBM = 128;
 constexpr int kTileBN = 128;
 constexpr int kTileRow = 256;  // bytes of one row of one group (128 fp16)
 constexpr size_t kTileStage = (size_t)(kTileBM + kTileBN) * kTileRow;
-constexpr size_t kTileLds = 2 * kTileStage + (size_t)kTileBN * 4;
+// LDS: two stages, the row exponents [kTileBN], 16 wave flags, the fixup's list.
+constexpr size_t kTileLds = 2 * kTileStage + ((size_t)kTileBN + 16 + kNzCap + 1) * 4;
 
 __device__ __forceinline__ int tile_off(int row, int chunk) { return row * kTileRow + ((chunk ^ (row & 15)) << 4); }
 
@@ -1767,12 +2154,14 @@ __device__ __forceinline__ void tile_store(const TileStage &st, unsigned char *s
     }
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void qgemm_tile_kernel(const uint32_t *__restrict__ xq, const int *__restrict__ xe,
-                                                       const uint32_t *__restrict__ packed,
-                                                       const uint16_t *__restrict__ scales, float *__restrict__ y,
-                                                       int M, int MT, int64_t N, int G) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void qgemm_tile_kernel(
+    const uint32_t *__restrict__ xq, const int *__restrict__ xe, const float *__restrict__ xd,
+    const float *__restrict__ dtot, const uint16_t *__restrict__ x, const uint32_t *__restrict__ packed,
+    const uint16_t *__restrict__ scales, float *__restrict__ y, int M, int MT, int64_t N, int G) {
     extern __shared__ __align__(16) unsigned char lds[];
     int *En = reinterpret_cast<int *>(lds + 2 * kTileStage);
+    uint32_t *flags = reinterpret_cast<uint32_t *>(En + kTileBN);
+    int *nz = reinterpret_cast<int *>(flags + 16);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -1787,13 +2176,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int64_t K = (int64_t)G * kGroup;
     const int64_t W = (int64_t)G * kWordsPerGroup;
 
-    // Row exponents: the largest scale of each row maps to [8, 16).
+    // Row exponents: the largest scale of each row maps to [8, 16).  A row
+    // whose smallest non-zero scale lies below 2^(E - 17) does not fold
+    // exactly (fold_inexact): its outputs are recomputed after the loop.
+    bool need = false;
     if (tid < kTileBN) {
         int64_t r = n0 + tid;
         r = r < N ? r : N - 1;
-        uint32_t mx = 0;
-        for (int g = 0; g < G; ++g) mx = max(mx, (uint32_t)scales[r * G + g] & 0x7FFFu);
-        En[tid] = __builtin_amdgcn_frexp_expf(bf16_to_f32(mx)) - 4;
+        uint32_t mx = 0, mn = 0x10000u;
+        for (int g = 0; g < G; ++g) {
+            const uint32_t b = (uint32_t)scales[r * G + g] & 0x7FFFu;
+            mx = max(mx, b);
+            if (b) mn = min(mn, b);
+        }
+        const int E = __builtin_amdgcn_frexp_expf(bf16_to_f32(mx)) - 4;
+        En[tid] = E;
+        need = mx != 0 && bf16_to_f32(mn) < ldexpf(1.0f, E - 17);
     }
     __syncthreads();
 
@@ -1874,20 +2272,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
 #undef QW3_TILE_STEP
 
-    // the exponents of the lane's 16 tokens, loaded together (past M: the last)
+    // the exponents and error masses of the lane's 16 tokens, loaded
+    // together (past M: the last)
     int xt[4][4];
+    float dmax = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int tok = m0 + wm * 64 + 16 * i + 4 * lc + r;
             xt[i][r] = xe[tok < M ? tok : M - 1];
+            dmax = fmaxf(dmax, dtot[tok < M ? tok : M - 1]);
         }
+    int en_max = -1000;
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
         const int nl = wn * 64 + 16 * jj + lr;
         const int64_t row = n0 + nl;
         const int en = En[nl];
+        en_max = max(en_max, en);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -1896,6 +2299,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 if (tok < M && row < N) y[(int64_t)tok * N + row] = ldexpf(acc[i][jj][r], en + xt[i][r]);
             }
         }
+    }
+    // The guard: rows that do not fold exactly, or a token error mass large
+    // enough to matter against this lane's rows -> the fixup pass.
+    need |= tile_coarse_flag(en_max, dmax);
+    publish_flag(need, flags);
+    __syncthreads();  // also orders the stores above before the fixup's
+    if (any_flag(flags)) {
+        const int mt = M - m0 < kTileBM ? M - m0 : kTileBM;
+        auto d_at = [&](int m, int g) { return xd[(int64_t)(m0 + m) * G + g]; };
+        const int nnz = build_nz(0, G, [&](int g) {
+            bool f = false;
+            for (int m = 0; m < mt; ++m) f |= d_at(m, g) != 0.f;
+            return f;
+        }, nz);
+        fixup_outputs<8>(x + (int64_t)m0 * K, K, mt, packed, scales, G, 0, G, BlockRows{n_tile, NT, kTileBN, N}, d_at,
+                         nz, nnz, true, y + (int64_t)m0 * N, N, tid, blockDim.x);
     }
 }
 #undef QW3_TILE_LOAD
@@ -1921,9 +2340,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-#ifndef QW3_PF_MIN_M
-#define QW3_PF_MIN_M 129
-#endif
+constexpr int kPfMinM = 129;  // fewest tokens that take the 256 x 256 tiles
 constexpr int kPfBM = 256, kPfBN = 256;
 constexpr size_t kPfStage = (size_t)kPfBM * kTileRow;  // 64 KB of activations per group
 
@@ -1931,7 +2348,8 @@ typedef unsigned u32x3_t __attribute__((ext_vector_type(3)));
 typedef __attribute__((address_space(3))) void pf_lds_void_t;
 
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void qgemm_pf_kernel(
-    const uint32_t *__restrict__ xq, const int *__restrict__ xe, const uint32_t *__restrict__ packed,
+    const uint32_t *__restrict__ xq, const int *__restrict__ xe, const float *__restrict__ xd,
+    const float *__restrict__ dtot, const uint16_t *__restrict__ x, const uint32_t *__restrict__ packed,
     const uint16_t *__restrict__ scales, float *__restrict__ out, int M, int MT, int64_t N, int G, int C,
     int64_t out_chunk) {
     constexpr int NI = 4;  // 16-row sub-tiles per wave
@@ -1939,6 +2357,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // reads from the other are then provably disjoint, so the compiler neither
     // drains the copy before a read nor needs the reads hidden in asm.
     __shared__ __align__(16) unsigned char stage_a[kPfStage], stage_b[kPfStage];
+    __shared__ uint32_t flags[16];
+    __shared__ int nz[kNzCap + 1];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1963,14 +2383,25 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int64_t r = n0 + wn * 16 * NI + 16 * i + lr;
         rows[i] = r < N ? r : N - 1;
     }
+    // Row exponents over the chunk (largest scale -> [8, 16)); a row whose
+    // smallest non-zero scale lies below 2^(E - 17) does not fold exactly
+    // (fold_inexact) and is recomputed after the loop.
     int en[NI];
+    bool need = false;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-        uint32_t mx = 0;
-        for (int g = gbeg + lc; g < gbeg + Gc; g += 4) mx = max(mx, (uint32_t)scales[rows[i] * G + g] & 0x7FFFu);
+        uint32_t mx = 0, mn = 0x10000u;
+        for (int g = gbeg + lc; g < gbeg + Gc; g += 4) {
+            const uint32_t b = (uint32_t)scales[rows[i] * G + g] & 0x7FFFu;
+            mx = max(mx, b);
+            if (b) mn = min(mn, b);
+        }
         mx = max(mx, (uint32_t)__shfl_xor((int)mx, 16));
         mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32));
+        mn = min(mn, (uint32_t)__shfl_xor((int)mn, 16));
+        mn = min(mn, (uint32_t)__shfl_xor((int)mn, 32));
         en[i] = __builtin_amdgcn_frexp_expf(bf16_to_f32(mx)) - 4;
+        need |= mx != 0 && bf16_to_f32(mn) < ldexpf(1.0f, en[i] - 17);
     }
     // 64 copy instructions per group, 8 per wave: instruction blk fills LDS
     // bytes [1024 blk, +1024) = rows 4 blk + lane/16, physical chunk lane%16.
@@ -2080,16 +2511,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // read the last one): loaded next to each store, every store waited for
     // its own load.
     int xt[8][4];
+    float dmax = 0.f;
 #pragma unroll
     for (int mi = 0; mi < 8; ++mi)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int tok = m0 + wm * 128 + 16 * mi + 4 * lc + r;
             xt[mi][r] = xe[tok < M ? tok : M - 1];
+            dmax = fmaxf(dmax, dtot[tok < M ? tok : M - 1]);
         }
+    int en_max = -1000;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
         const int64_t row = n0 + wn * 16 * NI + 16 * i + lr;
+        en_max = max(en_max, en[i]);
 #pragma unroll
         for (int mi = 0; mi < 8; ++mi) {
 #pragma unroll
@@ -2098,6 +2533,22 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 if (tok < M && row < N) y[(int64_t)tok * N + row] = ldexpf(acc[mi][i][r], en[i] + xt[mi][r]);
             }
         }
+    }
+    // The guard: rows that do not fold exactly, or a token error mass large
+    // enough to matter against this lane's rows -> the fixup pass.
+    need |= tile_coarse_flag(en_max, dmax);
+    publish_flag(need, flags);
+    __syncthreads();  // also orders the stores above before the fixup's
+    if (any_flag(flags)) {
+        const int mt = M - m0 < kPfBM ? M - m0 : kPfBM;
+        auto d_at = [&](int m, int g) { return xd[(int64_t)(m0 + m) * G + g]; };
+        const int nnz = build_nz(gbeg, gbeg + Gc, [&](int g) {
+            bool f = false;
+            for (int m = 0; m < mt; ++m) f |= d_at(m, g) != 0.f;
+            return f;
+        }, nz);
+        fixup_outputs<8>(x + (int64_t)m0 * K, K, mt, packed, scales, G, gbeg, gbeg + Gc, BlockRows{n_tile, NT, kPfBN, N},
+                         d_at, nz, nnz, true, y + (int64_t)m0 * N, N, tid, blockDim.x);
     }
 }
 
@@ -2147,15 +2598,21 @@ qw3_status cu_count(int *out) {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Device workspace of the batched-decode and prefill paths (converted
-// activations, K-chunk partial sums): one buffer per (device, stream), kept
-// until the process ends and grown to the largest request.  Work on one
-// stream runs in order, so the calls on that stream share its buffer; other
-// streams get their own.  A stream-ordered allocation and release per call
-// measured several microseconds per call; this costs nothing after the first
-// call of a size.  Growing synchronizes the stream first (the old buffer may
-// still be read by queued work), so under graph capture make one call of the
-// same size beforehand.
+// Device scratch of the batched-decode and prefill paths: converted
+// activations, the guard's error masses and K-chunk partial sums.
+//
+// One buffer per (device, stream handle).  The first call on a stream
+// allocates it (hipMalloc, whole MiB); a later call that needs more allocates
+// one at least twice as large and keeps the old one allocated until the
+// process ends, because work queued earlier -- or a graph captured earlier --
+// may still use it: nothing is ever freed or synchronized.  A call that would
+// allocate while its stream is being captured returns QW3_ERR_CAPTURE.
+// Calls on one stream run in order and share its buffer; other streams get
+// their own.  Streams are told apart by handle (the HIP runtime the library
+// runs under offers no stream id), so a stream created at the address of a
+// destroyed one inherits its buffer: the header asks callers to let a
+// stream's work finish before destroying it.  (A stream-ordered allocation
+// per call measured 4-8 us per call.)
 struct Workspace {
     int dev;
     hipStream_t stream;
@@ -2164,12 +2621,21 @@ struct Workspace {
 };
 std::mutex g_ws_mutex;
 std::vector<Workspace> g_ws;
+std::vector<void *> g_ws_retired;  // superseded buffers, held until the process ends
+
+bool stream_capturing(hipStream_t stream) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    return cs != hipStreamCaptureStatusNone;
+}
 
 qw3_status workspace(hipStream_t stream, size_t bytes, void **out) {
     int dev = 0;
     hipError_t err = hipGetDevice(&dev);
     if (err != hipSuccess) return hip_fail(err);
-    bytes = (bytes + (size_t(1) << 20) - 1) & ~((size_t(1) << 20) - 1);  // whole MiB: fewer regrowths
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     Workspace *w = nullptr;
     for (auto &e : g_ws)
@@ -2178,25 +2644,38 @@ qw3_status workspace(hipStream_t stream, size_t bytes, void **out) {
         *out = w->ptr;
         return QW3_OK;
     }
+    if (stream_capturing(stream)) return QW3_ERR_CAPTURE;
+    size_t grow = (bytes + (size_t(1) << 20) - 1) & ~((size_t(1) << 20) - 1);
+    if (w && grow < 2 * w->bytes) grow = 2 * w->bytes;
+    void *p = nullptr;
+    err = hipMalloc(&p, grow);
+    if (err != hipSuccess) return hip_fail(err);
     if (w) {
-        err = hipStreamSynchronize(stream);
-        if (err == hipSuccess) err = hipFree(w->ptr);
-        if (err != hipSuccess) return hip_fail(err);
-        w->ptr = nullptr;
-        w->bytes = 0;
+        g_ws_retired.push_back(w->ptr);
+        w->ptr = p;
+        w->bytes = grow;
     } else {
-        g_ws.push_back(Workspace{dev, stream, nullptr, 0});
-        w = &g_ws.back();
+        g_ws.push_back(Workspace{dev, stream, p, grow});
     }
-    err = hipMalloc(&w->ptr, bytes);
-    if (err != hipSuccess) {
-        w->ptr = nullptr;
-        return hip_fail(err);
-    }
-    w->bytes = bytes;
-    *out = w->ptr;
+    *out = p;
     return QW3_OK;
 }
+
+// Where a call takes its scratch from.
+struct ScratchSrc {
+    hipStream_t stream;
+    qw3_status get(size_t bytes, void **out) const { return workspace(stream, bytes, out); }
+};
+
+// Carves consecutive 256-byte-aligned pieces out of one scratch buffer.
+struct Carve {
+    size_t off = 0;
+    size_t take(size_t bytes) {
+        const size_t at = off;
+        off += (bytes + 255) & ~size_t(255);
+        return at;
+    }
+};
 
 qw3_status fill_zero(float *y, int64_t n, hipStream_t stream) {
     if (n == 0) return QW3_OK;
@@ -2213,21 +2692,16 @@ qw3_status blocks_per_cu(const void *kernel, int wgs, size_t lds, int *out) {
     return QW3_OK;
 }
 
-#ifndef QW3_GEMV_BPC
-#define QW3_GEMV_BPC 1
-#endif
 template <int T, bool MULTI>
 qw3_status launch_gemv_small(const uint16_t *x, GemvSegs sg, int count, int G, hipStream_t stream) {
     constexpr int R = kGemvWGS / T;
-    const size_t xs_bytes = (size_t)G * 64 * 4 + (size_t)G * 4;
-    const bool lds_x = xs_bytes <= kMaxLdsX;
-    const size_t lds = lds_x ? xs_bytes : 0;
+    const size_t lds = stage_words(G) * 4;
     const void *kern = reinterpret_cast<const void *>(&qgemv_small_kernel<T, MULTI, kGemvDepth>);
     int cus = 0, per_cu = 0;
     qw3_status st = cu_count(&cus);
     if (st == QW3_OK) st = blocks_per_cu(kern, kGemvWGS, lds, &per_cu);
     if (st != QW3_OK) return st;
-    if (QW3_GEMV_BPC > 0 && per_cu > QW3_GEMV_BPC) per_cu = QW3_GEMV_BPC;
+    if (per_cu > 1) per_cu = 1;  // one workgroup per CU: more bytes in flight measured slower
     const int64_t budget = (int64_t)cus * per_cu;
     int64_t tot = 0;
     for (int i = 0; i < count; ++i) tot += sg.rows[i];
@@ -2250,10 +2724,10 @@ qw3_status launch_gemv_small(const uint16_t *x, GemvSegs sg, int count, int G, h
     const int64_t rows_per_wave = ceil_div(tot, blocks * R);
     if (rows_per_wave <= 2)
         hipLaunchKernelGGL((qgemv_small_kernel<T, MULTI, 1>), dim3((unsigned)blocks), dim3(kGemvWGS), lds, stream, x,
-                           sg, G, lds_x ? 1 : 0);
+                           sg, G);
     else
         hipLaunchKernelGGL((qgemv_small_kernel<T, MULTI, kGemvDepth>), dim3((unsigned)blocks), dim3(kGemvWGS), lds,
-                           stream, x, sg, G, lds_x ? 1 : 0);
+                           stream, x, sg, G);
     return check_launch();
 }
 
@@ -2285,11 +2759,9 @@ qw3_status launch_gemv_big(const uint16_t *x, const uint32_t *packed, const uint
             wgs = T;
         }
     }
-    const size_t xs_bytes = (size_t)G * 64 * 4 + (size_t)G * 4;
-    const bool lds_x = xs_bytes <= kMaxLdsX;
+    const bool lds_x = (size_t)G * 65 * 4 <= kMaxLdsX;
     constexpr int kBigD = kGemvDepth, kHugeD = 1;
-    const size_t red_bytes = 2 * (size_t)((wgs <= 512 ? kBigD : kHugeD) + 1) * (wgs / 32) * sizeof(float);
-    const size_t lds = (lds_x && xs_bytes > red_bytes) ? xs_bytes : red_bytes;
+    const size_t lds = big_words(G, lds_x) * 4;
     const void *kern =
         wgs <= 512 ? (lds_x ? reinterpret_cast<const void *>(&qgemv_big_kernel<512, kBigD, true>)
                             : reinterpret_cast<const void *>(&qgemv_big_kernel<512, kBigD, false>))
@@ -2310,9 +2782,6 @@ qw3_status launch_gemv_big(const uint16_t *x, const uint32_t *packed, const uint
 // The matrix-core GEMV: one workgroup per CU, workgroups dealt to the
 // matrices in proportion to their 16-row tiles, at least one and at most one
 // per tile each (4 waves x 16 groups at K = 8192).
-#ifndef QW3_GEMV_MFMA
-#define QW3_GEMV_MFMA 1
-#endif
 template <int GPW, int WAVES, bool MULTI>
 qw3_status launch_gemv_mfma(const uint16_t *x, GemvSegs sg, int count, hipStream_t stream) {
     int cus = 0;
@@ -2327,7 +2796,7 @@ qw3_status launch_gemv_mfma(const uint16_t *x, GemvSegs sg, int count, hipStream
     for (int i = 0; i < kMaxSegs; ++i) {
         int64_t b = 0;
         if (tiles[i] > 0) {
-            b = (int64_t)kMfPerCu * cus * tiles[i] / tot;
+            b = (int64_t)cus * tiles[i] / tot;
             b = b < 1 ? 1 : (b > tiles[i] ? tiles[i] : b);
         }
         blocks += b;
@@ -2347,7 +2816,7 @@ qw3_status launch_gemv_mfma(const uint16_t *x, GemvSegs sg, int count, hipStream
 // choice depends on the matrix alone, so a matrix gets the same kernel -- and
 // the same bits -- from qgemv_w3g128 and from qgemv_w3g128_multi.
 bool gemv_mfma_takes(int G, const uint16_t *scales, int64_t N) {
-    if (!QW3_GEMV_MFMA || G != 64 || N == 0 || !aligned(scales, 8)) return false;
+    if (G != 64 || N == 0 || !aligned(scales, 8)) return false;
     int cus = 0;
     if (cu_count(&cus) != QW3_OK) return false;
     return ceil_div(N, 16) >= 4 * (int64_t)cus;
@@ -2409,27 +2878,45 @@ qw3_status launch_gemv_multi(const uint16_t *x, int count, const uint32_t *const
     return QW3_OK;
 }
 
-// Prefill: convert x once (per-token exponent), then one tile GEMM launch.
+// Scratch of the per-token conversion of Mp tokens: x' [Mp][K] fp16, the
+// exponents [Mp], the token error masses [Mp] and the group masses [Mp][G].
+struct TileX {
+    uint32_t *xq;
+    int *xe;
+    float *dtot, *xd;
+};
+size_t tile_x_layout(int64_t Mp, int64_t K, Carve &cv, size_t (&at)[4]) {
+    at[0] = cv.take((size_t)Mp * (size_t)K * 2);
+    at[1] = cv.take((size_t)Mp * sizeof(int));
+    at[2] = cv.take((size_t)Mp * sizeof(float));
+    at[3] = cv.take((size_t)Mp * (size_t)(K / kGroup) * sizeof(float));
+    return cv.off;
+}
+TileX tile_x_at(void *base, const size_t (&at)[4]) {
+    char *b = static_cast<char *>(base);
+    return TileX{reinterpret_cast<uint32_t *>(b + at[0]), reinterpret_cast<int *>(b + at[1]),
+                 reinterpret_cast<float *>(b + at[2]), reinterpret_cast<float *>(b + at[3])};
+}
+
+// 33..128 tokens: convert x once (per-token exponent), then one tile GEMM launch.
 qw3_status launch_gemm_tile(const uint16_t *x, const uint32_t *packed, const uint16_t *scales, float *y,
-                            int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+                            int64_t M, int64_t N, int64_t K, const ScratchSrc &src) {
     const int G = (int)(K / kGroup);
     const int MT = (int)ceil_div(M, kTileBM);
     const int64_t Mp = (int64_t)MT * kTileBM;
-    const size_t xq_bytes = (size_t)Mp * (size_t)K * 2;
-    const size_t xe_bytes = (size_t)Mp * sizeof(int);
-    void *scratch = nullptr;
-    {
-        const qw3_status ws = workspace(stream, xq_bytes + xe_bytes, &scratch);
-        if (ws != QW3_OK) return ws;
-    }
-    uint32_t *xq = reinterpret_cast<uint32_t *>(scratch);
-    int *xe = reinterpret_cast<int *>(static_cast<char *>(scratch) + xq_bytes);
-    hipLaunchKernelGGL(prep_tile_x_kernel, dim3((unsigned)Mp), dim3(256), 0, stream, x, xq, xe, (int)M, K);
-    qw3_status st = check_launch();
+    Carve cv;
+    size_t at[4];
+    void *base = nullptr;
+    qw3_status st = src.get(tile_x_layout(Mp, K, cv, at), &base);
+    if (st != QW3_OK) return st;
+    const TileX tx = tile_x_at(base, at);
+    hipLaunchKernelGGL(prep_tile_x_kernel, dim3((unsigned)Mp), dim3(256), 0, src.stream, x, tx.xq, tx.xe, tx.xd,
+                       tx.dtot, (int)M, K);
+    st = check_launch();
     if (st == QW3_OK) {
         const int64_t blocks = ceil_div(N, kTileBN) * MT;
-        hipLaunchKernelGGL(qgemm_tile_kernel, dim3((unsigned)blocks), dim3(256), kTileLds, stream, xq, xe, packed,
-                           scales, y, (int)M, MT, N, G);
+        hipLaunchKernelGGL(qgemm_tile_kernel, dim3((unsigned)blocks), dim3(256), kTileLds, src.stream, tx.xq, tx.xe,
+                           tx.xd, tx.dtot, x, packed, scales, y, (int)M, MT, N, G);
         st = check_launch();
     }
     return st;
@@ -2439,7 +2926,7 @@ qw3_status launch_gemm_tile(const uint16_t *x, const uint32_t *packed, const uin
 // launch (K split into C chunks when the tiles alone would not fill the
 // GPU), and a chunk sum.
 qw3_status launch_gemm_pf(const uint16_t *x, const uint32_t *packed, const uint16_t *scales, float *y, int64_t M,
-                          int64_t N, int64_t K, hipStream_t stream) {
+                          int64_t N, int64_t K, const ScratchSrc &src) {
     const int G = (int)(K / kGroup);
     const int MT = (int)ceil_div(M, kPfBM);
     const int64_t NT = ceil_div(N, kPfBN);
@@ -2449,29 +2936,28 @@ qw3_status launch_gemm_pf(const uint16_t *x, const uint32_t *packed, const uint1
     int C = 1;
     while (NT * MT * C * 2 <= cus && G % (2 * C) == 0) C *= 2;
     const int64_t Mp = (int64_t)MT * kPfBM;
-    const size_t xq_bytes = (size_t)Mp * (size_t)K * 2;
-    const size_t xe_bytes = ((size_t)Mp * sizeof(int) + 255) / 256 * 256;
-    const size_t part_bytes = C > 1 ? (size_t)C * (size_t)M * (size_t)N * sizeof(float) : 0;
-    void *scratch = nullptr;
-    {
-        const qw3_status ws = workspace(stream, xq_bytes + xe_bytes + part_bytes, &scratch);
-        if (ws != QW3_OK) return ws;
-    }
-    uint32_t *xq = reinterpret_cast<uint32_t *>(scratch);
-    int *xe = reinterpret_cast<int *>(static_cast<char *>(scratch) + xq_bytes);
-    float *part = reinterpret_cast<float *>(static_cast<char *>(scratch) + xq_bytes + xe_bytes);
-    hipLaunchKernelGGL(prep_tile_x_kernel, dim3((unsigned)Mp), dim3(256), 0, stream, x, xq, xe, (int)M, K);
+    Carve cv;
+    size_t at[4];
+    tile_x_layout(Mp, K, cv, at);
+    const size_t part_at = cv.take(C > 1 ? (size_t)C * (size_t)M * (size_t)N * sizeof(float) : 0);
+    void *base = nullptr;
+    st = src.get(cv.off, &base);
+    if (st != QW3_OK) return st;
+    const TileX tx = tile_x_at(base, at);
+    float *part = reinterpret_cast<float *>(static_cast<char *>(base) + part_at);
+    hipLaunchKernelGGL(prep_tile_x_kernel, dim3((unsigned)Mp), dim3(256), 0, src.stream, x, tx.xq, tx.xe, tx.xd,
+                       tx.dtot, (int)M, K);
     st = check_launch();
     if (st == QW3_OK) {
         float *dst = C > 1 ? part : y;
-        hipLaunchKernelGGL(qgemm_pf_kernel, dim3((unsigned)(NT * MT * C)), dim3(512), 0, stream, xq, xe, packed,
-                           scales, dst, (int)M, MT, N, G, C, (int64_t)M * N);
+        hipLaunchKernelGGL(qgemm_pf_kernel, dim3((unsigned)(NT * MT * C)), dim3(512), 0, src.stream, tx.xq, tx.xe,
+                           tx.xd, tx.dtot, x, packed, scales, dst, (int)M, MT, N, G, C, (int64_t)M * N);
         st = check_launch();
     }
     if (st == QW3_OK && C > 1) {
         const int64_t count = M * N;
-        hipLaunchKernelGGL(qgemm_chunk_sum_kernel, dim3((unsigned)ceil_div(count, 256)), dim3(256), 0, stream, part, y,
-                           count, C, count);
+        hipLaunchKernelGGL(qgemm_chunk_sum_kernel, dim3((unsigned)ceil_div(count, 256)), dim3(256), 0, src.stream,
+                           part, y, count, C, count);
         st = check_launch();
     }
     return st;
@@ -2479,12 +2965,6 @@ qw3_status launch_gemm_pf(const uint16_t *x, const uint32_t *packed, const uint1
 
 // Batched decode from registers (tokens <= 16 per pass), K in chunks of
 // WAVES x 8 groups.
-#ifndef QW3_MT_RING
-#define QW3_MT_RING 1
-#endif
-#ifndef QW3_MR_XH
-#define QW3_MR_XH 1
-#endif
 // TS = 1: passes of up to 16 tokens, through the ring kernel when the scale
 // rows are 8-byte aligned (it reads 8 bytes of scales at a time), else
 // through qgemm_mt_kernel (2 bytes at a time).  TS = 2: 17..32 tokens in one
@@ -2492,17 +2972,19 @@ qw3_status launch_gemm_pf(const uint16_t *x, const uint32_t *packed, const uint1
 // wave), scale rows 8-byte aligned.
 template <int WAVES, int TS>
 qw3_status launch_gemm_mt(const uint16_t *x, const uint32_t *packed, const uint16_t *scales, float *y, int64_t M,
-                          int64_t N, int64_t K, hipStream_t stream) {
+                          int64_t N, int64_t K, const ScratchSrc &src) {
     const int G = (int)(K / kGroup);
-    const bool ring = TS == 2 || (QW3_MT_RING && aligned(scales, 8));
+    const bool ring = TS == 2 || aligned(scales, 8);
     constexpr int Mp = 16 * TS;
     const int C = G / ((8 / TS) * WAVES);
     // Up to 6 tokens: the ring kernel converts the activations itself (at 8
     // it measured the same as the conversion launch).
-    const bool xh = QW3_MR_XH && ring && TS == 1 && M <= 6;
-    const size_t xq_bytes = xh ? 0 : (size_t)Mp * (size_t)K * 2;
-    const size_t xe_bytes = xh ? 0 : ((size_t)(G / 8) * Mp * sizeof(int16_t) + 255) / 256 * 256;
-    const size_t part_bytes = C > 1 ? (size_t)C * Mp * (size_t)N * sizeof(float) : 0;
+    const bool xh = ring && TS == 1 && M <= 6;
+    Carve cv;
+    const size_t xq_at = cv.take(xh ? 0 : (size_t)Mp * (size_t)K * 2);
+    const size_t xe_at = cv.take(xh ? 0 : (size_t)(G / 8) * Mp * sizeof(int16_t));
+    const size_t xd_at = cv.take(xh ? 0 : (size_t)G * Mp * sizeof(float));
+    const size_t part_at = cv.take(C > 1 ? (size_t)C * Mp * (size_t)N * sizeof(float) : 0);
     const void *kern = xh     ? reinterpret_cast<const void *>(&qgemm_mr_kernel<WAVES, TS, TS == 1>)
                        : ring ? reinterpret_cast<const void *>(&qgemm_mr_kernel<WAVES, TS, false>)
                               : reinterpret_cast<const void *>(&qgemm_mt_kernel<WAVES>);
@@ -2511,37 +2993,40 @@ qw3_status launch_gemm_mt(const uint16_t *x, const uint32_t *packed, const uint1
     qw3_status st = cu_count(&cus);
     if (st == QW3_OK) st = blocks_per_cu(kern, 64 * WAVES, lds, &per_cu);
     if (st != QW3_OK) return st;
-    void *scratch = nullptr;
-    if (xq_bytes + xe_bytes + part_bytes > 0) {
-        const qw3_status ws = workspace(stream, xq_bytes + xe_bytes + part_bytes, &scratch);
-        if (ws != QW3_OK) return ws;
+    void *base = nullptr;
+    if (cv.off > 0) {
+        st = src.get(cv.off, &base);
+        if (st != QW3_OK) return st;
     }
-    uint4 *xq = reinterpret_cast<uint4 *>(scratch);
-    int16_t *xe = reinterpret_cast<int16_t *>(static_cast<char *>(scratch) + xq_bytes);
-    float *part = reinterpret_cast<float *>(static_cast<char *>(scratch) + xq_bytes + xe_bytes);
+    char *b = static_cast<char *>(base);
+    uint4 *xq = reinterpret_cast<uint4 *>(b + xq_at);
+    int16_t *xe = reinterpret_cast<int16_t *>(b + xe_at);
+    float *xd = reinterpret_cast<float *>(b + xd_at);
+    float *part = reinterpret_cast<float *>(b + part_at);
     const int64_t tiles = ceil_div(N, 16);
     int64_t tb = (int64_t)cus * per_cu / C;
     if (tb < 1) tb = 1;
     if (tb > tiles) tb = tiles;
+    const hipStream_t stream = src.stream;
     for (int64_t m0 = 0; m0 < M && st == QW3_OK; m0 += Mp) {
         const int mc = (int)(M - m0 < Mp ? M - m0 : Mp);
         if (!xh) {
             const int64_t units = (int64_t)(G / 8) * Mp * 32;
             hipLaunchKernelGGL(prep_x_slice_kernel, dim3((unsigned)ceil_div(units, 256)), dim3(256), 0, stream,
-                               x + m0 * K, xq, xe, mc, Mp, K, G / 8);
+                               x + m0 * K, xq, xe, xd, mc, Mp, K, G / 8);
             st = check_launch();
             if (st != QW3_OK) break;
         }
         float *dst = C > 1 ? part : y + m0 * N;
         if (xh)
             hipLaunchKernelGGL((qgemm_mr_kernel<WAVES, TS, TS == 1>), dim3((unsigned)(tb * C)), dim3(64 * WAVES), lds,
-                               stream, xq, xe, x + m0 * K, packed, scales, dst, mc, N, G, C, (int64_t)Mp * N);
+                               stream, xq, xe, xd, x + m0 * K, packed, scales, dst, mc, N, G, C, (int64_t)Mp * N);
         else if (ring)
             hipLaunchKernelGGL((qgemm_mr_kernel<WAVES, TS, false>), dim3((unsigned)(tb * C)), dim3(64 * WAVES), lds,
-                               stream, xq, xe, x + m0 * K, packed, scales, dst, mc, N, G, C, (int64_t)Mp * N);
+                               stream, xq, xe, xd, x + m0 * K, packed, scales, dst, mc, N, G, C, (int64_t)Mp * N);
         else
             hipLaunchKernelGGL(qgemm_mt_kernel<WAVES>, dim3((unsigned)(tb * C)), dim3(64 * WAVES), 0, stream, xq, xe,
-                               packed, scales, dst, mc, N, G, C, (int64_t)Mp * N);
+                               xd, x + m0 * K, packed, scales, dst, mc, N, G, C, (int64_t)Mp * N);
         st = check_launch();
         if (st != QW3_OK || C == 1) continue;
         const int64_t count = (int64_t)mc * N;
@@ -2554,12 +3039,9 @@ qw3_status launch_gemm_mt(const uint16_t *x, const uint32_t *packed, const uint1
 
 // Up to four tokens: qgemm_m4_kernel, WAVES x 8 groups per K chunk (scale
 // rows 8-byte aligned).
-#ifndef QW3_GEMM_M4
-#define QW3_GEMM_M4 1
-#endif
 template <int WAVES>
 qw3_status launch_gemm_m4(const uint16_t *x, const uint32_t *packed, const uint16_t *scales, float *y, int64_t M,
-                          int64_t N, int64_t K, hipStream_t stream) {
+                          int64_t N, int64_t K, const ScratchSrc &src) {
     constexpr int Mp = 4;  // token slots of the partial sums
     const int G = (int)(K / kGroup);
     const int C = G / (8 * WAVES);
@@ -2572,21 +3054,21 @@ qw3_status launch_gemm_m4(const uint16_t *x, const uint32_t *packed, const uint1
     if (st != QW3_OK) return st;
     float *part = nullptr;
     if (part_bytes > 0) {
-        void *scratch = nullptr;
-        st = workspace(stream, part_bytes, &scratch);
+        void *base = nullptr;
+        st = src.get(part_bytes, &base);
         if (st != QW3_OK) return st;
-        part = static_cast<float *>(scratch);
+        part = static_cast<float *>(base);
     }
     const int64_t tiles = ceil_div(N, 16);
     int64_t tb = (int64_t)cus * per_cu / C;
     if (tb < 1) tb = 1;
     if (tb > tiles) tb = tiles;
-    hipLaunchKernelGGL(qgemm_m4_kernel<WAVES>, dim3((unsigned)(tb * C)), dim3(64 * WAVES), lds, stream, x, packed,
+    hipLaunchKernelGGL(qgemm_m4_kernel<WAVES>, dim3((unsigned)(tb * C)), dim3(64 * WAVES), lds, src.stream, x, packed,
                        scales, C > 1 ? part : y, (int)M, N, G, C, (int64_t)Mp * N);
     st = check_launch();
     if (st != QW3_OK || C == 1) return st;
     const int64_t count = M * N;
-    hipLaunchKernelGGL(qgemm_chunk_sum_kernel, dim3((unsigned)ceil_div(count, 256)), dim3(256), 0, stream, part, y,
+    hipLaunchKernelGGL(qgemm_chunk_sum_kernel, dim3((unsigned)ceil_div(count, 256)), dim3(256), 0, src.stream, part, y,
                        count, C, (int64_t)Mp * N);
     return check_launch();
 }
@@ -2594,51 +3076,76 @@ qw3_status launch_gemm_m4(const uint16_t *x, const uint32_t *packed, const uint1
 // Small-M path: convert x once into scratch, then one streaming pass over W
 // per chunk of up to 32 tokens.
 qw3_status launch_gemm_small(const uint16_t *x, const uint32_t *packed, const uint16_t *scales, float *y,
-                             int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+                             int64_t M, int64_t N, int64_t K, const ScratchSrc &src) {
     const int G = (int)(K / kGroup);
     if (M > 32) {
-        if (M >= QW3_PF_MIN_M) return launch_gemm_pf(x, packed, scales, y, M, N, K, stream);
-        return launch_gemm_tile(x, packed, scales, y, M, N, K, stream);
+        if (M >= kPfMinM) return launch_gemm_pf(x, packed, scales, y, M, N, K, src);
+        return launch_gemm_tile(x, packed, scales, y, M, N, K, src);
     }
     // Batched decode: 17..32 tokens in one pass when the scale rows allow the
     // ring kernel (chunks of 8 waves x 4 groups); otherwise passes of up to
     // 16 tokens in chunks of 8 waves x 8 groups (or 7 x 8 when K = 28672).
-    if (M <= 4 && QW3_GEMM_M4 && aligned(scales, 8)) {
-        if (G % 64 == 0) return launch_gemm_m4<8>(x, packed, scales, y, M, N, K, stream);
-        if (G % 56 == 0) return launch_gemm_m4<7>(x, packed, scales, y, M, N, K, stream);
+    if (M <= 4 && aligned(scales, 8)) {
+        if (G % 64 == 0) return launch_gemm_m4<8>(x, packed, scales, y, M, N, K, src);
+        if (G % 56 == 0) return launch_gemm_m4<7>(x, packed, scales, y, M, N, K, src);
     }
-    if (M > 16 && QW3_MT_RING && aligned(scales, 8) && G % 32 == 0)
-        return launch_gemm_mt<8, 2>(x, packed, scales, y, M, N, K, stream);
-    if (G % 64 == 0) return launch_gemm_mt<8, 1>(x, packed, scales, y, M, N, K, stream);
-    if (G % 56 == 0) return launch_gemm_mt<7, 1>(x, packed, scales, y, M, N, K, stream);
+    if (M > 16 && aligned(scales, 8) && G % 32 == 0) return launch_gemm_mt<8, 2>(x, packed, scales, y, M, N, K, src);
+    if (G % 64 == 0) return launch_gemm_mt<8, 1>(x, packed, scales, y, M, N, K, src);
+    if (G % 56 == 0) return launch_gemm_mt<7, 1>(x, packed, scales, y, M, N, K, src);
     const int mchunk = M > 16 ? 32 : 16;
-    const size_t xq_bytes = (size_t)mchunk * (size_t)K * 2;
-    const size_t xe_bytes = (size_t)G * mchunk * sizeof(int16_t);
-    void *scratch = nullptr;
-    {
-        const qw3_status ws = workspace(stream, xq_bytes + xe_bytes, &scratch);
-        if (ws != QW3_OK) return ws;
-    }
-    uint4 *xq = reinterpret_cast<uint4 *>(scratch);
-    int16_t *xe = reinterpret_cast<int16_t *>(static_cast<char *>(scratch) + xq_bytes);
-    qw3_status st = QW3_OK;
+    Carve cv;
+    const size_t xq_at = cv.take((size_t)mchunk * (size_t)K * 2);
+    const size_t xe_at = cv.take((size_t)G * mchunk * sizeof(int16_t));
+    const size_t xd_at = cv.take((size_t)G * mchunk * sizeof(float));
+    void *base = nullptr;
+    qw3_status st = src.get(cv.off, &base);
+    if (st != QW3_OK) return st;
+    char *b = static_cast<char *>(base);
+    uint4 *xq = reinterpret_cast<uint4 *>(b + xq_at);
+    int16_t *xe = reinterpret_cast<int16_t *>(b + xe_at);
+    float *xd = reinterpret_cast<float *>(b + xd_at);
     for (int64_t m0 = 0; m0 < M && st == QW3_OK; m0 += mchunk) {
         const int mc = (int)(M - m0 < mchunk ? M - m0 : mchunk);
         const int64_t units = (int64_t)G * mchunk * 4;
-        hipLaunchKernelGGL(prep_x_kernel, dim3((unsigned)ceil_div(units, 256)), dim3(256), 0, stream,
-                           x + m0 * K, xq, xe, mc, mchunk, K, G);
+        hipLaunchKernelGGL(prep_x_kernel, dim3((unsigned)ceil_div(units, 256)), dim3(256), 0, src.stream,
+                           x + m0 * K, xq, xe, xd, mc, mchunk, K, G);
         st = check_launch();
         if (st != QW3_OK) break;
         const unsigned blocks = (unsigned)ceil_div(N, 64);
         if (mchunk == 16)
-            hipLaunchKernelGGL(qgemm_mfma_kernel<1>, dim3(blocks), dim3(256), 0, stream, xq, xe, packed, scales,
-                               y + m0 * N, mc, mchunk, N, G, N);
+            hipLaunchKernelGGL(qgemm_mfma_kernel<1>, dim3(blocks), dim3(256), 0, src.stream, xq, xe, xd, x + m0 * K,
+                               packed, scales, y + m0 * N, mc, mchunk, N, G, N);
         else
-            hipLaunchKernelGGL(qgemm_mfma_kernel<2>, dim3(blocks), dim3(256), 0, stream, xq, xe, packed, scales,
-                               y + m0 * N, mc, mchunk, N, G, N);
+            hipLaunchKernelGGL(qgemm_mfma_kernel<2>, dim3(blocks), dim3(256), 0, src.stream, xq, xe, xd, x + m0 * K,
+                               packed, scales, y + m0 * N, mc, mchunk, N, G, N);
         st = check_launch();
     }
     return st;
+}
+
+// Validation shared by the two batched entry points.
+qw3_status check_gemm_args(const uint16_t *x, const int32_t *packed, const uint16_t *scales, const float *y,
+                           int64_t M, int64_t N, int64_t K) {
+    qw3_status st = check_shape(N, K);
+    if (st != QW3_OK) return st;
+    if (M < 0 || M > (int64_t(1) << 24)) return QW3_ERR_SHAPE;
+    if (N == 0 || M == 0) return QW3_OK;
+    if (!y) return QW3_ERR_NULL;
+    if (!aligned(y, 4)) return QW3_ERR_ALIGN;
+    if (K == 0) return QW3_OK;
+    if (!x || !packed || !scales) return QW3_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scales, 2)) return QW3_ERR_ALIGN;
+    return QW3_OK;
+}
+
+qw3_status run_gemm(const uint16_t *x, const int32_t *packed, const uint16_t *scales, float *y, int64_t M, int64_t N,
+                    int64_t K, const ScratchSrc &src) {
+    const qw3_status st = check_gemm_args(x, packed, scales, y, M, N, K);
+    if (st != QW3_OK || N == 0 || M == 0) return st;
+    if (K == 0) return fill_zero(y, M * N, src.stream);
+    const uint32_t *pw = reinterpret_cast<const uint32_t *>(packed);
+    if (M == 1) return launch_gemv(x, pw, scales, y, N, K, src.stream);
+    return launch_gemm_small(x, pw, scales, y, M, N, K, src);
 }
 
 }  // namespace
@@ -2736,18 +3243,7 @@ qw3_status qgemv_w3g128_multi(const uint16_t *x, int32_t count, const int32_t *c
 
 qw3_status qgemm_w3g128_smallM(const uint16_t *x, const int32_t *packed, const uint16_t *scales, float *y,
                                int64_t M, int64_t N, int64_t K, void *hip_stream) {
-    qw3_status st = check_shape(N, K);
-    if (st != QW3_OK) return st;
-    if (M < 0 || M > (int64_t(1) << 24)) return QW3_ERR_SHAPE;
-    if (N == 0 || M == 0) return QW3_OK;
-    if (!y) return QW3_ERR_NULL;
-    if (!aligned(y, 4)) return QW3_ERR_ALIGN;
-    if (K == 0) return fill_zero(y, M * N, (hipStream_t)hip_stream);
-    if (!x || !packed || !scales) return QW3_ERR_NULL;
-    if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scales, 2)) return QW3_ERR_ALIGN;
-    const uint32_t *pw = reinterpret_cast<const uint32_t *>(packed);
-    if (M == 1) return launch_gemv(x, pw, scales, y, N, K, (hipStream_t)hip_stream);
-    return launch_gemm_small(x, pw, scales, y, M, N, K, (hipStream_t)hip_stream);
+    return run_gemm(x, packed, scales, y, M, N, K, ScratchSrc{(hipStream_t)hip_stream});
 }
 
 const char *qstatus_str(qw3_status status) {
@@ -2757,6 +3253,7 @@ const char *qstatus_str(qw3_status status) {
         case QW3_ERR_SHAPE: return "invalid shape (negative size, K % 128 != 0, or K > QW3_MAX_K)";
         case QW3_ERR_ALIGN: return "misaligned pointer (x/packed/codes/w_out need 16 bytes)";
         case QW3_ERR_HIP: return "HIP runtime error (see qw3_last_hip_error)";
+        case QW3_ERR_CAPTURE: return "the stream's workspace would have to grow during graph capture";
         default: return "unknown status";
     }
 }

@@ -36,6 +36,17 @@
  *   - Each call is deterministic: the same inputs give bit-identical outputs
  *     on every run (all reductions run in a fixed order, no atomics).
  *   - Inputs must be finite; NaN or Inf in x or scales give unspecified y.
+ *     The products also assume every |s| * |x| below 2^100 and every
+ *     sum_k |x_k w_k| below 2^120 (far inside fp32), so that no partial sum
+ *     overflows; outside that y is unspecified.
+ *   - Accuracy of the products, for every input in that domain whatever the
+ *     spread of magnitudes within x or within a row's scales:
+ *       |y - sum_k x_k w_k| <= 1e-4 * sum_k |x_k w_k| + 1e-6   per output.
+ *     The fast paths multiply fp16 operands; the elements that their
+ *     conversion may round (activations about 2^21 below the largest of their
+ *     exponent set, scales more than 2^21 below the largest of their row on
+ *     the many-token tiles) are tracked, and every output whose error bound
+ *     could exceed 2^-21 is recomputed in fp32 by the same call.
  */
 #ifndef QW3_H
 #define QW3_H
@@ -53,7 +64,9 @@ enum {
     QW3_ERR_NULL = -1,  /* a required pointer is NULL                        */
     QW3_ERR_SHAPE = -2, /* negative size, K % 128 != 0, or K > QW3_MAX_K      */
     QW3_ERR_ALIGN = -3, /* a pointer is not aligned as stated above           */
-    QW3_ERR_HIP = -4    /* the HIP runtime reported an error                  */
+    QW3_ERR_HIP = -4,   /* the HIP runtime reported an error                  */
+    QW3_ERR_CAPTURE = -5 /* qgemm_w3g128_smallM would have to allocate its
+                            workspace while the stream is being captured       */
 };
 
 /* Largest supported in_features (1024 groups of 128). */
@@ -64,8 +77,9 @@ enum {
  *   codes  [N, K] uint8, values 0..7 (only the low 3 bits of each byte are
  *          used; larger values are a caller error)
  *   packed [N, 3K/32] int32, written
- * Storage layout of the GSQ model card ("exact-width packing -- no sub-byte
- * values are padded", [28672, 8192] -> [28672, 768]).
+ * Storage layout of the GSQ model card: the codes are packed at their exact
+ * 3-bit width with no padding bits, so a [28672, 8192] weight becomes
+ * [28672, 768] words.
  */
 qw3_status qpack_uint3(const uint8_t *codes, int32_t *packed, int64_t N, int64_t K,
                        void *hip_stream);
@@ -74,8 +88,8 @@ qw3_status qpack_uint3(const uint8_t *codes, int32_t *packed, int64_t N, int64_t
  * qrepack_w4c_uint3 -- repack the 4-bit-container intermediate into the
  * exact-width stream.
  *   w4     [N, K/8] int32: the codes as GSQ training writes them before the
- *          checkpoint is re-packed (GSQ model card, "Storage layout": the 3-bit
- *          codebook padded into a 4-bit INT32 container).  Reading taken: code
+ *          checkpoint is re-packed (GSQ model card, "Storage layout": training
+ *          first keeps each 3-bit code in a 4-bit slot of int32 words).  Reading taken: code
  *          k of a row is nibble k % 8 of word k / 8 of that row, least
  *          significant nibble first, in the nibble's low 3 bits; the top bit of
  *          each nibble is padding and ignored.
@@ -103,7 +117,8 @@ qw3_status qdequant_bf16(const int32_t *packed, const uint16_t *scales, uint16_t
  *   y [N] float32, written: y[n] = sum_k x[k] * scales[n][k/128] * (c[n][k] - 4)
  * The packed weights are streamed from memory once; the dense weight is never
  * formed (GLQ README, "Inference kernels").  fp32 accumulation; the result is
- * within 1e-4 * sum_k |x[k] w[n][k]| + 1e-6 of the exact sum.
+ * within 1e-4 * sum_k |x[k] w[n][k]| + 1e-6 of the exact sum (see the
+ * accuracy note above).  Uses no device memory beyond its arguments.
  */
 qw3_status qgemv_w3g128(const uint16_t *x, const int32_t *packed, const uint16_t *scales,
                         float *y, int64_t N, int64_t K, void *hip_stream);
@@ -133,19 +148,34 @@ qw3_status qgemv_w3g128_multi(const uint16_t *x, int32_t count, const int32_t *c
  *   y [M, N] float32, written: y[m][n] = sum_k x[m][k] * scales[n][k/128] * (c[n][k] - 4)
  * Any M >= 0 is accepted.  M == 1 runs the batch-1 kernel; small M streams
  * the weights once for the whole batch through bf16-exact fp16 matrix-core
- * products; large M (prefill) runs a tiled matrix-core kernel.  For M > 6
- * the call uses a device workspace that the library keeps per (device,
- * stream): the activations converted to fp16 (2 bytes per element, M rounded
- * up to 16 or 32, or to whole 128- or 256-token tiles) plus, when K is split
- * across workgroups, fp32 partial sums (4 bytes per output element and K
- * chunk).  For 2 <= M <= 6 the kernels convert the activations themselves and
- * the workspace holds only partial sums, when K is split (K = 28672, for one).  It is allocated (hipMalloc) by the first
- * call on a stream, grown -- after synchronizing that stream -- when a later
- * call needs more, and held until the process ends.  Calls on one stream run
- * in order and share it; calls on different streams use different buffers.
- * Under graph capture, make one call of the same size on the stream first, so
- * that nothing is allocated while capturing.  Same accuracy bound as
- * qgemv_w3g128.
+ * products; large M (prefill) runs a tiled matrix-core kernel.  Same accuracy
+ * bound as qgemv_w3g128.
+ *
+ * Workspace.  The call uses device scratch owned by the library, one buffer
+ * per (device, stream handle): the
+ * activations converted to fp16 (2 bytes per element, M rounded up to 16 or
+ * 32 per pass, or to whole 128- or 256-token tiles), per-group error masses
+ * (4 bytes per token and group) and, when K is split across workgroups, fp32
+ * partial sums (4 bytes per output element and K chunk).  Exceptions: M == 1
+ * uses none; 2 <= M <= 6 with 8-byte aligned scale rows and K / 128 a
+ * multiple of 64 or 56 converts the activations inside the kernel and uses
+ * only the partial sums, and only when K is split (K / 128 above 64 or 56,
+ * e.g. K = 28672).
+ *   - The first call on a stream allocates its buffer (hipMalloc).  A later
+ *     call that needs more allocates a buffer at least twice as large; the
+ *     superseded one is never freed or reused while the process runs, so work
+ *     queued earlier and graphs captured earlier stay valid.  Buffers are held
+ *     until the process ends.  The library never synchronizes a stream.
+ *   - Calls on one stream run in order and share its buffer; calls on
+ *     different streams use different buffers and may overlap.  Streams are
+ *     told apart by handle: before destroying a stream that has calls of this
+ *     library queued, wait for them (hipStreamSynchronize), since a stream
+ *     created later at the same address takes over the same buffer.
+ *   - Graph capture: a call captured on a stream uses that stream's buffer as
+ *     it is at capture time.  If the buffer would have to grow during capture
+ *     the call returns QW3_ERR_CAPTURE and enqueues nothing; make one call of
+ *     the largest size on the stream before capturing.  Replays stay valid
+ *     after later, larger calls on the stream (the old buffer is kept).
  */
 qw3_status qgemm_w3g128_smallM(const uint16_t *x, const int32_t *packed,
                                const uint16_t *scales, float *y, int64_t M, int64_t N,

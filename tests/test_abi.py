@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     assert q.raw().qw3_abi_version() == 1
-    for st in (q.QW3_OK, q.QW3_ERR_NULL, q.QW3_ERR_SHAPE, q.QW3_ERR_ALIGN, q.QW3_ERR_HIP):
+    for st in (q.QW3_OK, q.QW3_ERR_NULL, q.QW3_ERR_SHAPE, q.QW3_ERR_ALIGN, q.QW3_ERR_HIP, q.QW3_ERR_CAPTURE):
         assert q.qstatus_str(st)
     assert q.qstatus_str(12345) == "unknown status"
 

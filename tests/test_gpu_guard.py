@@ -1,0 +1,178 @@
+"""GPU parity of the products on inputs built to defeat their fp16 operands.
+
+Each case is compared with the oracle, element by element, within
+|y - y_ref| <= 1e-4 * sum_k |w_k x_k| + 1e-6 (the bound the workload statement
+fixes), through the C ABI, on every dispatch path: batch 1 (lane-per-group,
+long-row and matrix-core kernels), up to four tokens, the in-kernel and
+launched activation conversions of batched decode, 2-byte and 8-byte aligned
+scale rows, K split into chunks, the 128-token tiles and the 256-token
+prefill tiles.
+
+Two adversarial families (seeded):
+  "x": activations spanning 2^34 inside every group, slice and token -- large
+       (about 2^12) where the weight is code 4 (zero), tiny (about 2^-22)
+       where it is not, with O(1) scales, so the outputs are made of the
+       small terms that an fp16 operand with a shared exponent loses;
+  "s": scale rows spanning 2^28 -- group 0 of every row has scale 1024 and
+       codes all 4, the other groups scales near 2^-18 -- with N(0,1)
+       activations, which defeats a scale folded into an fp16 weight with
+       one exponent per row.
+Both must come out within the tolerance, which only the exactness guard's
+fixup pass achieves (tests/test_guard_emulation.py shows the fast conversion
+alone misses it on these inputs).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+RTOL = 1e-4
+ATOL = 1e-6
+
+
+def q():
+    import dequant_gemv_qgemv_amd as mod
+    return mod
+
+
+def say(*args):
+    print("[gpu-case]", *args, file=sys.stderr, flush=True)
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def assert_close(y_gpu, y_ref, a, what):
+    y_gpu = np.asarray(y_gpu, dtype=np.float64)
+    err = np.abs(y_gpu - y_ref)
+    bad = ~(err <= RTOL * a + ATOL)
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError("%s: %d of %d outside the bound; first %s: gpu %s ref %s a %s"
+                             % (what, int(bad.sum()), bad.size, idx.tolist(),
+                                [y_gpu[tuple(i)] for i in idx], [y_ref[tuple(i)] for i in idx],
+                                [a[tuple(i)] for i in idx]))
+
+
+def adversarial(kind, seed, m, n, k):
+    """codes uint8 [n, k], scales bf16 bits [n, k/128], x bf16 bits [m, k]."""
+    rng = np.random.default_rng(seed)
+    c = rng.integers(0, 8, size=(n, k), dtype=np.uint8)
+    c[c == 4] = 5
+    g = k // 128
+    if kind == "x":
+        c[:, ::8] = 4  # every 8th weight of every row is zero ...
+        xf = rng.standard_normal((m, k)).astype(np.float32) * np.float32(2.0 ** -22)
+        xf[:, ::8] = rng.standard_normal((m, (k + 7) // 8)).astype(np.float32) * np.float32(2.0 ** 12)  # ... and meets a large x
+        if m > 1:
+            xf[1] = rng.standard_normal(k).astype(np.float32)  # one benign token beside the others
+        s = synth.f32_to_bf16_bits(np.abs(rng.standard_normal((n, g))).astype(np.float32) + np.float32(0.5))
+    else:
+        c[:, :128] = 4  # group 0 is all zero weights, with the row's largest scale
+        sf = (np.abs(rng.standard_normal((n, g))).astype(np.float32) + np.float32(0.5)) * np.float32(2.0 ** -18)
+        sf[:, 0] = 1024.0
+        s = synth.f32_to_bf16_bits(sf)
+        xf = rng.standard_normal((m, k)).astype(np.float32)
+    return c, s, synth.f32_to_bf16_bits(xf)
+
+
+def run_and_check(kind, m, n, k, seed, scale_offset=0):
+    c, s, x = adversarial(kind, seed, m, n, k)
+    packed = q().qpack_uint3(dev(c))
+    if scale_offset:
+        big = torch.zeros(s.size + 8, dtype=torch.int16, device="cuda")
+        big[scale_offset:scale_offset + s.size] = dev(s.reshape(-1))
+        sd = big[scale_offset:scale_offset + s.size].view(n, k // 128)
+    else:
+        sd = dev(s)
+    say("guard", kind, "M=%d N=%d K=%d" % (m, n, k), "scale offset %d" % scale_offset)
+    if m == 1:
+        y = host(q().qgemv_w3g128(dev(x.reshape(-1)), packed, sd))[None, :]
+    else:
+        y = host(q().qgemm_w3g128_smallM(dev(x), packed, sd))
+    yr, a = oracle.gemm(x, oracle.pack(c), s, k)
+    assert_close(y, yr, a, "%s M=%d %dx%d" % (kind, m, n, k))
+    return y
+
+
+# batch 1: lane-per-group (K <= 8192), long rows through LDS (K = 28672) and
+# per lane (K = 65536), and the matrix-core kernel (N >= 16384 at K = 8192)
+@pytest.mark.parametrize("kind", ["x", "s"])
+@pytest.mark.parametrize("n,k", [(300, 1024), (200, 8192), (96, 28672), (24, 65536), (16400, 8192)])
+def test_guard_batch1(kind, n, k):
+    run_and_check(kind, 1, n, k, 100 + k + n)
+
+
+# batched decode: four-token kernel (K = 8192 one chunk, 28672 four), the ring
+# kernel converting in-kernel (5, 6 tokens) or after a conversion launch (8,
+# 16), 17..32 tokens in one pass, and the generic kernel (K / 128 = 8)
+@pytest.mark.parametrize("kind", ["x", "s"])
+@pytest.mark.parametrize("m", [2, 3, 4, 5, 6, 8, 16, 17, 32])
+@pytest.mark.parametrize("n,k", [(128, 8192), (48, 28672), (64, 1024)])
+def test_guard_batched(kind, m, n, k):
+    run_and_check(kind, m, n, k, 200 + m + k)
+
+
+# 2-byte aligned scale rows (the 16-token pass reading two bytes at a time)
+# and 8-byte aligned but not 16 (the ring and four-token kernels)
+@pytest.mark.parametrize("m", [3, 8, 24])
+@pytest.mark.parametrize("off", [1, 4])
+def test_guard_scale_views(m, off):
+    run_and_check("x", m, 40, 8192, 300 + m + off, scale_offset=off)
+
+
+# 128-token tiles (33..128 tokens) and 256-token prefill tiles (K split)
+@pytest.mark.parametrize("kind", ["x", "s"])
+@pytest.mark.parametrize("m,n,k", [(33, 64, 8192), (100, 130, 4096), (129, 72, 4096), (512, 64, 2048),
+                                   (300, 260, 1024)])
+def test_guard_tiles(kind, m, n, k):
+    run_and_check(kind, m, n, k, 400 + m + n)
+
+
+def test_guard_multi_matches_single():
+    """qgemv_w3g128_multi on adversarial activations: every output equals the
+    single-matrix call bit for bit and meets the bound."""
+    k = 8192
+    mats = []
+    for i, n in enumerate((300, 40, 40)):
+        c, s, x = adversarial("x", 500 + i, 1, n, k)
+        mats.append((c, s))
+    _, _, x = adversarial("x", 510, 1, 8, k)
+    xd = dev(x.reshape(-1))
+    say("guard multi")
+    dv = [(q().qpack_uint3(dev(c)), dev(s)) for c, s in mats]
+    ys = [host(o) for o in q().qgemv_w3g128_multi(xd, dv)]
+    for (c, s), (p, sd), y in zip(mats, dv, ys):
+        assert np.array_equal(y.view(np.uint32), host(q().qgemv_w3g128(xd, p, sd)).view(np.uint32))
+        yr, a = oracle.gemm(x, oracle.pack(c), s, k)
+        assert_close(y[None, :], yr, a, "multi")
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 16400, 8192), (4, 64, 28672), (16, 128, 8192), (32, 64, 8192),
+                                   (512, 64, 2048)])
+def test_guard_deterministic(m, n, k):
+    """With the fixup pass active, two calls give bit-identical outputs."""
+    c, s, x = adversarial("x", 600 + m, m, n, k)
+    packed, sd, xd = q().qpack_uint3(dev(c)), dev(s), dev(x)
+    say("guard determinism", m, n, k)
+    if m == 1:
+        y1 = host(q().qgemv_w3g128(xd.view(-1), packed, sd))
+        y2 = host(q().qgemv_w3g128(xd.view(-1), packed, sd))
+    else:
+        y1 = host(q().qgemm_w3g128_smallM(xd, packed, sd))
+        y2 = host(q().qgemm_w3g128_smallM(xd, packed, sd))
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
