@@ -277,24 +277,6 @@ __device__ __forceinline__ uint32_t exact_floor_bits(int e) {
     return 0u;
 }
 
-// Sum of |x| over the elements of the block below 2^(e-7) (the ones whose
-// fp16 form may be rounded or flushed), in fp32.
-__device__ __forceinline__ float small_mass(const uint4 (&xb)[4], int e) {
-    const uint32_t fl = exact_floor_bits(e);
-    float d = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t w[4] = {xb[i].x, xb[i].y, xb[i].z, xb[i].w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t lo = w[j] & 0x7FFFu, hi = (w[j] >> 16) & 0x7FFFu;
-            if (lo < fl) d += bf16_to_f32(lo);
-            if (hi < fl) d += bf16_to_f32(hi);
-        }
-    }
-    return d;
-}
-
 // 32 bf16 values -> x * 2^-(e + slot offset) as fp16, arranged as the 16
 // pairs of a block (kPairs order).
 __device__ __forceinline__ void convert_block(const uint4 (&xb)[4], int e, uint32_t (&out)[16]) {
@@ -315,6 +297,35 @@ __device__ __forceinline__ void convert_block(const uint4 (&xb)[4], int e, uint3
     }
 }
 
+// Conversion error of a block: sum over its 32 values of |x - x'|, x' the
+// value its fp16 operand stands for, fp16(x * 2^-(e+p)) * 2^(e+p) with the
+// slot offset p of convert_block.  fp16 subnormals are kept by the conversion
+// and by every fp16 product used here (measured on gfx950), so an element
+// converts exactly unless its low bits fall below 2^-24 after scaling; each
+// difference is exact in fp32.  Only called when the block has a value below
+// 2^(e-7), the smallest that is surely exact.
+__device__ __forceinline__ float conversion_error(const uint4 (&xb)[4], int e) {
+    float f[32];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t d[4] = {xb[i].x, xb[i].y, xb[i].z, xb[i].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            f[8 * i + 2 * j] = bf16_to_f32(d[j] & 0xFFFFu);
+            f[8 * i + 2 * j + 1] = bf16_to_f32(d[j] >> 16);
+        }
+    }
+    float err = 0.f;
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+        const PairSpec ps = kPairs[p];
+        const float a = ldexpf(f[ps.lo], -e - ps.p), b = ldexpf(f[ps.hi], -e - ps.pp);
+        err += ldexpf(fabsf(a - (float)(_Float16)a), e + ps.p);
+        err += ldexpf(fabsf(b - (float)(_Float16)b), e + ps.pp);
+    }
+    return err;
+}
+
 __device__ __forceinline__ void load_x32(const uint16_t *src, uint4 (&xb)[4]) {
     const uint4 *s = reinterpret_cast<const uint4 *>(src);
 #pragma unroll
@@ -333,7 +344,7 @@ constexpr int kNzCap = 128;  // compacted list of groups with a non-zero D
 // three little-endian words.  Each product (c - 4) x is exact in fp32; a
 // group's 128 products are added in order, the group sums (times their
 // scale) in runs of 32 groups, the runs in order.
-__device__ __noinline__ float exact_output(const uint16_t *__restrict__ xrow, const uint32_t *__restrict__ wrow,
+__device__ __forceinline__ float exact_output(const uint16_t *__restrict__ xrow, const uint32_t *__restrict__ wrow,
                                            const uint16_t *__restrict__ srow, int g0, int g1) {
     float tot = 0.f;
     for (int gb = g0; gb < g1; gb += 32) {
@@ -397,7 +408,7 @@ struct BlockRows {
 // receives their count (which may exceed kNzCap).  All threads of the
 // workgroup call it (it ends with a barrier).
 template <class AnyD>
-__device__ __noinline__ int build_nz(int g0, int g1, AnyD any_d, int *nz) {
+__device__ __forceinline__ int build_nz(int g0, int g1, AnyD any_d, int *nz) {
     if (threadIdx.x < 64) {
         const int lane = threadIdx.x;
         int cnt = 0;
@@ -423,7 +434,7 @@ __device__ __noinline__ int build_nz(int g0, int g1, AnyD any_d, int *nz) {
 // nnz > kNzCap: every group of the range).  Threads tid, tid + nthr, ... take
 // one row each.  The caller orders the fast path's stores before this pass.
 template <int TB, class DAt>
-__device__ __noinline__ void fixup_outputs(const uint16_t *__restrict__ x, int64_t ldx, int Mt,
+__device__ __forceinline__ void fixup_outputs(const uint16_t *__restrict__ x, int64_t ldx, int Mt,
                               const uint32_t *__restrict__ packed, const uint16_t *__restrict__ scales, int G,
                               int g0, int g1, const BlockRows &rows, DAt d_at, const int *nz, int nnz, bool fold,
                               float *__restrict__ out, int64_t ldo, int tid, int nthr) {
@@ -642,11 +653,11 @@ __device__ __forceinline__ void xstage_issue(const uint16_t *__restrict__ x, int
 // LDS layout of the converted activations: xs4[q][g] holds pairs 4q..4q+3 of
 // group g (16 bytes), q = 0..15, so that when lane g fetches its group the 64
 // lanes of each ds_read_b128 touch 64 consecutive 16-byte chunks (no bank
-// conflicts); exponents follow as int[G].  Each group's error mass D goes to
-// xd[g].  Returns whether this thread saw an element below its group's exact
-// range (D non-zero).
+// conflicts); exponents follow as int[G].  Returns whether this thread saw a
+// value below its group's surely-exact range (the guard's cheap test; the
+// conversion error itself is computed only then, by group_errors).
 template <int U>
-__device__ __forceinline__ bool xstage_convert(const XStage<U> &st, int G, uint32_t *smem, float *xd) {
+__device__ __forceinline__ bool xstage_convert(const XStage<U> &st, int G, uint32_t *smem) {
     uint4 *xs4 = reinterpret_cast<uint4 *>(smem);                // [16][G]
     int *xe = reinterpret_cast<int *>(smem + (size_t)G * 64);  // [G]
     bool small = false;
@@ -657,26 +668,61 @@ __device__ __forceinline__ bool xstage_convert(const XStage<U> &st, int G, uint3
         block_stats(st.raw[u], m, mn);
         m = max(m, dpp_u32<kDppQuadXor1>(m));
         m = max(m, dpp_u32<kDppQuadXor2>(m));
-        const int eg = group_exponent(m);
-        float d = 0.f;
-        if (idx < 4 * G && mn < exact_floor_bits(eg)) d = small_mass(st.raw[u], eg);  // rare
-        small |= d != 0.f;
-        d += dpp_f32<kDppQuadXor1>(d);
-        d += dpp_f32<kDppQuadXor2>(d);
         if (idx < 4 * G) {
             const int g = idx >> 2, blk = idx & 3;
+            const int eg = group_exponent(m);
+            small |= mn < exact_floor_bits(eg);
             uint32_t out[16];
             convert_block(st.raw[u], eg, out);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 xs4[(size_t)(4 * blk + i) * G + g] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
-            if (blk == 0) {
-                xe[g] = eg;
-                xd[g] = d;
-            }
+            if (blk == 0) xe[g] = eg;
         }
     }
     return small;
+}
+
+// The guard's error masses of a batch-1 activation vector, one exponent per
+// group as in the staging: xd[g] = conversion_error summed over group g.  All
+// threads of the workgroup call it (it ends with a barrier).
+__device__ __forceinline__ void group_errors(const uint16_t *__restrict__ x, int G, float *xd) {
+    for (int u = threadIdx.x; u < 4 * G; u += blockDim.x) {  // a quad of threads per group
+        uint4 xb[4];
+        load_x32(x + (size_t)(u >> 2) * kGroup + (u & 3) * 32, xb);
+        uint32_t m, mn;
+        block_stats(xb, m, mn);
+        m = max(m, dpp_u32<kDppQuadXor1>(m));
+        m = max(m, dpp_u32<kDppQuadXor2>(m));
+        float d = conversion_error(xb, group_exponent(m));
+        d += dpp_f32<kDppQuadXor1>(d);
+        d += dpp_f32<kDppQuadXor2>(d);
+        if ((u & 3) == 0) xd[u >> 2] = d;
+    }
+    __syncthreads();
+}
+
+// The same for the batched kernels that convert in-kernel: tokens t < M (x
+// row t at x + t * K), one exponent per (token, 8-group slice), the slices of
+// groups [g0, g0 + 8 S): xd[t][g - g0].  Half a wave per (token, slice).
+__device__ __forceinline__ void slice_errors(const uint16_t *__restrict__ x, int64_t K, int M, int g0, int S,
+                                             float *xd) {
+    const int units = M * S * 32;
+    for (int u = threadIdx.x; u < units; u += blockDim.x) {  // units and blockDim are multiples of 32
+        const int b = u & 3, gi = (u >> 2) & 7, ts = u >> 5;
+        const int t = ts / S, sl = ts % S;
+        uint4 xb[4];
+        load_x32(x + t * K + (int64_t)(g0 + 8 * sl + gi) * kGroup + 32 * b, xb);
+        uint32_t m, mn;
+        block_stats(xb, m, mn);
+#pragma unroll
+        for (int off = 1; off < 32; off <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 32));
+        float d = conversion_error(xb, group_exponent(m));
+        d += dpp_f32<kDppQuadXor1>(d);
+        d += dpp_f32<kDppQuadXor2>(d);
+        if (b == 0) xd[t * (8 * S) + 8 * sl + gi] = d;
+    }
+    __syncthreads();
 }
 
 // One word per wave in LDS: whether any lane of the wave passed `mine`.
@@ -708,9 +754,10 @@ __device__ __forceinline__ void xstage_fetch(const uint32_t *smem, int G, int gl
 }
 
 // Activation staging without LDS (very long rows): each lane converts its own
-// group in two passes (max, then convert).  Returns the group's error mass D.
-__device__ __forceinline__ float xstage_lane(const uint16_t *__restrict__ x, int gl, bool lane_on,
-                                             uint32_t (&xp)[64], int &e) {
+// group in two passes (max, then convert).  Returns the guard's cheap test
+// for the group (a value below its surely-exact range).
+__device__ __forceinline__ bool xstage_lane(const uint16_t *__restrict__ x, int gl, bool lane_on,
+                                            uint32_t (&xp)[64], int &e) {
     const uint16_t *xg = x + (size_t)(lane_on ? gl : 0) * kGroup;
     uint32_t m = 0, mn = 0x10000u;
 #pragma unroll
@@ -724,19 +771,17 @@ __device__ __forceinline__ float xstage_lane(const uint16_t *__restrict__ x, int
     }
     e = group_exponent(m);
     const bool small = lane_on && mn < exact_floor_bits(e);
-    float d = 0.f;
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk) {
         uint4 xb[4];
         load_x32(xg + blk * 32, xb);
         uint32_t out[16];
         convert_block(xb, e, out);
-        if (small) d += small_mass(xb, e);  // rare
 #pragma unroll
         for (int p = 0; p < 16; ++p) xp[blk * 16 + p] = lane_on ? out[p] : 0u;
     }
     if (!lane_on) e = 0;
-    return d;
+    return small;
 }
 
 // Up to 4 weight matrices with the same K that share one activation vector
@@ -807,10 +852,11 @@ __global__ __launch_bounds__(kGemvWGS) void qgemv_small_kernel(const uint16_t *_
         xstage_issue<1>(x, G, st);
 #pragma unroll
         for (int d = 0; d < D; ++d) load(row0 + d * stride, ring[d]);
-        publish_flag(xstage_convert<1>(st, G, smem, xd), flags);
+        publish_flag(xstage_convert<1>(st, G, smem), flags);
         __syncthreads();
         xstage_fetch(smem, G, gl, lane_on, xp, e);
     }
+    const bool fix = __builtin_amdgcn_readfirstlane(any_flag(flags) ? 1 : 0) != 0;  // the guard, workgroup-uniform
     const uint32_t magic = magic_vgpr();
 
     for (int64_t row = row0; row < N; row += E * stride) {
@@ -824,8 +870,9 @@ __global__ __launch_bounds__(kGemvWGS) void qgemv_small_kernel(const uint16_t *_
             if (gl == T - 1 && r < N) y[r] = tot;
         }
     }
-    if (any_flag(flags)) {  // workgroup-uniform, rare
+    if (fix) {  // rare
         __syncthreads();
+        group_errors(x, G, xd);
         const int nnz = build_nz(0, G, [&](int g) { return xd[g] != 0.f; }, nz);
         fixup_outputs<1>(x, 0, 1, packed, scales, G, 0, G, BlockRows{blk, nblk, R, N},
                          [&](int, int g) { return xd[g]; }, nz, nnz, false, y, 0, threadIdx.x, blockDim.x);
@@ -845,6 +892,15 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // LDS_X: the converted activations fit in LDS (K <= 32768); otherwise each
 // lane converts its own group.  A template parameter, so that one prologue
 // reaches the loop and the loop's waits are exact.
+// The batch-1 fixup out of line, for kernels held to 128 VGPRs (1024-thread
+// workgroups), where the inlined pass would crowd the main loop's registers.
+__device__ __noinline__ void fixup_m1_call(const uint16_t *x, const uint32_t *packed, const uint16_t *scales, float *y,
+                                           int G, BlockRows rows, const float *xd, const int *nz, int nnz, int tid,
+                                           int nthr) {
+    fixup_outputs<1>(x, 0, 1, packed, scales, G, 0, G, rows, [&](int, int g) { return xd[g]; }, nz, nnz, false, y, 0,
+                     tid, nthr);
+}
+
 constexpr int kBigRedWords = 256;  // half-sum slots of qgemv_big_kernel: 2 (E <= 4) x E x (<= 32 halves)
 // LDS words of qgemv_big_kernel: the staging (LDS_X) or the half sums, then
 // xd [G], 16 wave flags and the fixup's group list.
@@ -878,6 +934,7 @@ __global__ __launch_bounds__(MAXWGS) void qgemv_big_kernel(const uint16_t *__res
     uint32_t xp[64];
     int e = 0;
     RowBuf ring[E];
+    bool fix = false;
     if constexpr (LDS_X) {
         XStage<4> st;  // 4G <= 4 * blockDim (T >= G, blockDim >= T)
         xstage_issue<4>(x, G, st);
@@ -887,9 +944,10 @@ __global__ __launch_bounds__(MAXWGS) void qgemv_big_kernel(const uint16_t *__res
             load_row(packed, scales, row0 + d * stride, N, W, G, g_load, ring[d]);
         }
         __builtin_amdgcn_sched_barrier(0);
-        publish_flag(xstage_convert<4>(st, G, smem, xd), flags);
+        publish_flag(xstage_convert<4>(st, G, smem), flags);
         __syncthreads();
         xstage_fetch(smem, G, gl, lane_on, xp, e);
+        fix = __builtin_amdgcn_readfirstlane(any_flag(flags) ? 1 : 0) != 0;  // the guard, workgroup-uniform
         __syncthreads();  // LDS is reused for the half sums below
     } else {
 #pragma unroll
@@ -898,9 +956,7 @@ __global__ __launch_bounds__(MAXWGS) void qgemv_big_kernel(const uint16_t *__res
             load_row(packed, scales, row0 + d * stride, N, W, G, g_load, ring[d]);
         }
         __builtin_amdgcn_sched_barrier(0);
-        const float dg = xstage_lane(x, gl, lane_on, xp, e);
-        if (team == 0 && lane_on) xd[gl] = dg;  // seen after the loop's first barrier
-        publish_flag(dg != 0.f, flags);
+        publish_flag(xstage_lane(x, gl, lane_on, xp, e), flags);  // read after the loop's barriers
     }
     const uint32_t magic = magic_vgpr();
 
@@ -934,11 +990,17 @@ __global__ __launch_bounds__(MAXWGS) void qgemv_big_kernel(const uint16_t *__res
         }
         parity ^= 1;
     }
-    if (any_flag(flags)) {  // workgroup-uniform, rare
+    if (!LDS_X) fix = any_flag(flags);  // published before the loop's barriers
+    if (fix) {  // workgroup-uniform, rare
         __syncthreads();
+        group_errors(x, G, xd);
         const int nnz = build_nz(0, G, [&](int g) { return xd[g] != 0.f; }, nz);
-        fixup_outputs<1>(x, 0, 1, packed, scales, G, 0, G, BlockRows{(int64_t)blockIdx.x, (int64_t)gridDim.x, R, N},
-                         [&](int, int g) { return xd[g]; }, nz, nnz, false, y, 0, tid, wgs);
+        const BlockRows rows{(int64_t)blockIdx.x, (int64_t)gridDim.x, R, N};
+        if constexpr (MAXWGS > 512)
+            fixup_m1_call(x, packed, scales, y, G, rows, xd, nz, nnz, tid, wgs);
+        else
+            fixup_outputs<1>(x, 0, 1, packed, scales, G, 0, G, rows, [&](int, int g) { return xd[g]; }, nz, nnz, false,
+                             y, 0, tid, wgs);
     }
 }
 
@@ -1060,8 +1122,9 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_mfma_kernel(const uint16_t *
         load(s / NS, s % NS, ring[s % RS]);
         __builtin_amdgcn_sched_barrier(0);
     }
-    publish_flag(xstage_convert<XU>(st, G, smem, xd), flags);
+    publish_flag(xstage_convert<XU>(st, G, smem), flags);
     __syncthreads();
+    const bool fix = __builtin_amdgcn_readfirstlane(any_flag(flags) ? 1 : 0) != 0;  // the guard, workgroup-uniform
     h8_t xa[AS][16];  // step t = 4 * block + u: pairs 4u .. 4u + 3 of 32-code block `block`
     float fe[AS][4];  // 2^e of the groups whose partials this lane scales (lane row lj of each set)
     {
@@ -1163,8 +1226,9 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_mfma_kernel(const uint16_t *
             if constexpr (i >= NS * (UT - 1) && i < AH)
                 asm volatile("" ::"v"(ring[i].a), "v"(ring[i].b), "v"(ring[i].c), "v"(ring[i].s));
         });
-    if (any_flag(flags)) {  // workgroup-uniform, rare
+    if (fix) {  // rare
         __syncthreads();
+        group_errors(x, G, xd);
         const int nnz = build_nz(0, G, [&](int g) { return xd[g] != 0.f; }, nz);
         fixup_outputs<1>(x, 0, 1, packed, scales, G, 0, G, BlockRows{blk, nblk, 16, N},
                          [&](int, int g) { return xd[g]; }, nz, nnz, false, y, 0, threadIdx.x, blockDim.x);
@@ -1200,7 +1264,7 @@ __global__ __launch_bounds__(256) void prep_x_kernel(const uint16_t *__restrict_
         mx = max(mx, dpp_u32<kDppQuadXor1>(mx));
         mx = max(mx, dpp_u32<kDppQuadXor2>(mx));
         eg = group_exponent(mx);
-        if (mn < exact_floor_bits(eg)) d = small_mass(xb, eg);  // rare
+        if (mn < exact_floor_bits(eg)) d = conversion_error(xb, eg);  // rare
         convert_block(xb, eg, out);
     } else {
 #pragma unroll
@@ -1367,7 +1431,7 @@ __global__ __launch_bounds__(256) void prep_x_slice_kernel(const uint16_t *__res
 #pragma unroll
     for (int off = 1; off < 32; off <<= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 32));
     const int e = m < M ? group_exponent(mx) : 0;
-    float d = (m < M && mn < exact_floor_bits(e)) ? small_mass(xb, e) : 0.f;  // rare
+    float d = (m < M && mn < exact_floor_bits(e)) ? conversion_error(xb, e) : 0.f;  // rare
     const bool any = (__ballot(d != 0.f) >> (threadIdx.x & 32)) & 0xFFFFFFFFull;  // this half-wave
     d += dpp_f32<kDppQuadXor1>(d);
     d += dpp_f32<kDppQuadXor2>(d);
@@ -1678,16 +1742,9 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_mr_kernel(const uint4 *__res
         mx = max(mx, (uint32_t)__shfl_xor((int)mx, 16));
         mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32));
         const int e = group_exponent(mx);
-        // Error masses of token n % 8, groups g0 + 4(n / 8) + k: the four
-        // lane rows' blocks summed, kept in LDS for the fixup pass.
+        // The guard's cheap test (a value below the slice's exact range).
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            float d = mnk[k] < exact_floor_bits(e) ? small_mass(xh[k], e) : 0.f;  // rare
-            small |= d != 0.f;
-            d += __shfl_xor(d, 16);
-            d += __shfl_xor(d, 32);
-            if (j == 0 && (n & 7) < M) xdl[(n & 7) * (WAVES * 8) + wave * 8 + 4 * (n >> 3) + k] = d;
-        }
+        for (int k = 0; k < 4; ++k) small |= mnk[k] < exact_floor_bits(e);
         const bool lo = n < 8;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -1800,6 +1857,7 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_mr_kernel(const uint4 *__res
     if (any_flag(flags)) {  // workgroup-uniform, rare
         __syncthreads();
         const int gc0 = chunk * WAVES * GW, gc1 = gc0 + WAVES * GW;
+        if constexpr (XH) slice_errors(x, (int64_t)G * kGroup, M, gc0, WAVES, xdl);
         auto d_at = [&](int m, int g) {
             return XH ? xdl[m * (WAVES * 8) + (g - gc0)] : xd[(int64_t)g * Mp + m];
         };
@@ -1899,17 +1957,10 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_m4_kernel(const uint16_t *__
         mx = max(mx, (uint32_t)__shfl_xor((int)mx, 16));
         mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32));
         const int e = group_exponent(mx);
-        // Error masses of token n / 4, groups g0 + 4q + j (the quad's four
-        // blocks summed), kept in LDS for the fixup pass.
+        // The guard's cheap test (a value below the slice's exact range).
         bool small = false;
 #pragma unroll
-        for (int q = 0; q < NS; ++q) {
-            float d = mnq[q] < exact_floor_bits(e) ? small_mass(xb[q], e) : 0.f;  // rare
-            small |= d != 0.f;
-            d += dpp_f32<kDppQuadXor1>(d);
-            d += dpp_f32<kDppQuadXor2>(d);
-            if ((n & 3) == 0 && (n >> 2) < M) xdl[(n >> 2) * (WAVES * GW) + wave * GW + 4 * q + j] = d;
-        }
+        for (int q = 0; q < NS; ++q) small |= mnq[q] < exact_floor_bits(e);
         publish_flag(small, flags);
         const bool on = (n & 3) == j;
 #pragma unroll
@@ -1994,6 +2045,7 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_m4_kernel(const uint16_t *__
     if (any_flag(flags)) {  // workgroup-uniform (the loop's barriers published the flags), rare
         __syncthreads();
         const int gc0 = chunk * WAVES * GW, gc1 = gc0 + WAVES * GW;
+        slice_errors(x, (int64_t)G * kGroup, M, gc0, WAVES, xdl);
         auto d_at = [&](int m, int g) { return xdl[m * (WAVES * GW) + (g - gc0)]; };
         const int nnz = build_nz(gc0, gc1, [&](int g) {
             bool f = false;
@@ -2067,7 +2119,7 @@ __global__ __launch_bounds__(256) void prep_tile_x_kernel(const uint16_t *__rest
         load_x32(src + u * 32, xb);
         uint32_t bm, bn;
         block_stats(xb, bm, bn);
-        float d = bn < floor_bits ? small_mass(xb, e) : 0.f;  // rare
+        float d = bn < floor_bits ? conversion_error(xb, e) : 0.f;  // rare
         dsum += d;
         d += dpp_f32<kDppQuadXor1>(d);
         d += dpp_f32<kDppQuadXor2>(d);
@@ -2085,6 +2137,22 @@ __global__ __launch_bounds__(256) void prep_tile_x_kernel(const uint16_t *__rest
         xe[m] = e;
         dtot[m] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
     }
+}
+
+// The fixup pass of one tile-kernel workgroup, out of line so that the main
+// kernel's registers stay with its MFMA loop: tokens [0, mt) of the tile (x,
+// xd and y already offset to its first token), rows of `rows`, groups
+// [g0, g1), every row's fold checked.  All threads call it.
+__device__ __noinline__ void fixup_tile_call(const uint16_t *x, int64_t K, int mt, const uint32_t *packed,
+                                             const uint16_t *scales, int G, int g0, int g1, BlockRows rows,
+                                             const float *xd, int *nz, float *y, int64_t ldo) {
+    auto d_at = [&](int m, int g) { return xd[(int64_t)m * G + g]; };
+    const int nnz = build_nz(g0, g1, [&](int g) {
+        bool f = false;
+        for (int m = 0; m < mt; ++m) f |= d_at(m, g) != 0.f;
+        return f;
+    }, nz);
+    fixup_outputs<8>(x, K, mt, packed, scales, G, g0, g1, rows, d_at, nz, nnz, true, y, ldo, threadIdx.x, blockDim.x);
 }
 
 // Whether the tile kernels' fast result may be outside the accuracy bound
@@ -2194,6 +2262,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         need = mx != 0 && bf16_to_f32(mn) < ldexpf(1.0f, E - 17);
     }
     __syncthreads();
+    // The guard, decided before the loop: a row that does not fold exactly,
+    // or a token error mass large enough to matter against this lane's rows.
+    {
+        float dmax = 0.f;
+        int en_max = -1000;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int tok = m0 + (wave & 1) * 64 + 16 * i + 4 * ((tid & 63) >> 4) + r;
+                dmax = fmaxf(dmax, dtot[tok < M ? tok : M - 1]);
+            }
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) en_max = max(en_max, En[(wave >> 1) * 64 + 16 * jj + (tid & 15)]);
+        publish_flag(need || tile_coarse_flag(en_max, dmax), flags);
+    }
+    __syncthreads();
+    const bool fix = __builtin_amdgcn_readfirstlane(any_flag(flags) ? 1 : 0) != 0;
 
     // Loader roles.  A: token tid/2, 64 fp16 (half a group row) = 8 x 16 B.
     // B: rows tid/4 and 64 + tid/4, block tid%4 (12 bytes each).
@@ -2272,25 +2358,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
 #undef QW3_TILE_STEP
 
-    // the exponents and error masses of the lane's 16 tokens, loaded
-    // together (past M: the last)
+    // the exponents of the lane's 16 tokens, loaded together (past M: the last)
     int xt[4][4];
-    float dmax = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int tok = m0 + wm * 64 + 16 * i + 4 * lc + r;
             xt[i][r] = xe[tok < M ? tok : M - 1];
-            dmax = fmaxf(dmax, dtot[tok < M ? tok : M - 1]);
         }
-    int en_max = -1000;
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
         const int nl = wn * 64 + 16 * jj + lr;
         const int64_t row = n0 + nl;
         const int en = En[nl];
-        en_max = max(en_max, en);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -2300,21 +2381,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             }
         }
     }
-    // The guard: rows that do not fold exactly, or a token error mass large
-    // enough to matter against this lane's rows -> the fixup pass.
-    need |= tile_coarse_flag(en_max, dmax);
-    publish_flag(need, flags);
-    __syncthreads();  // also orders the stores above before the fixup's
-    if (any_flag(flags)) {
-        const int mt = M - m0 < kTileBM ? M - m0 : kTileBM;
-        auto d_at = [&](int m, int g) { return xd[(int64_t)(m0 + m) * G + g]; };
-        const int nnz = build_nz(0, G, [&](int g) {
-            bool f = false;
-            for (int m = 0; m < mt; ++m) f |= d_at(m, g) != 0.f;
-            return f;
-        }, nz);
-        fixup_outputs<8>(x + (int64_t)m0 * K, K, mt, packed, scales, G, 0, G, BlockRows{n_tile, NT, kTileBN, N}, d_at,
-                         nz, nnz, true, y + (int64_t)m0 * N, N, tid, blockDim.x);
+    if (fix) {  // workgroup-uniform, rare
+        __syncthreads();  // orders the stores above before the fixup's
+        fixup_tile_call(x + (int64_t)m0 * K, K, M - m0 < kTileBM ? M - m0 : kTileBM, packed, scales, G, 0, G,
+                        BlockRows{n_tile, NT, kTileBN, N}, xd + (int64_t)m0 * G, nz, y + (int64_t)m0 * N, N);
     }
 }
 #undef QW3_TILE_LOAD
@@ -2498,10 +2568,28 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(dma_off[i]));
     };
 
+    // The guard, decided before the loop: a row that does not fold exactly, or
+    // a token error mass of the tile large enough to matter against this
+    // wave's rows (4 tokens per lane, then the wave's maxima).
+    {
+        float dmax = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int tok = m0 + 4 * lane + r;
+            dmax = fmaxf(dmax, dtot[tok < M ? tok : M - 1]);
+        }
+        int en_max = max(max(en[0], en[1]), max(en[2], en[3]));
+        for (int off = 32; off >= 1; off >>= 1) {
+            dmax = fmaxf(dmax, __shfl_xor(dmax, off));
+            en_max = max(en_max, __shfl_xor(en_max, off));
+        }
+        publish_flag(need || tile_coarse_flag(en_max, dmax), flags);
+    }
     dma_a(gbeg, stage_a);
     load_w(gbeg, wcur, scur);
     __builtin_amdgcn_s_waitcnt(0);
     lds_barrier();
+    const bool fix = __builtin_amdgcn_readfirstlane(any_flag(flags) ? 1 : 0) != 0;
     // two groups per iteration, so each one's stage is a fixed array
     for (int g = gbeg; g < gbeg + Gc; g += 2) {
         group(g, stage_a, stage_b);
@@ -2511,20 +2599,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // read the last one): loaded next to each store, every store waited for
     // its own load.
     int xt[8][4];
-    float dmax = 0.f;
 #pragma unroll
     for (int mi = 0; mi < 8; ++mi)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int tok = m0 + wm * 128 + 16 * mi + 4 * lc + r;
             xt[mi][r] = xe[tok < M ? tok : M - 1];
-            dmax = fmaxf(dmax, dtot[tok < M ? tok : M - 1]);
         }
-    int en_max = -1000;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
         const int64_t row = n0 + wn * 16 * NI + 16 * i + lr;
-        en_max = max(en_max, en[i]);
 #pragma unroll
         for (int mi = 0; mi < 8; ++mi) {
 #pragma unroll
@@ -2534,21 +2618,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             }
         }
     }
-    // The guard: rows that do not fold exactly, or a token error mass large
-    // enough to matter against this lane's rows -> the fixup pass.
-    need |= tile_coarse_flag(en_max, dmax);
-    publish_flag(need, flags);
-    __syncthreads();  // also orders the stores above before the fixup's
-    if (any_flag(flags)) {
-        const int mt = M - m0 < kPfBM ? M - m0 : kPfBM;
-        auto d_at = [&](int m, int g) { return xd[(int64_t)(m0 + m) * G + g]; };
-        const int nnz = build_nz(gbeg, gbeg + Gc, [&](int g) {
-            bool f = false;
-            for (int m = 0; m < mt; ++m) f |= d_at(m, g) != 0.f;
-            return f;
-        }, nz);
-        fixup_outputs<8>(x + (int64_t)m0 * K, K, mt, packed, scales, G, gbeg, gbeg + Gc, BlockRows{n_tile, NT, kPfBN, N},
-                         d_at, nz, nnz, true, y + (int64_t)m0 * N, N, tid, blockDim.x);
+    if (fix) {  // workgroup-uniform, rare
+        __syncthreads();  // orders the stores above before the fixup's
+        fixup_tile_call(x + (int64_t)m0 * K, K, M - m0 < kPfBM ? M - m0 : kPfBM, packed, scales, G, gbeg, gbeg + Gc,
+                        BlockRows{n_tile, NT, kPfBN, N}, xd + (int64_t)m0 * G, nz, y + (int64_t)m0 * N, N);
     }
 }
 

@@ -65,8 +65,8 @@ enum {
     QW3_ERR_SHAPE = -2, /* negative size, K % 128 != 0, or K > QW3_MAX_K      */
     QW3_ERR_ALIGN = -3, /* a pointer is not aligned as stated above           */
     QW3_ERR_HIP = -4,   /* the HIP runtime reported an error                  */
-    QW3_ERR_CAPTURE = -5 /* qgemm_w3g128_smallM would have to allocate its
-                            workspace while the stream is being captured       */
+    QW3_ERR_CAPTURE = -5  /* qgemm_w3g128_smallM would have to allocate its
+                             workspace while the stream is being captured      */
 };
 
 /* Largest supported in_features (1024 groups of 128). */
