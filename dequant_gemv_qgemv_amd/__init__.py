@@ -26,6 +26,7 @@ __all__ = [
     "qgemv_w3g128",
     "qgemv_w3g128_multi",
     "qgemm_w3g128_smallM",
+    "qgemm_w3g128_smallM_noalloc",
     "qstatus_str",
     "check_quantization_config",
     "library_path",
@@ -37,11 +38,14 @@ __all__ = [
     "QW3_ERR_ALIGN",
     "QW3_ERR_HIP",
     "QW3_ERR_CAPTURE",
+    "QW3_ERR_SCRATCH",
+    "QW3_NOALLOC_SCRATCH_BYTES",
     "QW3_MAX_K",
     "QW3_MAX_MULTI",
 ]
 
-QW3_OK, QW3_ERR_NULL, QW3_ERR_SHAPE, QW3_ERR_ALIGN, QW3_ERR_HIP, QW3_ERR_CAPTURE = 0, -1, -2, -3, -4, -5
+QW3_OK, QW3_ERR_NULL, QW3_ERR_SHAPE, QW3_ERR_ALIGN, QW3_ERR_HIP, QW3_ERR_CAPTURE, QW3_ERR_SCRATCH = 0, -1, -2, -3, -4, -5, -6
+QW3_NOALLOC_SCRATCH_BYTES = 128 << 20
 QW3_MAX_K = 131072
 QW3_MAX_MULTI = 4
 GROUP = 128
@@ -49,7 +53,8 @@ GROUP = 128
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libqw3.so")
 _EXPORTS = ("qpack_uint3", "qrepack_w4c_uint3", "qdequant_bf16", "qgemv_w3g128", "qgemv_w3g128_multi",
-            "qgemm_w3g128_smallM", "qstatus_str", "qw3_last_hip_error", "qw3_abi_version")
+            "qgemm_w3g128_smallM", "qgemm_w3g128_smallM_noalloc", "qstatus_str", "qw3_last_hip_error",
+            "qw3_abi_version")
 
 if not os.path.exists(_LIB_PATH):
     raise ImportError(
@@ -63,9 +68,10 @@ _lib.qrepack_w4c_uint3.argtypes = [_vp, _vp, _i64, _i64, _vp]
 _lib.qdequant_bf16.argtypes = [_vp, _vp, _vp, _i64, _i64, _vp]
 _lib.qgemv_w3g128.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _vp]
 _lib.qgemm_w3g128_smallM.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]
+_lib.qgemm_w3g128_smallM_noalloc.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]
 _lib.qgemv_w3g128_multi.argtypes = [_vp, ctypes.c_int32, _vp, _vp, _vp, _vp, _i64, _vp]
 for _name in ("qpack_uint3", "qrepack_w4c_uint3", "qdequant_bf16", "qgemv_w3g128", "qgemv_w3g128_multi",
-              "qgemm_w3g128_smallM"):
+              "qgemm_w3g128_smallM", "qgemm_w3g128_smallM_noalloc"):
     getattr(_lib, _name).restype = ctypes.c_int
 _lib.qstatus_str.argtypes = [ctypes.c_int]
 _lib.qstatus_str.restype = ctypes.c_char_p
@@ -269,6 +275,24 @@ def qgemm_w3g128_smallM(x: torch.Tensor, packed: torch.Tensor, scales: torch.Ten
     with torch.cuda.device(packed.device):
         _check(_lib.qgemm_w3g128_smallM(_ptr(x), _ptr(packed), _ptr(scales), _ptr(out), m, n, k,
                                         _stream()), "qgemm_w3g128_smallM")
+    return out
+
+
+def qgemm_w3g128_smallM_noalloc(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
+                                out: torch.Tensor) -> torch.Tensor:
+    """qgemm_w3g128_smallM without any device allocation: the caller passes
+    `out` (float32 [M, N]) and the library's static scratch is used."""
+    n, k = _check_weight(packed, scales)
+    _need(x, "x", _BF16, 2)
+    m = x.shape[0]
+    if x.shape[1] != k or x.device != packed.device:
+        raise ValueError("x must be [M, %d] on %s" % (k, packed.device))
+    _need(out, "out", (torch.float32,), 2)
+    if tuple(out.shape) != (m, n) or out.device != packed.device:
+        raise ValueError("out must be [%d, %d] on %s" % (m, n, packed.device))
+    with torch.cuda.device(packed.device):
+        _check(_lib.qgemm_w3g128_smallM_noalloc(_ptr(x), _ptr(packed), _ptr(scales), _ptr(out), m, n, k,
+                                                _stream()), "qgemm_w3g128_smallM_noalloc")
     return out
 
 

@@ -2734,10 +2734,41 @@ qw3_status workspace(hipStream_t stream, size_t bytes, void **out) {
     return QW3_OK;
 }
 
+// Static source, for callers that cannot allocate (qgemm_w3g128_smallM_noalloc):
+// the file-scope array `scratch`, one copy per device for the life of the
+// process.  On the host its name is only a stand-in; the device address is
+// looked up once per device with hipGetSymbolAddress (with that device
+// current) and used everywhere instead.  Calls on one device share the array,
+// so calls that overlap on one device race; every byte a call reads from it
+// is written earlier by the same call, so nothing needs clearing.
+constexpr size_t kScratchBytes = size_t(QW3_NOALLOC_SCRATCH_BYTES);
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+void *g_scratch_ptr[64];
+
+qw3_status static_scratch(size_t bytes, void **out) {
+    if (bytes > kScratchBytes) return QW3_ERR_SCRATCH;
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return hip_fail(err);
+    if (dev < 0 || dev >= 64) return hip_fail(hipErrorInvalidDevice);
+    std::lock_guard<std::mutex> lock(g_dev_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess) return hip_fail(err);
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return QW3_OK;
+}
+
 // Where a call takes its scratch from.
 struct ScratchSrc {
     hipStream_t stream;
-    qw3_status get(size_t bytes, void **out) const { return workspace(stream, bytes, out); }
+    bool fixed;  // the static array instead of the per-stream workspace
+    qw3_status get(size_t bytes, void **out) const {
+        return fixed ? static_scratch(bytes, out) : workspace(stream, bytes, out);
+    }
 };
 
 // Carves consecutive 256-byte-aligned pieces out of one scratch buffer.
@@ -3316,7 +3347,12 @@ qw3_status qgemv_w3g128_multi(const uint16_t *x, int32_t count, const int32_t *c
 
 qw3_status qgemm_w3g128_smallM(const uint16_t *x, const int32_t *packed, const uint16_t *scales, float *y,
                                int64_t M, int64_t N, int64_t K, void *hip_stream) {
-    return run_gemm(x, packed, scales, y, M, N, K, ScratchSrc{(hipStream_t)hip_stream});
+    return run_gemm(x, packed, scales, y, M, N, K, ScratchSrc{(hipStream_t)hip_stream, false});
+}
+
+qw3_status qgemm_w3g128_smallM_noalloc(const uint16_t *x, const int32_t *packed, const uint16_t *scales, float *y,
+                                       int64_t M, int64_t N, int64_t K, void *hip_stream) {
+    return run_gemm(x, packed, scales, y, M, N, K, ScratchSrc{(hipStream_t)hip_stream, true});
 }
 
 const char *qstatus_str(qw3_status status) {
@@ -3327,6 +3363,7 @@ const char *qstatus_str(qw3_status status) {
         case QW3_ERR_ALIGN: return "misaligned pointer (x/packed/codes/w_out need 16 bytes)";
         case QW3_ERR_HIP: return "HIP runtime error (see qw3_last_hip_error)";
         case QW3_ERR_CAPTURE: return "the stream's workspace would have to grow during graph capture";
+        case QW3_ERR_SCRATCH: return "the call needs more than the static scratch (QW3_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }

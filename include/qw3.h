@@ -65,8 +65,10 @@ enum {
     QW3_ERR_SHAPE = -2, /* negative size, K % 128 != 0, or K > QW3_MAX_K      */
     QW3_ERR_ALIGN = -3, /* a pointer is not aligned as stated above           */
     QW3_ERR_HIP = -4,   /* the HIP runtime reported an error                  */
-    QW3_ERR_CAPTURE = -5  /* qgemm_w3g128_smallM would have to allocate its
+    QW3_ERR_CAPTURE = -5, /* qgemm_w3g128_smallM would have to allocate its
                              workspace while the stream is being captured      */
+    QW3_ERR_SCRATCH = -6  /* qgemm_w3g128_smallM_noalloc needs more than
+                             QW3_NOALLOC_SCRATCH_BYTES of scratch               */
 };
 
 /* Largest supported in_features (1024 groups of 128). */
@@ -180,6 +182,33 @@ qw3_status qgemv_w3g128_multi(const uint16_t *x, int32_t count, const int32_t *c
 qw3_status qgemm_w3g128_smallM(const uint16_t *x, const int32_t *packed,
                                const uint16_t *scales, float *y, int64_t M, int64_t N,
                                int64_t K, void *hip_stream);
+
+/* Device scratch of qgemm_w3g128_smallM_noalloc, per device (128 MiB). */
+#define QW3_NOALLOC_SCRATCH_BYTES (128ull << 20)
+
+/*
+ * qgemm_w3g128_smallM_noalloc -- qgemm_w3g128_smallM for callers that cannot
+ * allocate device memory: code under graph capture that has not sized a
+ * workspace, tight serving loops, harnesses that forbid hipMalloc.
+ *   Same arguments, layout, validation, accuracy and results as
+ *   qgemm_w3g128_smallM (the same kernels; bit-identical outputs).
+ *   Scratch comes from a static device array of QW3_NOALLOC_SCRATCH_BYTES
+ *   that the library holds on every device it runs on until the process
+ *   ends; the call itself never allocates, frees or synchronizes.  A call
+ *   that needs more scratch returns QW3_ERR_SCRATCH and enqueues nothing.
+ *   Needs, in bytes (Mp = M rounded up to 16 or 32 per batched pass, or to
+ *   whole 128- or 256-token tiles; G = K / 128; C = K chunks):
+ *     batched decode  2 Mp K + 5 G Mp + 4 C Mp N   (about 9 MiB for 32 tokens
+ *                     against either MLP matrix of a 70B layer);
+ *     prefill         2 Mp K + 4 Mp (G + 2) + 4 C M N  (about 97 MiB for 512
+ *                     tokens against an 8192 x 28672 matrix).
+ *   All calls on one device share the array: calls that overlap in time on
+ *   one device (different streams, or graph replays) race and must be
+ *   ordered by the caller.
+ */
+qw3_status qgemm_w3g128_smallM_noalloc(const uint16_t *x, const int32_t *packed,
+                                       const uint16_t *scales, float *y, int64_t M, int64_t N,
+                                       int64_t K, void *hip_stream);
 
 /* Text for a status code (static storage, never NULL). */
 const char *qstatus_str(qw3_status status);

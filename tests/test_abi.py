@@ -40,7 +40,8 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     assert q.raw().qw3_abi_version() == 1
-    for st in (q.QW3_OK, q.QW3_ERR_NULL, q.QW3_ERR_SHAPE, q.QW3_ERR_ALIGN, q.QW3_ERR_HIP, q.QW3_ERR_CAPTURE):
+    for st in (q.QW3_OK, q.QW3_ERR_NULL, q.QW3_ERR_SHAPE, q.QW3_ERR_ALIGN, q.QW3_ERR_HIP, q.QW3_ERR_CAPTURE,
+               q.QW3_ERR_SCRATCH):
         assert q.qstatus_str(st)
     assert q.qstatus_str(12345) == "unknown status"
 
@@ -64,10 +65,12 @@ def test_bad_shapes(n, k):
     assert lib.qdequant_bf16(A16, A16B, A16C, n, k, S) == q.QW3_ERR_SHAPE
     assert lib.qgemv_w3g128(A16, A16B, A16C, A16D, n, k, S) == q.QW3_ERR_SHAPE
     assert lib.qgemm_w3g128_smallM(A16, A16B, A16C, A16D, 2, n, k, S) == q.QW3_ERR_SHAPE
+    assert lib.qgemm_w3g128_smallM_noalloc(A16, A16B, A16C, A16D, 2, n, k, S) == q.QW3_ERR_SHAPE
 
 
 def test_bad_m():
     assert q.raw().qgemm_w3g128_smallM(A16, A16B, A16C, A16D, -1, 4, 128, S) == q.QW3_ERR_SHAPE
+    assert q.raw().qgemm_w3g128_smallM_noalloc(A16, A16B, A16C, A16D, -1, 4, 128, S) == q.QW3_ERR_SHAPE
 
 
 def test_null_pointers():
@@ -84,6 +87,7 @@ def test_null_pointers():
         args[i] = NULL
         assert lib.qgemv_w3g128(*args, 4, 128, S) == q.QW3_ERR_NULL
         assert lib.qgemm_w3g128_smallM(*args, 3, 4, 128, S) == q.QW3_ERR_NULL
+        assert lib.qgemm_w3g128_smallM_noalloc(*args, 3, 4, 128, S) == q.QW3_ERR_NULL
 
 
 def test_misaligned_pointers():
@@ -100,6 +104,7 @@ def test_misaligned_pointers():
     assert lib.qgemv_w3g128(A16, A16B, ODD, A16D, 4, 128, S) == q.QW3_ERR_ALIGN
     assert lib.qgemv_w3g128(A16, A16B, A16C, ctypes.c_void_p(0x40002), 4, 128, S) == q.QW3_ERR_ALIGN
     assert lib.qgemm_w3g128_smallM(MIS, A16B, A16C, A16D, 3, 4, 128, S) == q.QW3_ERR_ALIGN
+    assert lib.qgemm_w3g128_smallM_noalloc(MIS, A16B, A16C, A16D, 3, 4, 128, S) == q.QW3_ERR_ALIGN
 
 
 def test_empty_sizes_enqueue_nothing():
@@ -110,7 +115,9 @@ def test_empty_sizes_enqueue_nothing():
     assert lib.qdequant_bf16(NULL, NULL, NULL, 0, 1024, S) == q.QW3_OK
     assert lib.qgemv_w3g128(NULL, NULL, NULL, NULL, 0, 1024, S) == q.QW3_OK
     assert lib.qgemm_w3g128_smallM(NULL, NULL, NULL, NULL, 0, 5, 1024, S) == q.QW3_OK
+    assert lib.qgemm_w3g128_smallM_noalloc(NULL, NULL, NULL, NULL, 0, 5, 1024, S) == q.QW3_OK
     assert lib.qgemm_w3g128_smallM(NULL, NULL, NULL, NULL, 5, 0, 1024, S) == q.QW3_OK
+    assert lib.qgemm_w3g128_smallM_noalloc(NULL, NULL, NULL, NULL, 5, 0, 1024, S) == q.QW3_OK
 
 
 def test_quantization_config_descriptor():
