@@ -13,11 +13,14 @@ copies exceed twice the 256 MB Infinity Cache; each step reads a copy that
 is not cache resident.  Steps are timed with HIP events recorded on the stream
 the kernels are launched on.
 
-Prints ONE JSON line on stdout.  `--extra` also measures the other workloads
-(the full layer at batch 1, batched decode M = 4..32, prefill M = 512) and
-prints them as JSON lines on stderr; the batch-1 projections there are timed
-per call inside a replayed HIP graph, since a host launch costs more than the
-smaller ones take to run.
+Prints ONE JSON line on stdout.  Unless --no-summary, the other workloads
+follow on stderr, one JSON line each: the full 70B decoder layer at batch 1
+(per-layer us and aggregate GB/s, 7 launches and with q/k/v and gate/up fused),
+batched decode M = 4..32 and prefill M = 512 on gate_proj and down_proj --
+each as device time per call from a replayed HIP graph (a host launch costs
+more than the smaller projections take to run) with back-to-back stream
+launches beside it.  `--extra` adds the dense branch at M = 512 and the
+oracle's host rates; `--case NAME:M` times one workload alone.
 """
 from __future__ import annotations
 
@@ -164,13 +167,90 @@ def graph_time(torch, fn, reps: int, replays: int, warmup: int):
     side.wait_stream(torch.cuda.current_stream())
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.stream(side):
-        fn(0)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(graph):
-            for i in range(reps):
-                fn(i)
+        fn(0)  # sizes the library's workspace for this stream before capture
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=side):
+        for i in range(reps):
+            fn(i)
     torch.cuda.synchronize()
     return time_steps(torch, lambda i: graph.replay(), replays, warmup) / reps
+
+
+def workload_summary(torch, q, steps):
+    """The other workloads of the benchmark on stderr, one JSON line each:
+    the 70B decoder layer at batch 1 (7 projections, and the same layer with
+    q/k/v and gate/up each fused into one launch), batched decode M = 4..32
+    and prefill M = 512 on gate_proj and down_proj.  Device time per call
+    from a replayed HIP graph (host launch cost excluded), and the time of
+    back-to-back stream launches beside it."""
+    import synth
+    kept = {}
+    layer = {}
+    total_bytes, total_ms = 0, 0.0
+    lines = []
+    for name in ("q_proj", "k_proj", "v_proj", "o_proj", "gate_proj", "up_proj", "down_proj"):
+        _, _, packed, scales = make_weight(torch, q, name)
+        n, k = synth.LAYER_70B[name][:2]
+        rot = Rotation(torch, packed, scales)
+        del packed, scales
+        kept[name] = (rot, n, k)
+        xd = torch.from_numpy(synth.layer_x(1, k).reshape(-1).view(np.int16)).cuda()
+        y = torch.empty(n, dtype=torch.float32, device="cuda")
+        fn = lambda i: q.qgemv_w3g128(xd, rot[i][0], rot[i][1], out=y)  # noqa: E731
+        ms_launch = time_steps(torch, fn, steps, max(10, steps // 10))
+        ms = graph_time(torch, fn, 20, max(10, steps // 20), 3)
+        b = gemv_bytes(n, k)
+        layer[name] = {"us": round(ms * 1e3, 3), "GB/s": round(b / ms / 1e6, 1), "bytes": b,
+                       "us_stream_launches": round(ms_launch * 1e3, 3)}
+        total_bytes += b
+        total_ms += ms
+        if name in ("gate_proj", "down_proj"):
+            for m in (4, 8, 16, 32, 512):
+                xm = torch.from_numpy(synth.layer_x(m, k).view(np.int16)).cuda()
+                ym = torch.empty((m, n), dtype=torch.float32, device="cuda")
+                fm = lambda i: q.qgemm_w3g128_smallM(xm, rot[i][0], rot[i][1], out=ym)  # noqa: E731
+                st = max(20, steps // (8 if m == 512 else 2))
+                ms_l = time_steps(torch, fm, st, 5)
+                ms_g = graph_time(torch, fm, 4 if m == 512 else 20, max(5, st // 20), 2)
+                bm = gemv_bytes(n, k, m)
+                tf = 2.0 * m * n * k / ms_g / 1e9
+                lines.append({"workload": "%s [%d, %d] M=%d" % (name, n, k, m), "us": round(ms_g * 1e3, 3),
+                              "GB/s": round(bm / ms_g / 1e6, 1), "HBM_frac": round(bm / ms_g / 1e6 / HBM_PEAK_GBS, 4),
+                              "TFLOP/s": round(tf, 2), "MFMA_frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                              "us_stream_launches": round(ms_l * 1e3, 3), "algorithmic_bytes": bm})
+    x1 = torch.from_numpy(synth.layer_x(1, 8192).reshape(-1).view(np.int16)).cuda()
+    x2 = torch.from_numpy(synth.layer_x(1, 28672).reshape(-1).view(np.int16)).cuda()
+    ys = {nm: torch.empty(kept[nm][1], dtype=torch.float32, device="cuda") for nm in kept}
+
+    def one_by_one(i):
+        for nm in ("q_proj", "k_proj", "v_proj", "o_proj", "gate_proj", "up_proj", "down_proj"):
+            r = kept[nm][0][i]
+            q.qgemv_w3g128(x2 if nm == "down_proj" else x1, r[0], r[1], out=ys[nm])
+
+    def fused(i):
+        r = {nm: kept[nm][0][i] for nm in kept}
+        q.qgemv_w3g128_multi(x1, [r["q_proj"], r["k_proj"], r["v_proj"]],
+                             outs=[ys["q_proj"], ys["k_proj"], ys["v_proj"]])
+        q.qgemv_w3g128(x1, r["o_proj"][0], r["o_proj"][1], out=ys["o_proj"])
+        q.qgemv_w3g128_multi(x1, [r["gate_proj"], r["up_proj"]], outs=[ys["gate_proj"], ys["up_proj"]])
+        q.qgemv_w3g128(x2, r["down_proj"][0], r["down_proj"][1], out=ys["down_proj"])
+
+    layer_ms = graph_time(torch, one_by_one, 8, max(10, steps // 20), 3)
+    fused_ms = graph_time(torch, fused, 8, max(10, steps // 20), 3)
+    lines.insert(0, {"workload": "Llama-3.1-70B decoder layer at B=1: q/o [8192, 8192], k/v [1024, 8192], "
+                                 "gate/up [28672, 8192], down [8192, 28672] (device time, graph replay)",
+                     "layer_bytes": total_bytes,
+                     "layer_us": round(layer_ms * 1e3, 3), "layer_GB/s": round(total_bytes / layer_ms / 1e6, 1),
+                     "layer_HBM_frac": round(total_bytes / layer_ms / 1e6 / HBM_PEAK_GBS, 4),
+                     "fused_layer_us": round(fused_ms * 1e3, 3),
+                     "fused_layer_GB/s": round(total_bytes / fused_ms / 1e6, 1),
+                     "fused_layer_HBM_frac": round(total_bytes / fused_ms / 1e6 / HBM_PEAK_GBS, 4),
+                     "fused_layer_launches": "q/k/v in one qgemv_w3g128_multi, o, gate/up in one, down",
+                     "per_projection": layer, "per_projection_us_sum": round(total_ms * 1e3, 3)})
+    del kept, ys
+    torch.cuda.empty_cache()
+    for rec in lines:
+        print(json.dumps(rec), file=sys.stderr, flush=True)
 
 
 def bench_extra(torch, q, steps, warmup):
@@ -360,11 +440,14 @@ def run_case(torch, q, case: str, steps: int, warmup: int):
         y = torch.empty((m, n), dtype=torch.float32, device="cuda")
         fn = lambda i: q.qgemm_w3g128_smallM(x, rot[i][0], rot[i][1], out=y)  # noqa: E731
     ms = time_steps(torch, fn, steps, warmup)
+    ms_g = graph_time(torch, fn, 4 if m >= 128 else 20, max(5, steps // 20), 2)
     b = gemv_bytes(n, k, m)
     tf = 2.0 * m * n * k / ms / 1e9
     print(json.dumps({"workload": "%s [%d, %d] M=%d" % (name, n, k, m), "steps": steps, "us": round(ms * 1e3, 3),
                       "GB/s": round(b / ms / 1e6, 1), "HBM_frac": round(b / ms / 1e6 / HBM_PEAK_GBS, 4),
                       "TFLOP/s": round(tf, 2), "MFMA_frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                      "us_graph_replay": round(ms_g * 1e3, 3),
+                      "HBM_frac_graph_replay": round(b / ms_g / 1e6 / HBM_PEAK_GBS, 4),
                       "algorithmic_bytes": b}), flush=True)
 
 
@@ -375,6 +458,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--extra", action="store_true", help="also time layer / batched / prefill workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-summary", action="store_true",
+                    help="skip the other workloads' lines (layer, batched decode, prefill) on stderr")
     ap.add_argument("--calibrate", action="store_true",
                     help="first run 5 plain 256 MiB device copies (torch copy_), the known-size "
                          "reference for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE counters")
@@ -451,9 +536,11 @@ def main():
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(c, s, x, k)
+    rot = packed = scales = None  # free the rotated copies before the other workloads
+    torch.cuda.empty_cache()
+    if not args.no_summary:
+        workload_summary(torch, q, max(200, args.steps))
     if args.extra:
-        del rot, packed, scales
-        torch.cuda.empty_cache()
         bench_extra(torch, q, max(50, args.steps // 4), max(10, args.warmup // 4))
     print(json.dumps(line), flush=True)
 
