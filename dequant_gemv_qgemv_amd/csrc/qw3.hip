@@ -3081,9 +3081,10 @@ qw3_status launch_gemm_mt(const uint16_t *x, const uint32_t *packed, const uint1
     const bool ring = TS == 2 || aligned(scales, 8);
     constexpr int Mp = 16 * TS;
     const int C = G / ((8 / TS) * WAVES);
-    // Up to 6 tokens: the ring kernel converts the activations itself (at 8
-    // it measured the same as the conversion launch).
-    const bool xh = ring && TS == 1 && M <= 6;
+    // Up to 8 tokens the ring kernel converts the activations itself (at 8,
+    // about 1 us faster than the conversion launch in front of it; at 16
+    // tokens, with one token per lane, about 1.5 us slower).
+    const bool xh = ring && TS == 1 && M <= 8;
     Carve cv;
     const size_t xq_at = cv.take(xh ? 0 : (size_t)Mp * (size_t)K * 2);
     const size_t xe_at = cv.take(xh ? 0 : (size_t)(G / 8) * Mp * sizeof(int16_t));

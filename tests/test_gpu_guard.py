@@ -118,8 +118,8 @@ def test_guard_batch1(kind, n, k):
 
 
 # batched decode: four-token kernel (K = 8192 one chunk, 28672 four), the ring
-# kernel converting in-kernel (5, 6 tokens) or after a conversion launch (8,
-# 16), 17..32 tokens in one pass, and the generic kernel (K / 128 = 8)
+# kernel converting in-kernel (5..8 tokens) or after a conversion launch
+# (16), 17..32 tokens in one pass, and the generic kernel (K / 128 = 8)
 @pytest.mark.parametrize("kind", ["x", "s"])
 @pytest.mark.parametrize("m", [2, 3, 4, 5, 6, 8, 16, 17, 32])
 @pytest.mark.parametrize("n,k", [(128, 8192), (48, 28672), (64, 1024)])
