@@ -176,6 +176,34 @@ def graph_time(torch, fn, reps: int, replays: int, warmup: int):
     return time_steps(torch, lambda i: graph.replay(), replays, warmup) / reps
 
 
+LAYER_ORDER = ("q_proj", "k_proj", "v_proj", "o_proj", "gate_proj", "up_proj", "down_proj")
+
+
+def layer_calls(torch, q, kept):
+    """The 70B decoder layer at batch 1 over rotated weights kept[name] =
+    (Rotation, N, K): one_by_one(i) makes the 7 qgemv_w3g128 calls, fused(i)
+    the same work in 4 launches (q/k/v and gate/up through qgemv_w3g128_multi)."""
+    import synth
+    x1 = torch.from_numpy(synth.layer_x(1, 8192).reshape(-1).view(np.int16)).cuda()
+    x2 = torch.from_numpy(synth.layer_x(1, 28672).reshape(-1).view(np.int16)).cuda()
+    ys = {nm: torch.empty(kept[nm][1], dtype=torch.float32, device="cuda") for nm in kept}
+
+    def one_by_one(i):
+        for nm in LAYER_ORDER:
+            r = kept[nm][0][i]
+            q.qgemv_w3g128(x2 if nm == "down_proj" else x1, r[0], r[1], out=ys[nm])
+
+    def fused(i):
+        r = {nm: kept[nm][0][i] for nm in kept}
+        q.qgemv_w3g128_multi(x1, [r["q_proj"], r["k_proj"], r["v_proj"]],
+                             outs=[ys["q_proj"], ys["k_proj"], ys["v_proj"]])
+        q.qgemv_w3g128(x1, r["o_proj"][0], r["o_proj"][1], out=ys["o_proj"])
+        q.qgemv_w3g128_multi(x1, [r["gate_proj"], r["up_proj"]], outs=[ys["gate_proj"], ys["up_proj"]])
+        q.qgemv_w3g128(x2, r["down_proj"][0], r["down_proj"][1], out=ys["down_proj"])
+
+    return one_by_one, fused, ys
+
+
 def workload_summary(torch, q, steps):
     """The other workloads of the benchmark on stderr, one JSON line each:
     the 70B decoder layer at batch 1 (7 projections, and the same layer with
@@ -188,7 +216,7 @@ def workload_summary(torch, q, steps):
     layer = {}
     total_bytes, total_ms = 0, 0.0
     lines = []
-    for name in ("q_proj", "k_proj", "v_proj", "o_proj", "gate_proj", "up_proj", "down_proj"):
+    for name in LAYER_ORDER:
         _, _, packed, scales = make_weight(torch, q, name)
         n, k = synth.LAYER_70B[name][:2]
         rot = Rotation(torch, packed, scales)
@@ -218,23 +246,7 @@ def workload_summary(torch, q, steps):
                               "GB/s": round(bm / ms_g / 1e6, 1), "HBM_frac": round(bm / ms_g / 1e6 / HBM_PEAK_GBS, 4),
                               "TFLOP/s": round(tf, 2), "MFMA_frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
                               "us_stream_launches": round(ms_l * 1e3, 3), "algorithmic_bytes": bm})
-    x1 = torch.from_numpy(synth.layer_x(1, 8192).reshape(-1).view(np.int16)).cuda()
-    x2 = torch.from_numpy(synth.layer_x(1, 28672).reshape(-1).view(np.int16)).cuda()
-    ys = {nm: torch.empty(kept[nm][1], dtype=torch.float32, device="cuda") for nm in kept}
-
-    def one_by_one(i):
-        for nm in ("q_proj", "k_proj", "v_proj", "o_proj", "gate_proj", "up_proj", "down_proj"):
-            r = kept[nm][0][i]
-            q.qgemv_w3g128(x2 if nm == "down_proj" else x1, r[0], r[1], out=ys[nm])
-
-    def fused(i):
-        r = {nm: kept[nm][0][i] for nm in kept}
-        q.qgemv_w3g128_multi(x1, [r["q_proj"], r["k_proj"], r["v_proj"]],
-                             outs=[ys["q_proj"], ys["k_proj"], ys["v_proj"]])
-        q.qgemv_w3g128(x1, r["o_proj"][0], r["o_proj"][1], out=ys["o_proj"])
-        q.qgemv_w3g128_multi(x1, [r["gate_proj"], r["up_proj"]], outs=[ys["gate_proj"], ys["up_proj"]])
-        q.qgemv_w3g128(x2, r["down_proj"][0], r["down_proj"][1], out=ys["down_proj"])
-
+    one_by_one, fused, ys = layer_calls(torch, q, kept)
     layer_ms = graph_time(torch, one_by_one, 8, max(10, steps // 20), 3)
     fused_ms = graph_time(torch, fused, 8, max(10, steps // 20), 3)
     lines.insert(0, {"workload": "Llama-3.1-70B decoder layer at B=1: q/o [8192, 8192], k/v [1024, 8192], "
@@ -420,13 +432,39 @@ def read_copy_ceiling(torch):
     del src, dst
 
 
+def run_layer_case(torch, q, fused: bool, steps: int):
+    """The whole 70B decoder layer at batch 1 (7 launches, or 4 with q/k/v and
+    gate/up fused), device time per layer from a replayed HIP graph."""
+    import synth
+    kept = {}
+    total = 0
+    for name in LAYER_ORDER:
+        _, _, packed, scales = make_weight(torch, q, name)
+        n, k = synth.LAYER_70B[name][:2]
+        kept[name] = (Rotation(torch, packed, scales), n, k)
+        total += gemv_bytes(n, k)
+        del packed, scales
+    one_by_one, fused_fn, _ = layer_calls(torch, q, kept)
+    fn = fused_fn if fused else one_by_one
+    ms = graph_time(torch, fn, 8, max(10, steps // 8), 3)
+    print(json.dumps({"workload": "Llama-3.1-70B decoder layer at B=1, %s (device time, graph replay)"
+                      % ("4 launches: q/k/v and gate/up fused" if fused else "7 launches"),
+                      "layer_bytes": total, "layer_us": round(ms * 1e3, 3),
+                      "layer_GB/s": round(total / ms / 1e6, 1),
+                      "layer_HBM_frac": round(total / ms / 1e6 / HBM_PEAK_GBS, 4)}), flush=True)
+
+
 def run_case(torch, q, case: str, steps: int, warmup: int):
-    """One projection of the 70B layer at M rows of activations, stream launches."""
+    """One projection of the 70B layer at M rows of activations, stream launches
+    (layer:1 and layer_fused:1: the whole layer at batch 1)."""
     import synth
     name, m = case.split(":")
     m = int(m)
+    if name in ("layer", "layer_fused") and m == 1:
+        return run_layer_case(torch, q, name == "layer_fused", steps)
     if name not in synth.LAYER_70B or m < 1:
-        raise SystemExit("--case wants NAME:M with NAME one of %s" % ", ".join(synth.LAYER_70B))
+        raise SystemExit("--case wants NAME:M with NAME one of %s, or layer:1 / layer_fused:1"
+                         % ", ".join(synth.LAYER_70B))
     c, s, packed, scales = make_weight(torch, q, name)
     n, k = c.shape
     del c, s
@@ -451,6 +489,57 @@ def run_case(torch, q, case: str, steps: int, warmup: int):
                       "algorithmic_bytes": b}), flush=True)
 
 
+def traffic_from_counters(fetch_csv: str, write_csv: str, out_path: str = TRAFFIC_FILE) -> dict:
+    """Summarise two rocprofv3 counter runs of `bench.py --calibrate` (one with
+    --pmc FETCH_SIZE, one with --pmc WRITE_SIZE) into HBM bytes per launch of
+    the default workload's kernel.  Both counters report KiB per dispatch; the
+    calibration copies (5 x 256 MiB read and written, the largest copy
+    dispatches of the run) give the factor from counter to bytes.  Writes the
+    record, keyed by the kernel source hash, to out_path."""
+    import csv
+    kernel = "qgemv_mfma_kernel<16, 4, false>"
+    copy_bytes, copies = 256 * 2 ** 20, 5
+
+    def per_kernel(path, counter):
+        vals, cps = [], []
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                v = float(r["Counter_Value"])
+                if kernel in r["Kernel_Name"]:
+                    vals.append(v)
+                elif "copyBuffer" in r["Kernel_Name"] or "copy" in r["Kernel_Name"].lower():
+                    cps.append(v)
+        if not vals or len(cps) < copies:
+            raise SystemExit("%s: %d dispatches of %s, %d copy dispatches" % (path, len(vals), kernel, len(cps)))
+        cal = sorted(cps)[-copies:]
+        return sum(vals) / len(vals), sum(cal) / len(cal), len(vals)
+
+    f_k, f_cal, nd = per_kernel(fetch_csv, "FETCH_SIZE")
+    w_k, w_cal, _ = per_kernel(write_csv, "WRITE_SIZE")
+    fs, ws = copy_bytes / (f_cal * 1024), copy_bytes / (w_cal * 1024)
+    rd, wr = int(round(f_k * 1024 * fs)), int(round(w_k * 1024 * ws))
+    alg = gemv_bytes(28672, 8192)
+    rec = {"kernel": kernel, "workload": "gate_proj W3G128 GEMV [28672, 8192], batch 1",
+           "kernel_source_sha256_16": kernel_source_hash(), "fetch_size_kib_raw": round(f_k, 2),
+           "write_size_kib_raw": round(w_k, 2), "calibration_copy_bytes": copy_bytes,
+           "calibration_copies": copies, "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
+           "hbm_read_bytes_per_launch": rd, "hbm_write_bytes_per_launch": wr, "hbm_bytes_per_launch": rd + wr,
+           "algorithmic_bytes_per_launch": alg, "traffic_over_algorithmic": round((rd + wr) / alg, 4),
+           "dispatches_averaged": nd,
+           "commands": ["rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- "
+                        "python3 bench.py --steps 10 --warmup 2 --no-cpu-baseline --no-summary --calibrate",
+                        "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- "
+                        "python3 bench.py --steps 10 --warmup 2 --no-cpu-baseline --no-summary --calibrate",
+                        "python3 bench.py --traffic-from gpurun_out/pmc_fetch/run_counter_collection.csv "
+                        "gpurun_out/pmc_write/run_counter_collection.csv"]}
+    with open(out_path, "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -466,10 +555,16 @@ def main():
     ap.add_argument("--ceiling", action="store_true",
                     help="also time a plain 1 GiB device copy and a streaming-read kernel and print "
                          "their GB/s on stderr")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarise two rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE) of --calibrate into "
+                         "the committed traffic record and exit (no GPU needed)")
     ap.add_argument("--case", metavar="NAME:M",
-                    help="time one other workload instead of the default line, e.g. gate_proj:16 or "
-                         "down_proj:512 (for profiling); prints its JSON line on stdout")
+                    help="time one other workload instead of the default line, e.g. gate_proj:16, "
+                         "down_proj:512 or layer:1 / layer_fused:1 (for profiling); prints its JSON line on stdout")
     args = ap.parse_args()
+    if args.traffic_from:
+        print(json.dumps(traffic_from_counters(*args.traffic_from)))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
