@@ -462,9 +462,22 @@ def run_case(torch, q, case: str, steps: int, warmup: int):
     m = int(m)
     if name in ("layer", "layer_fused") and m == 1:
         return run_layer_case(torch, q, name == "layer_fused", steps)
+    if name.endswith("_dense") and name[:-6] in synth.LAYER_70B and m == 512:
+        # the unfused prefill (qdequant_bf16, then a library bf16 GEMM) beside the fused kernel
+        base = name[:-6]
+        _, _, packed, scales = make_weight(torch, q, base)
+        n, k = synth.LAYER_70B[base][:2]
+        rot = Rotation(torch, packed, scales)
+        del packed, scales
+        xm = torch.from_numpy(synth.layer_x(m, k).view(np.int16)).cuda()
+        ym = torch.empty((m, n), dtype=torch.float32, device="cuda")
+        fused = time_steps(torch, lambda i: q.qgemm_w3g128_smallM(xm, rot[i][0], rot[i][1], out=ym),
+                           max(10, steps // 8), max(2, warmup // 4))
+        print(json.dumps(dense_branch(torch, q, base, n, k, rot, fused)), flush=True)
+        return
     if name not in synth.LAYER_70B or m < 1:
-        raise SystemExit("--case wants NAME:M with NAME one of %s, or layer:1 / layer_fused:1"
-                         % ", ".join(synth.LAYER_70B))
+        raise SystemExit("--case wants NAME:M with NAME one of %s, or layer:1 / layer_fused:1, "
+                         "or NAME_dense:512" % ", ".join(synth.LAYER_70B))
     c, s, packed, scales = make_weight(torch, q, name)
     n, k = c.shape
     del c, s
@@ -560,7 +573,8 @@ def main():
                          "the committed traffic record and exit (no GPU needed)")
     ap.add_argument("--case", metavar="NAME:M",
                     help="time one other workload instead of the default line, e.g. gate_proj:16, "
-                         "down_proj:512 or layer:1 / layer_fused:1 (for profiling); prints its JSON line on stdout")
+                         "down_proj:512, layer:1 / layer_fused:1 or gate_proj_dense:512 (the dequantize-then-GEMM "
+                         "prefill beside the fused one) (for profiling); prints its JSON line on stdout")
     args = ap.parse_args()
     if args.traffic_from:
         print(json.dumps(traffic_from_counters(*args.traffic_from)))
