@@ -475,15 +475,21 @@ def run_case(torch, q, case: str, steps: int, warmup: int):
                            max(10, steps // 8), max(2, warmup // 4))
         print(json.dumps(dense_branch(torch, q, base, n, k, rot, fused)), flush=True)
         return
+    invariant = name.endswith("_bi") and name[:-3] in synth.LAYER_70B
+    if invariant:
+        name = name[:-3]
     if name not in synth.LAYER_70B or m < 1:
         raise SystemExit("--case wants NAME:M with NAME one of %s, or layer:1 / layer_fused:1, "
-                         "or NAME_dense:512" % ", ".join(synth.LAYER_70B))
+                         "NAME_dense:512 or NAME_bi:M" % ", ".join(synth.LAYER_70B))
     c, s, packed, scales = make_weight(torch, q, name)
     n, k = c.shape
     del c, s
     rot = Rotation(torch, packed, scales)
     x = torch.from_numpy(synth.layer_x(m, k).view(np.int16)).cuda()
-    if m == 1:
+    if invariant:  # rows bit-identical to the batch-1 product, the weights read once per row
+        y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+        fn = lambda i: q.qgemm_w3g128_batch_invariant(x, rot[i][0], rot[i][1], out=y)  # noqa: E731
+    elif m == 1:
         x = x.reshape(-1)
         y = torch.empty(n, dtype=torch.float32, device="cuda")
         fn = lambda i: q.qgemv_w3g128(x, rot[i][0], rot[i][1], out=y)  # noqa: E731
@@ -494,7 +500,8 @@ def run_case(torch, q, case: str, steps: int, warmup: int):
     ms_g = graph_time(torch, fn, 4 if m >= 128 else 20, max(5, steps // 20), 2)
     b = gemv_bytes(n, k, m)
     tf = 2.0 * m * n * k / ms / 1e9
-    print(json.dumps({"workload": "%s [%d, %d] M=%d" % (name, n, k, m), "steps": steps, "us": round(ms * 1e3, 3),
+    what = "%s [%d, %d] M=%d%s" % (name, n, k, m, ", batch-invariant (batch-1 kernel per row)" if invariant else "")
+    print(json.dumps({"workload": what, "steps": steps, "us": round(ms * 1e3, 3),
                       "GB/s": round(b / ms / 1e6, 1), "HBM_frac": round(b / ms / 1e6 / HBM_PEAK_GBS, 4),
                       "TFLOP/s": round(tf, 2), "MFMA_frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
                       "us_graph_replay": round(ms_g * 1e3, 3),
@@ -573,8 +580,9 @@ def main():
                          "the committed traffic record and exit (no GPU needed)")
     ap.add_argument("--case", metavar="NAME:M",
                     help="time one other workload instead of the default line, e.g. gate_proj:16, "
-                         "down_proj:512, layer:1 / layer_fused:1 or gate_proj_dense:512 (the dequantize-then-GEMM "
-                         "prefill beside the fused one) (for profiling); prints its JSON line on stdout")
+                         "down_proj:512, layer:1 / layer_fused:1, gate_proj_dense:512 (the dequantize-then-GEMM "
+                         "prefill beside the fused one) or gate_proj_bi:8 (the batch-invariant product) (for "
+                         "profiling); prints its JSON line on stdout")
     args = ap.parse_args()
     if args.traffic_from:
         print(json.dumps(traffic_from_counters(*args.traffic_from)))

@@ -42,18 +42,21 @@ __all__ = [
     "QW3_NOALLOC_SCRATCH_BYTES",
     "QW3_MAX_K",
     "QW3_MAX_MULTI",
+    "QW3_MAX_BATCH_INVARIANT_M",
 ]
 
 QW3_OK, QW3_ERR_NULL, QW3_ERR_SHAPE, QW3_ERR_ALIGN, QW3_ERR_HIP, QW3_ERR_CAPTURE, QW3_ERR_SCRATCH = 0, -1, -2, -3, -4, -5, -6
 QW3_NOALLOC_SCRATCH_BYTES = 128 << 20
 QW3_MAX_K = 131072
 QW3_MAX_MULTI = 4
+QW3_MAX_BATCH_INVARIANT_M = 65535
 GROUP = 128
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libqw3.so")
 _EXPORTS = ("qpack_uint3", "qrepack_w4c_uint3", "qdequant_bf16", "qgemv_w3g128", "qgemv_w3g128_multi",
-            "qgemm_w3g128_smallM", "qgemm_w3g128_smallM_noalloc", "qstatus_str", "qw3_last_hip_error",
+            "qgemm_w3g128_smallM", "qgemm_w3g128_smallM_noalloc", "qgemm_w3g128_batch_invariant", "qstatus_str",
+            "qw3_last_hip_error",
             "qw3_abi_version")
 
 if not os.path.exists(_LIB_PATH):
@@ -69,6 +72,7 @@ _lib.qdequant_bf16.argtypes = [_vp, _vp, _vp, _i64, _i64, _vp]
 _lib.qgemv_w3g128.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _vp]
 _lib.qgemm_w3g128_smallM.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]
 _lib.qgemm_w3g128_smallM_noalloc.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]
+_lib.qgemm_w3g128_batch_invariant.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]
 _lib.qgemv_w3g128_multi.argtypes = [_vp, ctypes.c_int32, _vp, _vp, _vp, _vp, _i64, _vp]
 for _name in ("qpack_uint3", "qrepack_w4c_uint3", "qdequant_bf16", "qgemv_w3g128", "qgemv_w3g128_multi",
               "qgemm_w3g128_smallM", "qgemm_w3g128_smallM_noalloc"):
@@ -293,6 +297,26 @@ def qgemm_w3g128_smallM_noalloc(x: torch.Tensor, packed: torch.Tensor, scales: t
     with torch.cuda.device(packed.device):
         _check(_lib.qgemm_w3g128_smallM_noalloc(_ptr(x), _ptr(packed), _ptr(scales), _ptr(out), m, n, k,
                                                 _stream()), "qgemm_w3g128_smallM_noalloc")
+    return out
+
+
+def qgemm_w3g128_batch_invariant(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
+                                 out: torch.Tensor | None = None) -> torch.Tensor:
+    """Y[M, N] = X dequant(W)^T with row m bit-identical to qgemv_w3g128(X[m]);
+    reads the weights once per row of X."""
+    n, k = _check_weight(packed, scales)
+    _need(x, "x", _BF16, 2)
+    m = x.shape[0]
+    if x.shape[1] != k or x.device != packed.device:
+        raise ValueError("x must be [M, %d] on %s" % (k, packed.device))
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=packed.device)
+    _need(out, "out", (torch.float32,), 2)
+    if tuple(out.shape) != (m, n) or out.device != packed.device:
+        raise ValueError("out must be [%d, %d] on %s" % (m, n, packed.device))
+    with torch.cuda.device(packed.device):
+        _check(_lib.qgemm_w3g128_batch_invariant(_ptr(x), _ptr(packed), _ptr(scales), _ptr(out), m, n, k,
+                                                 _stream()), "qgemm_w3g128_batch_invariant")
     return out
 
 

@@ -814,6 +814,7 @@ __global__ __launch_bounds__(kGemvWGS) void qgemv_small_kernel(const uint16_t *_
                                                                const GemvSegs sg, int G) {
     constexpr int R = kGemvWGS / T;
     extern __shared__ uint32_t smem[];
+    x += (int64_t)blockIdx.y * G * kGroup;  // token blockIdx.y (one token unless batch-invariant)
     float *xd = reinterpret_cast<float *>(smem + (size_t)G * 65);
     uint32_t *flags = smem + (size_t)G * 66;
     int *nz = reinterpret_cast<int *>(flags + 16);
@@ -829,8 +830,8 @@ __global__ __launch_bounds__(kGemvWGS) void qgemv_small_kernel(const uint16_t *_
     }
     const uint32_t *__restrict__ packed = MULTI ? seg_pick(sg.packed, kseg) : sg.packed[0];
     const uint16_t *__restrict__ scales = MULTI ? seg_pick(sg.scales, kseg) : sg.scales[0];
-    float *__restrict__ y = MULTI ? seg_pick(sg.y, kseg) : sg.y[0];
     const int64_t N = MULTI ? seg_pick(sg.rows, kseg) : sg.rows[0];
+    float *__restrict__ y = (MULTI ? seg_pick(sg.y, kseg) : sg.y[0]) + (int64_t)blockIdx.y * N;
     const int gl = threadIdx.x % T;
     const bool lane_on = gl < G;
     const int g_load = lane_on ? gl : G - 1;
@@ -913,6 +914,8 @@ __global__ __launch_bounds__(MAXWGS) void qgemv_big_kernel(const uint16_t *__res
                                                          const uint16_t *__restrict__ scales,
                                                          float *__restrict__ y, int64_t N, int G, int T) {
     extern __shared__ uint32_t smem[];
+    x += (int64_t)blockIdx.y * G * kGroup;  // token blockIdx.y (one token unless batch-invariant)
+    y += (int64_t)blockIdx.y * N;
     float *xd = reinterpret_cast<float *>(smem + big_xd_at(G, LDS_X));
     uint32_t *flags = smem + big_xd_at(G, LDS_X) + G;
     int *nz = reinterpret_cast<int *>(flags + 16);
@@ -1088,8 +1091,10 @@ __global__ __launch_bounds__(64 * WAVES) void qgemv_mfma_kernel(const uint16_t *
     }
     const uint32_t *__restrict__ packed = MULTI ? seg_pick(sg.packed, kseg) : sg.packed[0];
     const uint16_t *__restrict__ scales = MULTI ? seg_pick(sg.scales, kseg) : sg.scales[0];
-    float *__restrict__ y = MULTI ? seg_pick(sg.y, kseg) : sg.y[0];
     const int64_t N = MULTI ? seg_pick(sg.rows, kseg) : sg.rows[0];
+    // token blockIdx.y (one token unless batch-invariant)
+    float *__restrict__ y = (MULTI ? seg_pick(sg.y, kseg) : sg.y[0]) + (int64_t)blockIdx.y * N;
+    x += (int64_t)blockIdx.y * G * kGroup;
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15, lj = lane >> 4;
@@ -2797,7 +2802,7 @@ qw3_status blocks_per_cu(const void *kernel, int wgs, size_t lds, int *out) {
 }
 
 template <int T, bool MULTI>
-qw3_status launch_gemv_small(const uint16_t *x, GemvSegs sg, int count, int G, hipStream_t stream) {
+qw3_status launch_gemv_small(const uint16_t *x, GemvSegs sg, int count, int G, hipStream_t stream, int M) {
     constexpr int R = kGemvWGS / T;
     const size_t lds = stage_words(G) * 4;
     const void *kern = reinterpret_cast<const void *>(&qgemv_small_kernel<T, MULTI, kGemvDepth>);
@@ -2827,27 +2832,28 @@ qw3_status launch_gemv_small(const uint16_t *x, GemvSegs sg, int count, int G, h
     // kGemvDepth (deeper rings would only re-read the last row).
     const int64_t rows_per_wave = ceil_div(tot, blocks * R);
     if (rows_per_wave <= 2)
-        hipLaunchKernelGGL((qgemv_small_kernel<T, MULTI, 1>), dim3((unsigned)blocks), dim3(kGemvWGS), lds, stream, x,
-                           sg, G);
+        hipLaunchKernelGGL((qgemv_small_kernel<T, MULTI, 1>), dim3((unsigned)blocks, (unsigned)M), dim3(kGemvWGS),
+                           lds, stream, x, sg, G);
     else
-        hipLaunchKernelGGL((qgemv_small_kernel<T, MULTI, kGemvDepth>), dim3((unsigned)blocks), dim3(kGemvWGS), lds,
-                           stream, x, sg, G);
+        hipLaunchKernelGGL((qgemv_small_kernel<T, MULTI, kGemvDepth>), dim3((unsigned)blocks, (unsigned)M),
+                           dim3(kGemvWGS), lds, stream, x, sg, G);
     return check_launch();
 }
 
 template <bool MULTI>
-qw3_status launch_gemv_small_any(const uint16_t *x, const GemvSegs &sg, int count, int G, hipStream_t stream) {
-    if (G <= 1) return launch_gemv_small<1, MULTI>(x, sg, count, G, stream);
-    if (G <= 2) return launch_gemv_small<2, MULTI>(x, sg, count, G, stream);
-    if (G <= 4) return launch_gemv_small<4, MULTI>(x, sg, count, G, stream);
-    if (G <= 8) return launch_gemv_small<8, MULTI>(x, sg, count, G, stream);
-    if (G <= 16) return launch_gemv_small<16, MULTI>(x, sg, count, G, stream);
-    if (G <= 32) return launch_gemv_small<32, MULTI>(x, sg, count, G, stream);
-    return launch_gemv_small<64, MULTI>(x, sg, count, G, stream);
+qw3_status launch_gemv_small_any(const uint16_t *x, const GemvSegs &sg, int count, int G, hipStream_t stream,
+                                 int M = 1) {
+    if (G <= 1) return launch_gemv_small<1, MULTI>(x, sg, count, G, stream, M);
+    if (G <= 2) return launch_gemv_small<2, MULTI>(x, sg, count, G, stream, M);
+    if (G <= 4) return launch_gemv_small<4, MULTI>(x, sg, count, G, stream, M);
+    if (G <= 8) return launch_gemv_small<8, MULTI>(x, sg, count, G, stream, M);
+    if (G <= 16) return launch_gemv_small<16, MULTI>(x, sg, count, G, stream, M);
+    if (G <= 32) return launch_gemv_small<32, MULTI>(x, sg, count, G, stream, M);
+    return launch_gemv_small<64, MULTI>(x, sg, count, G, stream, M);
 }
 
 qw3_status launch_gemv_big(const uint16_t *x, const uint32_t *packed, const uint16_t *scales, float *y,
-                           int64_t N, int G, hipStream_t stream) {
+                           int64_t N, int G, hipStream_t stream, int M) {
     // Team of T >= G lanes, T a multiple of 32; the workgroup holds whole
     // waves and at most 1024 threads (T <= 1024 since K <= QW3_MAX_K).
     int T = 32 * ((G + 31) / 32);
@@ -2879,7 +2885,7 @@ qw3_status launch_gemv_big(const uint16_t *x, const uint32_t *packed, const uint
     if (blocks > (int64_t)cus * per_cu) blocks = (int64_t)cus * per_cu;
     hipLaunchKernelGGL(reinterpret_cast<void (*)(const uint16_t *, const uint32_t *, const uint16_t *, float *,
                                                  int64_t, int, int)>(const_cast<void *>(kern)),
-                       dim3((unsigned)blocks), dim3(wgs), lds, stream, x, packed, scales, y, N, G, T);
+                       dim3((unsigned)blocks, (unsigned)M), dim3(wgs), lds, stream, x, packed, scales, y, N, G, T);
     return check_launch();
 }
 
@@ -2887,7 +2893,7 @@ qw3_status launch_gemv_big(const uint16_t *x, const uint32_t *packed, const uint
 // matrices in proportion to their 16-row tiles, at least one and at most one
 // per tile each (4 waves x 16 groups at K = 8192).
 template <int GPW, int WAVES, bool MULTI>
-qw3_status launch_gemv_mfma(const uint16_t *x, GemvSegs sg, int count, hipStream_t stream) {
+qw3_status launch_gemv_mfma(const uint16_t *x, GemvSegs sg, int count, hipStream_t stream, int M = 1) {
     int cus = 0;
     const qw3_status st = cu_count(&cus);
     if (st != QW3_OK) return st;
@@ -2907,8 +2913,8 @@ qw3_status launch_gemv_mfma(const uint16_t *x, GemvSegs sg, int count, hipStream
         sg.blk_end[i] = (int)blocks;
     }
     const size_t lds = mf_lds<GPW, WAVES>();
-    hipLaunchKernelGGL((qgemv_mfma_kernel<GPW, WAVES, MULTI>), dim3((unsigned)blocks), dim3(64 * WAVES), lds, stream,
-                       x, sg);
+    hipLaunchKernelGGL((qgemv_mfma_kernel<GPW, WAVES, MULTI>), dim3((unsigned)blocks, (unsigned)M), dim3(64 * WAVES),
+                       lds, stream, x, sg);
     return check_launch();
 }
 
@@ -2926,8 +2932,10 @@ bool gemv_mfma_takes(int G, const uint16_t *scales, int64_t N) {
     return ceil_div(N, 16) >= 4 * (int64_t)cus;
 }
 
+// M > 1 (the batch-invariant product): the same launch with a token grid
+// dimension, token m reading x + m K and writing y + m N.
 qw3_status launch_gemv(const uint16_t *x, const uint32_t *packed, const uint16_t *scales, float *y,
-                       int64_t N, int64_t K, hipStream_t stream) {
+                       int64_t N, int64_t K, hipStream_t stream, int M = 1) {
     const int G = (int)(K / kGroup);
     if (G <= 64) {
         GemvSegs sg = {};
@@ -2935,10 +2943,10 @@ qw3_status launch_gemv(const uint16_t *x, const uint32_t *packed, const uint16_t
         sg.scales[0] = scales;
         sg.y[0] = y;
         sg.rows[0] = N;
-        if (gemv_mfma_takes(G, scales, N)) return launch_gemv_mfma<16, 4, false>(x, sg, 1, stream);
-        return launch_gemv_small_any<false>(x, sg, 1, G, stream);
+        if (gemv_mfma_takes(G, scales, N)) return launch_gemv_mfma<16, 4, false>(x, sg, 1, stream, M);
+        return launch_gemv_small_any<false>(x, sg, 1, G, stream, M);
     }
-    return launch_gemv_big(x, packed, scales, y, N, G, stream);
+    return launch_gemv_big(x, packed, scales, y, N, G, stream, M);
 }
 
 // Several matrices sharing x: one launch when rows fit one wave (K <= 8192),
@@ -3344,6 +3352,21 @@ qw3_status qgemv_w3g128_multi(const uint16_t *x, int32_t count, const int32_t *c
     if (!aligned(x, 16)) return QW3_ERR_ALIGN;
     return launch_gemv_multi(x, count, reinterpret_cast<const uint32_t *const *>(packed), scales, y, N, K,
                              (hipStream_t)hip_stream);
+}
+
+qw3_status qgemm_w3g128_batch_invariant(const uint16_t *x, const int32_t *packed, const uint16_t *scales,
+                                        float *y, int64_t M, int64_t N, int64_t K, void *hip_stream) {
+    qw3_status st = check_shape(N, K);
+    if (st != QW3_OK) return st;
+    if (M < 0 || M > QW3_MAX_BATCH_INVARIANT_M) return QW3_ERR_SHAPE;
+    if (N == 0 || M == 0) return QW3_OK;
+    if (!y) return QW3_ERR_NULL;
+    if (!aligned(y, 4)) return QW3_ERR_ALIGN;
+    if (K == 0) return fill_zero(y, M * N, (hipStream_t)hip_stream);
+    if (!x || !packed || !scales) return QW3_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scales, 2)) return QW3_ERR_ALIGN;
+    return launch_gemv(x, reinterpret_cast<const uint32_t *>(packed), scales, y, N, K, (hipStream_t)hip_stream,
+                       (int)M);
 }
 
 qw3_status qgemm_w3g128_smallM(const uint16_t *x, const int32_t *packed, const uint16_t *scales, float *y,

@@ -183,6 +183,31 @@ qw3_status qgemm_w3g128_smallM(const uint16_t *x, const int32_t *packed,
                                const uint16_t *scales, float *y, int64_t M, int64_t N,
                                int64_t K, void *hip_stream);
 
+/* Largest M of one qgemm_w3g128_batch_invariant call. */
+#define QW3_MAX_BATCH_INVARIANT_M 65535
+
+/*
+ * qgemm_w3g128_batch_invariant -- the M-row product with every row computed
+ * exactly as the batch-1 product computes it.  The GLQ README ("Inference
+ * kernels") ties its fixed-order reductions to reproducible outputs at batch
+ * 1 and in batched prefill.  qgemm_w3g128_smallM is deterministic run to run,
+ * but its batched and tiled kernels add a row's products in other orders than
+ * the batch-1 kernel, so its rows agree with qgemv_w3g128 only within the
+ * accuracy bound; here a row's bits do not depend on the batch.
+ *   x [M, K] bf16 (row stride K), packed [N, 3K/32] int32, scales [N, K/128] bf16
+ *   y [M, N] float32, written: row m equals, bit for bit, what qgemv_w3g128
+ *   writes for x row m (the same kernel with a token grid dimension, in one
+ *   launch).
+ * It reads the weights once per row of x (M times the batch-1 traffic, partly
+ * served from the caches), so it is for callers that need outputs independent
+ * of the batch, not for throughput.  0 <= M <= QW3_MAX_BATCH_INVARIANT_M,
+ * else QW3_ERR_SHAPE; other validation, alignment and errors as for
+ * qgemv_w3g128.  Uses no device memory beyond its arguments.
+ */
+qw3_status qgemm_w3g128_batch_invariant(const uint16_t *x, const int32_t *packed,
+                                        const uint16_t *scales, float *y, int64_t M, int64_t N,
+                                        int64_t K, void *hip_stream);
+
 /* Device scratch of qgemm_w3g128_smallM_noalloc, per device (128 MiB). */
 #define QW3_NOALLOC_SCRATCH_BYTES (128ull << 20)
 

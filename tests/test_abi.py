@@ -66,11 +66,16 @@ def test_bad_shapes(n, k):
     assert lib.qgemv_w3g128(A16, A16B, A16C, A16D, n, k, S) == q.QW3_ERR_SHAPE
     assert lib.qgemm_w3g128_smallM(A16, A16B, A16C, A16D, 2, n, k, S) == q.QW3_ERR_SHAPE
     assert lib.qgemm_w3g128_smallM_noalloc(A16, A16B, A16C, A16D, 2, n, k, S) == q.QW3_ERR_SHAPE
+    assert lib.qgemm_w3g128_batch_invariant(A16, A16B, A16C, A16D, 2, n, k, S) == q.QW3_ERR_SHAPE
 
 
 def test_bad_m():
     assert q.raw().qgemm_w3g128_smallM(A16, A16B, A16C, A16D, -1, 4, 128, S) == q.QW3_ERR_SHAPE
     assert q.raw().qgemm_w3g128_smallM_noalloc(A16, A16B, A16C, A16D, -1, 4, 128, S) == q.QW3_ERR_SHAPE
+    lib = q.raw()
+    assert lib.qgemm_w3g128_batch_invariant(A16, A16B, A16C, A16D, -1, 4, 128, S) == q.QW3_ERR_SHAPE
+    # one token per grid row: at most QW3_MAX_BATCH_INVARIANT_M rows
+    assert lib.qgemm_w3g128_batch_invariant(A16, A16B, A16C, A16D, 65536, 4, 128, S) == q.QW3_ERR_SHAPE
 
 
 def test_null_pointers():
@@ -88,6 +93,7 @@ def test_null_pointers():
         assert lib.qgemv_w3g128(*args, 4, 128, S) == q.QW3_ERR_NULL
         assert lib.qgemm_w3g128_smallM(*args, 3, 4, 128, S) == q.QW3_ERR_NULL
         assert lib.qgemm_w3g128_smallM_noalloc(*args, 3, 4, 128, S) == q.QW3_ERR_NULL
+        assert lib.qgemm_w3g128_batch_invariant(*args, 3, 4, 128, S) == q.QW3_ERR_NULL
 
 
 def test_misaligned_pointers():
@@ -105,6 +111,8 @@ def test_misaligned_pointers():
     assert lib.qgemv_w3g128(A16, A16B, A16C, ctypes.c_void_p(0x40002), 4, 128, S) == q.QW3_ERR_ALIGN
     assert lib.qgemm_w3g128_smallM(MIS, A16B, A16C, A16D, 3, 4, 128, S) == q.QW3_ERR_ALIGN
     assert lib.qgemm_w3g128_smallM_noalloc(MIS, A16B, A16C, A16D, 3, 4, 128, S) == q.QW3_ERR_ALIGN
+    assert lib.qgemm_w3g128_batch_invariant(MIS, A16B, A16C, A16D, 3, 4, 128, S) == q.QW3_ERR_ALIGN
+    assert lib.qgemm_w3g128_batch_invariant(A16, A16B, A16C, ctypes.c_void_p(0x40002), 3, 4, 128, S) == q.QW3_ERR_ALIGN
 
 
 def test_empty_sizes_enqueue_nothing():
@@ -118,6 +126,8 @@ def test_empty_sizes_enqueue_nothing():
     assert lib.qgemm_w3g128_smallM_noalloc(NULL, NULL, NULL, NULL, 0, 5, 1024, S) == q.QW3_OK
     assert lib.qgemm_w3g128_smallM(NULL, NULL, NULL, NULL, 5, 0, 1024, S) == q.QW3_OK
     assert lib.qgemm_w3g128_smallM_noalloc(NULL, NULL, NULL, NULL, 5, 0, 1024, S) == q.QW3_OK
+    assert lib.qgemm_w3g128_batch_invariant(NULL, NULL, NULL, NULL, 0, 5, 1024, S) == q.QW3_OK
+    assert lib.qgemm_w3g128_batch_invariant(NULL, NULL, NULL, NULL, 5, 0, 1024, S) == q.QW3_OK
 
 
 def test_quantization_config_descriptor():

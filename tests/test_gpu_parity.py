@@ -360,6 +360,50 @@ def test_qgemv_multi_matches_single(k, ns):
             assert_close(y[None, :], yr, a, "multi")
 
 
+# ----------------------------------------------- batch-invariant product --
+
+@pytest.mark.parametrize("m,n,k", [(1, 37, 256), (5, 300, 1024), (3, 130, 8192), (4, 16400, 8192),
+                                   (7, 200, 28672), (2, 9, 131072)])
+def test_batch_invariant_rows_equal_gemv(m, n, k):
+    """Every row of qgemm_w3g128_batch_invariant equals qgemv_w3g128 on that
+    activation row bit for bit (the lane-per-group, matrix-core and long-row
+    kernels), and the rows meet the tolerance against the oracle."""
+    say("batch invariant", m, n, k)
+    c = synth.codes_all8(5300 + m, n, k)
+    s = synth.scales(5301 + m, n, k // 128, sigma=0.02, eps=1e-3)
+    x = synth.activations(5302 + m, m, k)
+    p, sd, xd = gpu_pack(c), dev(s), dev(x)
+    y = host(q().qgemm_w3g128_batch_invariant(xd, p, sd))
+    for r in range(m):
+        yr1 = host(q().qgemv_w3g128(xd[r].contiguous(), p, sd))
+        assert np.array_equal(y[r].view(np.uint32), yr1.view(np.uint32)), r
+    yr, a = oracle.gemm(x, oracle.pack(c), s, k)
+    assert_close(y, yr, a, "batch invariant")
+
+
+def test_batch_invariant_wide_range_rows_take_the_fixup():
+    """Rows whose activations defeat the fast conversion (large values on
+    code-4 weights, tiny ones elsewhere) go through the exact recompute in
+    the batch-1 kernel; their rows still equal qgemv_w3g128's and meet the
+    tolerance, next to ordinary rows."""
+    m, n, k = 3, 64, 1024
+    rng = np.random.default_rng(5310)
+    c = rng.integers(0, 8, size=(n, k)).astype(np.uint8)
+    c[:, ::8] = 4
+    s = synth.scales(5311, n, k // 128, sigma=0.02, eps=1e-3)
+    x = synth.activations(5312, m, k)
+    xf = synth.bf16_bits_to_f32(x).astype(np.float64)
+    xf[1] *= 2.0 ** -22
+    xf[1, ::8] = rng.standard_normal(k // 8) * 2.0 ** 12
+    x = synth.f32_to_bf16_bits(xf.astype(np.float32))
+    p, sd, xd = gpu_pack(c), dev(s), dev(x)
+    y = host(q().qgemm_w3g128_batch_invariant(xd, p, sd))
+    for r in range(m):
+        assert np.array_equal(y[r].view(np.uint32), host(q().qgemv_w3g128(xd[r].contiguous(), p, sd)).view(np.uint32))
+    yr, a = oracle.gemm(x, oracle.pack(c), s, k)
+    assert_close(y, yr, a, "batch invariant, wide range")
+
+
 def test_qgemv_multi_qkv_full_size():
     names = ("q_proj", "k_proj", "v_proj")
     k = synth.LAYER_70B["q_proj"][1]
