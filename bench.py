@@ -560,6 +560,58 @@ def traffic_from_counters(fetch_csv: str, write_csv: str, out_path: str = TRAFFI
     return rec
 
 
+# Kernels of the library, as the tracer names them (the per-call traffic of a
+# --case run is the sum over these, each dispatched once per call).
+LIB_KERNELS = ("qgemv_", "qgemm_", "prep_x", "prep_tile_x")
+
+
+def case_traffic_from_counters(case: str, fetch_csv: str, write_csv: str) -> dict:
+    """HBM bytes per call of `bench.py --case NAME:M --calibrate` from its two
+    counter runs (FETCH_SIZE, WRITE_SIZE): each library kernel's average per
+    dispatch, scaled by what the counters read for the run's five 256 MiB
+    calibration copies, summed over the kernels of one call."""
+    import csv
+    import synth
+    name, m = case.split(":")
+    m = int(m)
+    n, k = synth.LAYER_70B[name][:2]
+    copy_bytes, copies = 256 * 2 ** 20, 5
+
+    def per_kernel(path, counter):
+        vals, cps = {}, []
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                kn = r["Kernel_Name"]
+                v = float(r["Counter_Value"])
+                if any(t in kn for t in LIB_KERNELS) and "qpack" not in kn:
+                    short = kn.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+                    vals.setdefault(short, []).append(v)
+                elif "copyBuffer" in kn or "copy" in kn.lower():
+                    cps.append(v)
+        if not vals or len(cps) < copies:
+            raise SystemExit("%s: no library kernels or fewer than %d copy dispatches" % (path, copies))
+        cal = sorted(cps)[-copies:]
+        return {kk: (sum(v) / len(v), len(v)) for kk, v in vals.items()}, sum(cal) / len(cal)
+
+    f, f_cal = per_kernel(fetch_csv, "FETCH_SIZE")
+    w, w_cal = per_kernel(write_csv, "WRITE_SIZE")
+    fs, ws = copy_bytes / (f_cal * 1024), copy_bytes / (w_cal * 1024)
+    kernels = {}
+    total = 0
+    for kk in sorted(f):
+        rd = int(round(f[kk][0] * 1024 * fs))
+        wr = int(round(w.get(kk, (0.0, 0))[0] * 1024 * ws))
+        kernels[kk] = {"fetch_bytes": rd, "write_bytes": wr, "dispatches": f[kk][1]}
+        total += rd + wr
+    alg = gemv_bytes(n, k, m)
+    return {"case": case, "workload": "%s [%d, %d] M=%d, one qgemm_w3g128_smallM call" % (name, n, k, m),
+            "per_kernel": kernels, "hbm_bytes_per_call": total, "algorithmic_bytes_per_call": alg,
+            "traffic_over_algorithmic": round(total / alg, 4), "fetch_scale": round(fs, 4),
+            "write_scale": round(ws, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -575,6 +627,9 @@ def main():
     ap.add_argument("--ceiling", action="store_true",
                     help="also time a plain 1 GiB device copy and a streaming-read kernel and print "
                          "their GB/s on stderr")
+    ap.add_argument("--case-traffic-from", nargs=3, metavar=("CASE", "FETCH_CSV", "WRITE_CSV"),
+                    help="summarise two counter runs (FETCH_SIZE, WRITE_SIZE) of --case CASE --calibrate into "
+                         "HBM bytes per call, per library kernel; prints JSON (no GPU needed)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE) of --calibrate into "
                          "the committed traffic record and exit (no GPU needed)")
@@ -586,6 +641,9 @@ def main():
     args = ap.parse_args()
     if args.traffic_from:
         print(json.dumps(traffic_from_counters(*args.traffic_from)))
+        return
+    if args.case_traffic_from:
+        print(json.dumps(case_traffic_from_counters(*args.case_traffic_from)))
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
