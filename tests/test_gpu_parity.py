@@ -381,6 +381,22 @@ def test_batch_invariant_rows_equal_gemv(m, n, k):
     assert_close(y, yr, a, "batch invariant")
 
 
+def test_batch_invariant_largest_m():
+    """M = QW3_MAX_BATCH_INVARIANT_M rows (one grid row per token): every row
+    against the oracle, a sample of rows bit for bit against qgemv_w3g128."""
+    m, n, k = q().QW3_MAX_BATCH_INVARIANT_M, 3, 256
+    say("batch invariant, largest M", m)
+    c = synth.codes_all8(5320, n, k)
+    s = synth.scales(5321, n, k // 128, sigma=0.02, eps=1e-3)
+    x = synth.activations(5322, m, k)
+    p, sd, xd = gpu_pack(c), dev(s), dev(x)
+    y = host(q().qgemm_w3g128_batch_invariant(xd, p, sd))
+    yr, a = oracle.gemm(x, oracle.pack(c), s, k)
+    assert_close(y, yr, a, "batch invariant, largest M")
+    for r in (0, 1, 4097, m // 2, m - 2, m - 1):
+        assert np.array_equal(y[r].view(np.uint32), host(q().qgemv_w3g128(xd[r].contiguous(), p, sd)).view(np.uint32))
+
+
 def test_batch_invariant_wide_range_rows_take_the_fixup():
     """Rows whose activations defeat the fast conversion (large values on
     code-4 weights, tiny ones elsewhere) go through the exact recompute in
