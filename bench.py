@@ -40,7 +40,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 matrix peak, published
 MALL_BYTES = 256 * 2 ** 20
 METRIC = "W3G128 GEMV effective HBM GB/s and % of peak (70B layer shapes, B=1)"
-KERNEL_SRC = os.path.join(ROOT, "dequant_gemv_qgemv_amd", "csrc", "qw3.hip")
+KERNEL_SRC_DIR = os.path.join(ROOT, "dequant_gemv_qgemv_amd", "csrc")
+KERNEL_BUILD = os.path.join(ROOT, "dequant_gemv_qgemv_amd", "_build.py")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qgemv_gate_proj_traffic.json")
 
 
@@ -50,8 +51,16 @@ def gemv_bytes(n: int, k: int, m: int = 1) -> int:
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+    """Hash of the library's sources and its build flags (the recorded counters
+    describe the code these produce)."""
+    h = hashlib.sha256()
+    paths = sorted(os.path.join(KERNEL_SRC_DIR, f) for f in os.listdir(KERNEL_SRC_DIR)
+                   if f.endswith((".hip", ".h")))
+    for path in paths + [KERNEL_BUILD]:
+        h.update(os.path.basename(path).encode() + b"\0")
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic():

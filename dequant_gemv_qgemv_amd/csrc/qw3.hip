@@ -1,474 +1,15 @@
-// W3G128 fused dequantize-and-multiply kernels for gfx950 (CDNA4), with the
-// C ABI declared in include/qw3.h.
-//
-// Format (GSQ model card "Llama-3.1-70B-Instruct-3Bit-GSQ", "Storage layout"):
-// a row of K weights is a little-endian bitstream of 3K bits packed into 3K/32
-// int32 words, code k in stream bits [3k, 3k+3); one bf16 scale per 128
-// weights; weight = scale * (code - 4).  A group of 128 codes is exactly 12
-// words (48 bytes, three 16-byte loads) and a 32-code block is 3 words, so
-// every group and block starts on a word boundary.
-//
-// Decode.  Two codes are turned into an exact fp16 pair with two VALU ops:
-//   v = (window & mask) | 0x64006400   puts code a at mantissa bits [p,p+3) of
-//                                      the low half and code b at [p',p'+3) of
-//                                      the high half: fp16 values 1024 + a*2^p
-//                                      and 1024 + b*2^p'
-//   q = v - (1024 + 4*2^p, 1024 + 4*2^p')   (one v_pk_add_f16)
-// which yields ((a - 4) * 2^p, (b - 4) * 2^p') exactly; the 2^-p factors are
-// folded into the activations.  `window` is a 32-bit funnel shift of the
-// 96-bit block.  The 16 pairs of a block come from 7 windows, three of which
-// are the raw words, so a block of 32 codes costs 4 shifts + 16 and-or + 16
-// packed adds.  Which two codes share a pair does not matter for a dot product
-// as long as the activations are paired the same way, so activations are
-// converted once into the same pairing (kPairs below).
-//
-// Activations.  x is bf16; the products use fp16 operands, so each exponent
-// set (a group of 128 activations at batch 1, an 8-group slice of a token in
-// batched decode, a whole token in the tile kernels) is scaled by a power of
-// two 2^-e that brings its largest magnitude into [2^14, 2^15), each element
-// by its slot's 2^-p (p <= 7), and rounded to fp16.  bf16 has 8 significant
-// bits and fp16 11, so every element of magnitude at least 2^(e-7) lands in
-// the fp16 normal range and converts exactly; 2^e is multiplied back in fp32
-// together with the weight scale.  Those products are exact and only the fp32
-// accumulation rounds.
-//
-// Exactness guard.  Smaller elements (about 2^21 or more below the largest of
-// their set) may be rounded or flushed.  The conversion sums their magnitudes
-// per (token, group) into D, which bounds what they can change in any output:
-// |sum_k w_k (x_k - x'_k)| <= 4 sum_g |s_g| D_g.  When some D is non-zero a
-// pass after the fast loop (fixup_outputs) evaluates that bound for every
-// output the workgroup wrote and recomputes in fp32 the ones above 2^-21, so
-// each output meets |y - y_exact| <= 1e-4 sum_k |w_k x_k| + 1e-6 whatever the
-// spread of x.  The tile kernels also fold the group scale into the fp16
-// weight, exact while every scale of the row lies within 2^21 of its largest;
-// other rows are recomputed by the same pass.  The fast loops are unchanged:
-// the pass costs nothing when every D is zero and every row folds exactly.
-#include <hip/hip_runtime.h>
-
-#include <stdint.h>
-#include <stdio.h>
-#include <string.h>
-
-#include <mutex>
+// W3G128 fused dequantize-and-multiply for gfx950 (CDNA4): the batched-decode
+// and prefill kernels, the format utilities (qpack, repack, qdequant) and the
+// C ABI declared in include/qw3.h.  The format, decode, activation conversion
+// and exactness guard shared by every kernel are in qw3_common.h; the batch-1
+// kernels in qw3_gemv.hip.
 #include <vector>
-#include <type_traits>
 
-#include "qw3.h"
+#include "qw3_common.h"
+
+using namespace qw3_shared;
 
 namespace {
-
-typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
-typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
-typedef float f4_t __attribute__((ext_vector_type(4)));
-
-constexpr int kGroup = 128;         // weights per scale
-constexpr int kWordsPerGroup = 12;  // 128 * 3 / 32
-
-// ----------------------------------------------------------- decode table --
-// The 16 code pairs of a 32-code block: window index (0: w0, 1: bits [4,36),
-// 2: [12,44), 3: w1, 4: [41,73), 5: w2, 6: [71,96)), low code, high code, and
-// their bit offsets p, p' inside the window's two 16-bit halves.  Every code
-// 0..31 appears once; lo at 3*lo - start(win) = p, hi at 3*hi - start - 16 = p'.
-struct PairSpec {
-    int win, lo, hi, p, pp;
-};
-constexpr PairSpec kPairs[16] = {
-    {0, 0, 7, 0, 5},   {0, 1, 6, 3, 2},   {1, 2, 9, 2, 7},   {1, 3, 8, 5, 4},
-    {2, 4, 10, 0, 2},  {2, 5, 11, 3, 5},  {3, 12, 18, 4, 6}, {3, 13, 17, 7, 3},
-    {4, 14, 19, 1, 0}, {4, 15, 21, 4, 6}, {4, 16, 20, 7, 3}, {5, 22, 28, 2, 4},
-    {5, 23, 27, 5, 1}, {6, 24, 29, 1, 0}, {6, 25, 31, 4, 6}, {6, 26, 30, 7, 3}};
-constexpr int kWinStart[7] = {0, 4, 12, 32, 41, 64, 71};
-
-constexpr bool pairs_cover_block() {
-    int seen = 0;
-    for (int i = 0; i < 16; ++i) {
-        const PairSpec ps = kPairs[i];
-        if (3 * ps.lo - kWinStart[ps.win] != ps.p || 3 * ps.hi - kWinStart[ps.win] - 16 != ps.pp) return false;
-        if (ps.p < 0 || ps.p > 7 || ps.pp < 0 || ps.pp > 7) return false;
-        seen |= (1 << ps.lo) | (1 << ps.hi);
-    }
-    return seen == -1;
-}
-static_assert(pairs_cover_block(), "decode table must cover codes 0..31 once at valid offsets");
-
-__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
-
-__device__ __forceinline__ h2_t as_h2(uint32_t u) { return __builtin_bit_cast(h2_t, u); }
-
-__device__ __forceinline__ uint32_t pack_h2(_Float16 lo, _Float16 hi) {
-    h2_t v = {lo, hi};
-    return __builtin_bit_cast(uint32_t, v);
-}
-
-// Exact ((a-4)*2^P, (b-4)*2^PP) from a window holding code a at bits [P, P+3)
-// and code b at bits [16+PP, 16+PP+3).
-// `magic` is 0x64006400 held in a VGPR (see magic_vgpr()): with the mask in an
-// SGPR the and/or pair then issues as a single v_and_or_b32 (gfx9 VOP3 cannot
-// encode two literal constants).
-template <int P, int PP>
-__device__ __forceinline__ h2_t q_pair(uint32_t win, uint32_t magic) {
-    constexpr uint32_t kMask = (7u << P) | (7u << (16 + PP));
-    constexpr h2_t kSub = {(_Float16)(1024.0f + 4.0f * (1 << P)), (_Float16)(1024.0f + 4.0f * (1 << PP))};
-    const uint32_t v = (win & kMask) | magic;
-    return as_h2(v) - kSub;
-}
-
-// 0x64006400 (two fp16 1024.0) in a VGPR the compiler cannot constant-fold.
-__device__ __forceinline__ uint32_t magic_vgpr() {
-    uint32_t m;
-    asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(m));
-    return m;
-}
-
-template <int I>
-__device__ __forceinline__ h2_t q_pair_i(const uint32_t (&win)[7], uint32_t magic) {
-    constexpr PairSpec ps = kPairs[I];
-    return q_pair<ps.p, ps.pp>(win[ps.win], magic);
-}
-
-// The 32 codes of words (w0, w1, w2) as 16 exact fp16 pairs, kPairs order.
-__device__ __forceinline__ void decode_block(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t magic,
-                                             h2_t (&q)[16]) {
-    const uint32_t win[7] = {w0,
-                             __builtin_amdgcn_alignbit(w1, w0, 4),
-                             __builtin_amdgcn_alignbit(w1, w0, 12),
-                             w1,
-                             __builtin_amdgcn_alignbit(w2, w1, 9),
-                             w2,
-                             w2 >> 7};
-    q[0] = q_pair_i<0>(win, magic);
-    q[1] = q_pair_i<1>(win, magic);
-    q[2] = q_pair_i<2>(win, magic);
-    q[3] = q_pair_i<3>(win, magic);
-    q[4] = q_pair_i<4>(win, magic);
-    q[5] = q_pair_i<5>(win, magic);
-    q[6] = q_pair_i<6>(win, magic);
-    q[7] = q_pair_i<7>(win, magic);
-    q[8] = q_pair_i<8>(win, magic);
-    q[9] = q_pair_i<9>(win, magic);
-    q[10] = q_pair_i<10>(win, magic);
-    q[11] = q_pair_i<11>(win, magic);
-    q[12] = q_pair_i<12>(win, magic);
-    q[13] = q_pair_i<13>(win, magic);
-    q[14] = q_pair_i<14>(win, magic);
-    q[15] = q_pair_i<15>(win, magic);
-}
-
-// Pairs 4u .. 4u + 3 of a block (kPairs order), u a compile-time value after
-// unrolling: the same values as decode_block, a quarter at a time.  Each
-// quarter needs one funnel shift (windows 1, 2, 4, 6; windows 0, 3, 5 are the
-// words themselves).
-__device__ __forceinline__ void decode_quarter(int u, uint32_t w0, uint32_t w1, uint32_t w2, uint32_t magic,
-                                               h2_t (&q)[4]) {
-    if (u == 0) {
-        const uint32_t win[7] = {w0, __builtin_amdgcn_alignbit(w1, w0, 4), 0, 0, 0, 0, 0};
-        q[0] = q_pair_i<0>(win, magic);
-        q[1] = q_pair_i<1>(win, magic);
-        q[2] = q_pair_i<2>(win, magic);
-        q[3] = q_pair_i<3>(win, magic);
-    } else if (u == 1) {
-        const uint32_t win[7] = {0, 0, __builtin_amdgcn_alignbit(w1, w0, 12), w1, 0, 0, 0};
-        q[0] = q_pair_i<4>(win, magic);
-        q[1] = q_pair_i<5>(win, magic);
-        q[2] = q_pair_i<6>(win, magic);
-        q[3] = q_pair_i<7>(win, magic);
-    } else if (u == 2) {
-        const uint32_t win[7] = {0, 0, 0, 0, __builtin_amdgcn_alignbit(w2, w1, 9), w2, 0};
-        q[0] = q_pair_i<8>(win, magic);
-        q[1] = q_pair_i<9>(win, magic);
-        q[2] = q_pair_i<10>(win, magic);
-        q[3] = q_pair_i<11>(win, magic);
-    } else {
-        const uint32_t win[7] = {0, 0, 0, 0, 0, w2, w2 >> 7};
-        q[0] = q_pair_i<12>(win, magic);
-        q[1] = q_pair_i<13>(win, magic);
-        q[2] = q_pair_i<14>(win, magic);
-        q[3] = q_pair_i<15>(win, magic);
-    }
-}
-
-// acc + sum over the block of q * x', x' given as 16 fp16 pairs in pair order.
-__device__ __forceinline__ float dot_block(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t magic,
-                                           const uint32_t *xp, float acc) {
-    h2_t q[16];
-    decode_block(w0, w1, w2, magic, q);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc = __builtin_amdgcn_fdot2(q[i], as_h2(xp[i]), acc, false);
-    return acc;
-}
-
-// ---------------------------------------------------------------- DPP ------
-template <int CTRL, int ROW_MASK = 0xF>
-__device__ __forceinline__ float dpp_f32(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
-}
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
-}
-constexpr int kDppQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
-constexpr int kDppQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
-constexpr int kDppRowHalfMirror = 0x141;
-constexpr int kDppRowMirror = 0x140;
-constexpr int kDppRowBcast15 = 0x142;
-constexpr int kDppRowBcast31 = 0x143;
-
-// Sum over aligned segments of T lanes (T a power of two <= 64).  The total
-// lands in the last lane of each segment (and, for T <= 16, in all of them).
-template <int T>
-__device__ __forceinline__ float segment_sum(float v) {
-    if constexpr (T >= 2) v += dpp_f32<kDppQuadXor1>(v);
-    if constexpr (T >= 4) v += dpp_f32<kDppQuadXor2>(v);
-    if constexpr (T >= 8) v += dpp_f32<kDppRowHalfMirror>(v);
-    if constexpr (T >= 16) v += dpp_f32<kDppRowMirror>(v);
-    if constexpr (T >= 32) v += dpp_f32<kDppRowBcast15, 0xA>(v);
-    if constexpr (T >= 64) v += dpp_f32<kDppRowBcast31, 0xC>(v);
-    return v;
-}
-
-// ------------------------------------------------- activation conversion --
-// Largest |x| of 32 bf16 values (as a bf16 magnitude bit pattern).
-__device__ __forceinline__ uint32_t absmax32(const uint4 (&xb)[4]) {
-    uint32_t m = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t d[4] = {xb[i].x, xb[i].y, xb[i].z, xb[i].w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            m = max(m, d[j] & 0x7FFFu);
-            m = max(m, (d[j] >> 16) & 0x7FFFu);
-        }
-    }
-    return m;
-}
-
-// Exponent e with (largest magnitude) * 2^-e in [2^14, 2^15).
-__device__ __forceinline__ int group_exponent(uint32_t absmax_bits) {
-    return __builtin_amdgcn_frexp_expf(bf16_to_f32(absmax_bits)) - 15;
-}
-
-// Largest magnitude and smallest non-zero magnitude (0x10000 when all are
-// zero) of 32 bf16 values, as bf16 magnitude bit patterns; packed 16-bit max
-// and min, one of each per two values.
-typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ void block_stats(const uint4 (&xb)[4], uint32_t &mx, uint32_t &mn) {
-    u16x2_t vmax = {0, 0}, vmin = {0xFFFF, 0xFFFF};
-    const u16x2_t one = {1, 1};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t d[4] = {xb[i].x, xb[i].y, xb[i].z, xb[i].w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const u16x2_t v = __builtin_bit_cast(u16x2_t, d[j] & 0x7FFF7FFFu);
-            vmax = __builtin_elementwise_max(vmax, v);
-            vmin = __builtin_elementwise_min(vmin, v - one);  // zero wraps to 0xFFFF
-        }
-    }
-    mx = max((uint32_t)vmax.x, (uint32_t)vmax.y);
-    mn = min((uint32_t)vmin.x, (uint32_t)vmin.y) + 1u;
-}
-
-// bf16 magnitude bits of 2^(e-7): elements at least this large convert to
-// fp16 normals exactly under exponent e for every slot offset p <= 7.
-__device__ __forceinline__ uint32_t exact_floor_bits(int e) {
-    const int b = e + 120;  // biased bf16 exponent of 2^(e-7)
-    if (b >= 1) return (uint32_t)min(b, 255) << 7;
-    if (b >= -6) return 1u << (b + 6);  // a bf16 subnormal
-    return 0u;
-}
-
-// 32 bf16 values -> x * 2^-(e + slot offset) as fp16, arranged as the 16
-// pairs of a block (kPairs order).
-__device__ __forceinline__ void convert_block(const uint4 (&xb)[4], int e, uint32_t (&out)[16]) {
-    float f[32];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t d[4] = {xb[i].x, xb[i].y, xb[i].z, xb[i].w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            f[8 * i + 2 * j] = bf16_to_f32(d[j] & 0xFFFFu);
-            f[8 * i + 2 * j + 1] = bf16_to_f32(d[j] >> 16);
-        }
-    }
-#pragma unroll
-    for (int p = 0; p < 16; ++p) {
-        const PairSpec ps = kPairs[p];
-        out[p] = pack_h2((_Float16)ldexpf(f[ps.lo], -e - ps.p), (_Float16)ldexpf(f[ps.hi], -e - ps.pp));
-    }
-}
-
-// Conversion error of a block: sum over its 32 values of |x - x'|, x' the
-// value its fp16 operand stands for, fp16(x * 2^-(e+p)) * 2^(e+p) with the
-// slot offset p of convert_block.  fp16 subnormals are kept by the conversion
-// and by every fp16 product used here (measured on gfx950), so an element
-// converts exactly unless its low bits fall below 2^-24 after scaling; each
-// difference is exact in fp32.  Only called when the block has a value below
-// 2^(e-7), the smallest that is surely exact.
-__device__ __forceinline__ float conversion_error(const uint4 (&xb)[4], int e) {
-    float f[32];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t d[4] = {xb[i].x, xb[i].y, xb[i].z, xb[i].w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            f[8 * i + 2 * j] = bf16_to_f32(d[j] & 0xFFFFu);
-            f[8 * i + 2 * j + 1] = bf16_to_f32(d[j] >> 16);
-        }
-    }
-    float err = 0.f;
-#pragma unroll
-    for (int p = 0; p < 16; ++p) {
-        const PairSpec ps = kPairs[p];
-        const float a = ldexpf(f[ps.lo], -e - ps.p), b = ldexpf(f[ps.hi], -e - ps.pp);
-        err += ldexpf(fabsf(a - (float)(_Float16)a), e + ps.p);
-        err += ldexpf(fabsf(b - (float)(_Float16)b), e + ps.pp);
-    }
-    return err;
-}
-
-__device__ __forceinline__ void load_x32(const uint16_t *src, uint4 (&xb)[4]) {
-    const uint4 *s = reinterpret_cast<const uint4 *>(src);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) xb[i] = s[i];
-}
-
-// ------------------------------------------------------- exact fixup pass --
-// Outputs whose bound 4 sum_g |s_g| D_g exceeds kFixBudget are recomputed by
-// exact_output.  The budget leaves half of the 1e-6 absolute term of the
-// accuracy bound for the fast path's own fp32 rounding.
-constexpr float kFixBudget = 0x1p-21f;
-constexpr int kNzCap = 128;  // compacted list of groups with a non-zero D
-
-// sum_{g0 <= g < g1} s[g] * sum_{k in g} (c_k - 4) x_k in fp32 by one thread,
-// read the plain way: code i of a 32-code block is bits [3i, 3i + 3) of its
-// three little-endian words.  Each product (c - 4) x is exact in fp32; a
-// group's 128 products are added in order, the group sums (times their
-// scale) in runs of 32 groups, the runs in order.
-__device__ __forceinline__ float exact_output(const uint16_t *__restrict__ xrow, const uint32_t *__restrict__ wrow,
-                                           const uint16_t *__restrict__ srow, int g0, int g1) {
-    float tot = 0.f;
-    for (int gb = g0; gb < g1; gb += 32) {
-        const int ge = min(gb + 32, g1);
-        float run = 0.f;
-        for (int g = gb; g < ge; ++g) {
-            const uint32_t *gw = wrow + (int64_t)g * kWordsPerGroup;
-            float acc = 0.f;
-            for (int b = 0; b < 4; ++b) {
-                const uint32_t w[4] = {gw[3 * b], gw[3 * b + 1], gw[3 * b + 2], 0u};
-                uint4 xb[4];
-                load_x32(xrow + (int64_t)g * kGroup + 32 * b, xb);
-                const uint32_t xw[16] = {xb[0].x, xb[0].y, xb[0].z, xb[0].w, xb[1].x, xb[1].y, xb[1].z, xb[1].w,
-                                         xb[2].x, xb[2].y, xb[2].z, xb[2].w, xb[3].x, xb[3].y, xb[3].z, xb[3].w};
-#pragma unroll
-                for (int i = 0; i < 32; ++i) {
-                    const int bit = 3 * i;
-                    const uint32_t c = __builtin_amdgcn_alignbit(w[(bit >> 5) + 1], w[bit >> 5], bit & 31) & 7u;
-                    const float xv = bf16_to_f32((i & 1) ? (xw[i >> 1] >> 16) : (xw[i >> 1] & 0xFFFFu));
-                    acc = fmaf((float)((int)c - 4), xv, acc);
-                }
-            }
-            run = fmaf(acc, bf16_to_f32(srow[g]), run);
-        }
-        tot += run;
-    }
-    return tot;
-}
-
-// Whether folding the scales of row srow[g0..g1) into fp16 weights as
-// s * 2^-E, E chosen so that the largest maps to [8, 16), is inexact for some
-// non-zero scale: exact iff s * 2^-E >= 2^-17 (8 significant bits then sit at
-// or above fp16's smallest subnormal, and so do the products with (c-4) 2^p).
-__device__ __forceinline__ bool fold_inexact(const uint16_t *__restrict__ srow, int g0, int g1) {
-    uint32_t mx = 0, mn = 0x10000u;
-    for (int g = g0; g < g1; ++g) {
-        const uint32_t b = srow[g] & 0x7FFFu;
-        mx = max(mx, b);
-        if (b) mn = min(mn, b);
-    }
-    if (mx == 0) return false;
-    const int E = __builtin_amdgcn_frexp_expf(bf16_to_f32(mx)) - 4;
-    return bf16_to_f32(mn) < ldexpf(1.0f, E - 17);
-}
-
-// The rows a workgroup wrote: blocks blk, blk + nblk, blk + 2 nblk, ... of R
-// consecutive rows each, rows past N dropped.
-struct BlockRows {
-    int64_t blk, nblk, R, N;
-    __device__ int64_t count() const {
-        const int64_t nb = (N + R - 1) / R;
-        return blk < nb ? ((nb - blk + nblk - 1) / nblk) * R : 0;
-    }
-    __device__ int64_t row(int64_t i) const {
-        const int64_t r = (blk + (i / R) * nblk) * R + i % R;
-        return r < N ? r : -1;
-    }
-};
-
-// Wave 0 lists in nz[0..) the groups g in [g0, g1) with any_d(g); nz[kNzCap]
-// receives their count (which may exceed kNzCap).  All threads of the
-// workgroup call it (it ends with a barrier).
-template <class AnyD>
-__device__ __forceinline__ int build_nz(int g0, int g1, AnyD any_d, int *nz) {
-    if (threadIdx.x < 64) {
-        const int lane = threadIdx.x;
-        int cnt = 0;
-        for (int base = g0; base < g1; base += 64) {
-            const int g = base + lane;
-            const bool f = g < g1 && any_d(g);
-            const uint64_t bal = __ballot(f);
-            const int pos = cnt + __popcll(bal & ((uint64_t(1) << lane) - 1));
-            if (f && pos < kNzCap) nz[pos] = g;
-            cnt += __popcll(bal);
-        }
-        if (lane == 0) nz[kNzCap] = cnt;
-    }
-    __syncthreads();
-    return nz[kNzCap];
-}
-
-// The fixup pass over the outputs out[m * ldo + r] (tokens m < Mt, x row m at
-// x + m * ldx; rows r of `rows`) computed over the groups [g0, g1): with D(m, g)
-// = d_at(m, g), the outputs whose bound exceeds kFixBudget -- and, with `fold`,
-// every output of a row whose scales do not fold exactly -- are recomputed by
-// exact_output.  nz / nnz list the groups with a non-zero D (nz == nullptr or
-// nnz > kNzCap: every group of the range).  Threads tid, tid + nthr, ... take
-// one row each.  The caller orders the fast path's stores before this pass.
-template <int TB, class DAt>
-__device__ __forceinline__ void fixup_outputs(const uint16_t *__restrict__ x, int64_t ldx, int Mt,
-                              const uint32_t *__restrict__ packed, const uint16_t *__restrict__ scales, int G,
-                              int g0, int g1, const BlockRows &rows, DAt d_at, const int *nz, int nnz, bool fold,
-                              float *__restrict__ out, int64_t ldo, int tid, int nthr) {
-    const int64_t W = (int64_t)G * kWordsPerGroup;
-    const bool dense = nz == nullptr || nnz > kNzCap;
-    const int ne = dense ? g1 - g0 : nnz;
-    const int64_t nrows = rows.count();
-    for (int64_t i = tid; i < nrows; i += nthr) {
-        const int64_t r = rows.row(i);
-        if (r < 0) continue;
-        const uint16_t *srow = scales + r * G;
-        const bool all = fold && fold_inexact(srow, g0, g1);
-        for (int m0 = 0; m0 < Mt; m0 += TB) {
-            float b[TB];
-#pragma unroll
-            for (int t = 0; t < TB; ++t) b[t] = 0.f;
-            if (!all) {
-                for (int e = 0; e < ne; ++e) {
-                    const int g = dense ? g0 + e : nz[e];
-                    const float s = fabsf(bf16_to_f32(srow[g]));
-#pragma unroll
-                    for (int t = 0; t < TB; ++t)
-                        if (m0 + t < Mt) b[t] = fmaf(s, d_at(m0 + t, g), b[t]);
-                }
-            }
-#pragma unroll
-            for (int t = 0; t < TB; ++t) {
-                const int m = m0 + t;
-                if (m < Mt && (all || !(4.0f * b[t] <= kFixBudget)))
-                    out[(int64_t)m * ldo + r] = exact_output(x + (int64_t)m * ldx, packed + r * W, srow, g0, g1);
-            }
-        }
-    }
-}
 
 // ------------------------------------------------------------- qpack -------
 // One thread per (row, group): 128 codes in, 12 words out (grid-stride loop).
@@ -580,664 +121,6 @@ __global__ __launch_bounds__(256) void qdequant_kernel(const uint32_t *__restric
                                                        uint16_t *__restrict__ w_out, int64_t chunks) {
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < chunks; i += (int64_t)gridDim.x * 256)
         dequant_chunk(packed, scales, w_out, i);
-}
-
-// ------------------------------------------------------------ qgemv -------
-// Batch-1 fused GEMV.  A team of T lanes owns one output row at a time; lane
-// g of the team owns weight group g (128 weights = 12 words = 48 contiguous
-// bytes), so the team's three 16-byte loads per lane cover the row
-// contiguously.  The lane's 128 activations stay in 64 VGPRs as fp16 pairs
-// for the whole kernel ("x-stationary").  R = WGS / T teams per workgroup walk
-// the rows in a grid-stride loop.  Each lane keeps a ring of D rows in flight:
-// the loads of row i + D are issued as soon as row i has been decoded, so the
-// memory system always holds D rows per team (the GEMV is latency-bound
-// without it).  Partial sums are reduced in a fixed order (DPP inside a wave,
-// then LDS across waves), so results are run-to-run identical.
-constexpr int kGemvDepth = 3;    // rows in flight per team
-constexpr int kGemvWGS = 256;     // threads per workgroup, teams of T <= 64
-constexpr size_t kMaxLdsX = 64 * 1024;
-
-struct RowBuf {
-    uint4 a, b, c;  // the lane's 12 words of the row
-    uint32_t s;     // the lane's bf16 scale
-};
-
-// Loads the lane's 12 words and scale of row r.  Every load is issued
-// unconditionally -- rows past the end read the last row, lanes without a
-// group read the last group -- so the code between loads is straight-line and
-// the compiler can wait for exactly the loads a step needs (s_waitcnt vmcnt(n))
-// instead of draining every load in flight.  The extra rows are never stored
-// and the extra groups meet zero activations.
-typedef unsigned u32x4v_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint4 load_words16(const uint32_t *p) { return *reinterpret_cast<const uint4 *>(p); }
-
-__device__ __forceinline__ void load_row(const uint32_t *__restrict__ packed, const uint16_t *__restrict__ scales,
-                                         int64_t r, int64_t N, int64_t W, int G, int g_load, RowBuf &rb) {
-    const int64_t rr = r < N ? r : N - 1;
-    const uint32_t *p = packed + rr * W + g_load * kWordsPerGroup;
-    rb.a = load_words16(p);
-    rb.b = load_words16(p + 4);
-    rb.c = load_words16(p + 8);
-    rb.s = scales[rr * G + g_load];
-}
-
-// sum_k q_k x'_k * 2^e * s over the lane's group of one row.
-__device__ __forceinline__ float row_partial(const RowBuf &rb, const uint32_t (&xp)[64], int e, uint32_t magic) {
-    const float a0 = dot_block(rb.a.x, rb.a.y, rb.a.z, magic, xp + 0, 0.f);
-    const float a1 = dot_block(rb.a.w, rb.b.x, rb.b.y, magic, xp + 16, 0.f);
-    const float a2 = dot_block(rb.b.z, rb.b.w, rb.c.x, magic, xp + 32, 0.f);
-    const float a3 = dot_block(rb.c.y, rb.c.z, rb.c.w, magic, xp + 48, 0.f);
-    return ldexpf((a0 + a1) + (a2 + a3), e) * bf16_to_f32(rb.s);
-}
-
-// Activation staging, LDS path.  The workgroup converts x once: 4 threads (a
-// quad) per group, one 32-value block each, U blocks per thread at most; then
-// every lane copies its own group's 64 pairs and exponent into registers.
-// Issue (raw loads) and finish (convert, exchange) are split so the row loads
-// can be issued in between.
-template <int U>
-struct XStage {
-    uint4 raw[U][4];
-};
-
-template <int U>
-__device__ __forceinline__ void xstage_issue(const uint16_t *__restrict__ x, int G, XStage<U> &st) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        int idx = threadIdx.x + u * blockDim.x;
-        if (idx >= 4 * G) idx = 4 * G - 1;  // clamped: always issued
-        load_x32(x + (size_t)(idx >> 2) * kGroup + (idx & 3) * 32, st.raw[u]);
-    }
-}
-
-// LDS layout of the converted activations: xs4[q][g] holds pairs 4q..4q+3 of
-// group g (16 bytes), q = 0..15, so that when lane g fetches its group the 64
-// lanes of each ds_read_b128 touch 64 consecutive 16-byte chunks (no bank
-// conflicts); exponents follow as int[G].  Returns whether this thread saw a
-// value below its group's surely-exact range (the guard's cheap test; the
-// conversion error itself is computed only then, by group_errors).
-template <int U>
-__device__ __forceinline__ bool xstage_convert(const XStage<U> &st, int G, uint32_t *smem) {
-    uint4 *xs4 = reinterpret_cast<uint4 *>(smem);                // [16][G]
-    int *xe = reinterpret_cast<int *>(smem + (size_t)G * 64);  // [G]
-    bool small = false;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int idx = threadIdx.x + u * blockDim.x;  // quads share validity: 4G and blockDim are multiples of 4
-        uint32_t m, mn;
-        block_stats(st.raw[u], m, mn);
-        m = max(m, dpp_u32<kDppQuadXor1>(m));
-        m = max(m, dpp_u32<kDppQuadXor2>(m));
-        if (idx < 4 * G) {
-            const int g = idx >> 2, blk = idx & 3;
-            const int eg = group_exponent(m);
-            small |= mn < exact_floor_bits(eg);
-            uint32_t out[16];
-            convert_block(st.raw[u], eg, out);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                xs4[(size_t)(4 * blk + i) * G + g] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
-            if (blk == 0) xe[g] = eg;
-        }
-    }
-    return small;
-}
-
-// The guard's error masses of a batch-1 activation vector, one exponent per
-// group as in the staging: xd[g] = conversion_error summed over group g.  All
-// threads of the workgroup call it (it ends with a barrier).
-__device__ __forceinline__ void group_errors(const uint16_t *__restrict__ x, int G, float *xd) {
-    for (int u = threadIdx.x; u < 4 * G; u += blockDim.x) {  // a quad of threads per group
-        uint4 xb[4];
-        load_x32(x + (size_t)(u >> 2) * kGroup + (u & 3) * 32, xb);
-        uint32_t m, mn;
-        block_stats(xb, m, mn);
-        m = max(m, dpp_u32<kDppQuadXor1>(m));
-        m = max(m, dpp_u32<kDppQuadXor2>(m));
-        float d = conversion_error(xb, group_exponent(m));
-        d += dpp_f32<kDppQuadXor1>(d);
-        d += dpp_f32<kDppQuadXor2>(d);
-        if ((u & 3) == 0) xd[u >> 2] = d;
-    }
-    __syncthreads();
-}
-
-// The same for the batched kernels that convert in-kernel: tokens t < M (x
-// row t at x + t * K), one exponent per (token, 8-group slice), the slices of
-// groups [g0, g0 + 8 S): xd[t][g - g0].  Half a wave per (token, slice).
-__device__ __forceinline__ void slice_errors(const uint16_t *__restrict__ x, int64_t K, int M, int g0, int S,
-                                             float *xd) {
-    const int units = M * S * 32;
-    for (int u = threadIdx.x; u < units; u += blockDim.x) {  // units and blockDim are multiples of 32
-        const int b = u & 3, gi = (u >> 2) & 7, ts = u >> 5;
-        const int t = ts / S, sl = ts % S;
-        uint4 xb[4];
-        load_x32(x + t * K + (int64_t)(g0 + 8 * sl + gi) * kGroup + 32 * b, xb);
-        uint32_t m, mn;
-        block_stats(xb, m, mn);
-#pragma unroll
-        for (int off = 1; off < 32; off <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 32));
-        float d = conversion_error(xb, group_exponent(m));
-        d += dpp_f32<kDppQuadXor1>(d);
-        d += dpp_f32<kDppQuadXor2>(d);
-        if (b == 0) xd[t * (8 * S) + 8 * sl + gi] = d;
-    }
-    __syncthreads();
-}
-
-// One word per wave in LDS: whether any lane of the wave passed `mine`.
-__device__ __forceinline__ void publish_flag(bool mine, uint32_t *flags) {
-    const uint64_t bal = __ballot(mine);
-    if ((threadIdx.x & 63) == 0) flags[threadIdx.x >> 6] = bal != 0 ? 1u : 0u;
-}
-__device__ __forceinline__ bool any_flag(const uint32_t *flags) {
-    uint32_t f = 0;
-    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) f |= flags[w];
-    return f != 0;
-}
-
-// After a barrier: this lane's pairs and exponent (zeros for lanes without a group).
-__device__ __forceinline__ void xstage_fetch(const uint32_t *smem, int G, int gl, bool lane_on,
-                                             uint32_t (&xp)[64], int &e) {
-    const int *xe = reinterpret_cast<const int *>(smem + (size_t)G * 64);
-    const int gs = lane_on ? gl : 0;
-    const uint4 *xs4 = reinterpret_cast<const uint4 *>(smem);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const uint4 v = xs4[(size_t)i * G + gs];
-        xp[4 * i] = lane_on ? v.x : 0u;
-        xp[4 * i + 1] = lane_on ? v.y : 0u;
-        xp[4 * i + 2] = lane_on ? v.z : 0u;
-        xp[4 * i + 3] = lane_on ? v.w : 0u;
-    }
-    e = lane_on ? xe[gs] : 0;
-}
-
-// Activation staging without LDS (very long rows): each lane converts its own
-// group in two passes (max, then convert).  Returns the guard's cheap test
-// for the group (a value below its surely-exact range).
-__device__ __forceinline__ bool xstage_lane(const uint16_t *__restrict__ x, int gl, bool lane_on,
-                                            uint32_t (&xp)[64], int &e) {
-    const uint16_t *xg = x + (size_t)(lane_on ? gl : 0) * kGroup;
-    uint32_t m = 0, mn = 0x10000u;
-#pragma unroll
-    for (int blk = 0; blk < 4; ++blk) {
-        uint4 xb[4];
-        load_x32(xg + blk * 32, xb);
-        uint32_t bm, bn;
-        block_stats(xb, bm, bn);
-        m = max(m, bm);
-        mn = min(mn, bn);
-    }
-    e = group_exponent(m);
-    const bool small = lane_on && mn < exact_floor_bits(e);
-#pragma unroll
-    for (int blk = 0; blk < 4; ++blk) {
-        uint4 xb[4];
-        load_x32(xg + blk * 32, xb);
-        uint32_t out[16];
-        convert_block(xb, e, out);
-#pragma unroll
-        for (int p = 0; p < 16; ++p) xp[blk * 16 + p] = lane_on ? out[p] : 0u;
-    }
-    if (!lane_on) e = 0;
-    return small;
-}
-
-// Up to 4 weight matrices with the same K that share one activation vector
-// (e.g. the q, k and v projections of a layer) in one launch (one activation
-// staging): the workgroups are dealt to the matrices in proportion to their
-// rows, so each workgroup works on one matrix and its pointers stay uniform.
-constexpr int kMaxSegs = 4;
-struct GemvSegs {
-    const uint32_t *packed[kMaxSegs];
-    const uint16_t *scales[kMaxSegs];
-    float *y[kMaxSegs];
-    int64_t rows[kMaxSegs];
-    int blk_end[kMaxSegs];  // cumulative workgroup counts; unused entries repeat the total
-};
-
-template <typename P>
-__device__ __forceinline__ P seg_pick(const P (&v)[kMaxSegs], int k) {
-    return k == 0 ? v[0] : (k == 1 ? v[1] : (k == 2 ? v[2] : v[3]));
-}
-
-// Teams of T <= 64 lanes (T a power of two >= G): the reduction is DPP only.
-// Order of the prologue: activation loads, then the first D rows, then the
-// conversion (which waits only for the activation loads).
-// LDS words of the batch-1 staging for G groups: xs4 [16][G] x 16 B and xe [G],
-// then xd [G] (error masses), 16 wave flags and the fixup's group list.
-__host__ __device__ constexpr size_t stage_words(int G) { return (size_t)G * 66 + 16 + kNzCap + 1; }
-
-template <int T, bool MULTI, int D>
-__global__ __launch_bounds__(kGemvWGS) void qgemv_small_kernel(const uint16_t *__restrict__ x,
-                                                               const GemvSegs sg, int G) {
-    constexpr int R = kGemvWGS / T;
-    extern __shared__ uint32_t smem[];
-    x += (int64_t)blockIdx.y * G * kGroup;  // token blockIdx.y (one token unless batch-invariant)
-    float *xd = reinterpret_cast<float *>(smem + (size_t)G * 65);
-    uint32_t *flags = smem + (size_t)G * 66;
-    int *nz = reinterpret_cast<int *>(flags + 16);
-    // This workgroup's matrix (workgroup-uniform) and its place among the
-    // workgroups of that matrix.
-    int kseg = 0, blk = blockIdx.x, nblk = gridDim.x;
-    if constexpr (MULTI) {
-        kseg = ((int)blockIdx.x >= sg.blk_end[0]) + ((int)blockIdx.x >= sg.blk_end[1]) +
-               ((int)blockIdx.x >= sg.blk_end[2]);
-        const int b0 = kseg == 0 ? 0 : seg_pick(sg.blk_end, kseg - 1);
-        blk = blockIdx.x - b0;
-        nblk = seg_pick(sg.blk_end, kseg) - b0;
-    }
-    const uint32_t *__restrict__ packed = MULTI ? seg_pick(sg.packed, kseg) : sg.packed[0];
-    const uint16_t *__restrict__ scales = MULTI ? seg_pick(sg.scales, kseg) : sg.scales[0];
-    const int64_t N = MULTI ? seg_pick(sg.rows, kseg) : sg.rows[0];
-    float *__restrict__ y = (MULTI ? seg_pick(sg.y, kseg) : sg.y[0]) + (int64_t)blockIdx.y * N;
-    const int gl = threadIdx.x % T;
-    const bool lane_on = gl < G;
-    const int g_load = lane_on ? gl : G - 1;
-    const int64_t W = (int64_t)G * kWordsPerGroup;
-    const int64_t stride = (int64_t)nblk * R;
-    const int64_t row0 = (int64_t)blk * R + threadIdx.x / T;
-    auto load = [&](int64_t r, RowBuf &rb) { load_row(packed, scales, r, N, W, G, g_load, rb); };
-
-    // Ring of E = D + 1 row buffers.  Step i first issues the loads of row
-    // i + D into the buffer that step i - 1 finished with, then decodes row i:
-    // D rows are in flight while a row is decoded (the scheduling barrier
-    // keeps the compiler from sinking the loads behind the decode).
-    constexpr int E = D + 1;
-    uint32_t xp[64];
-    int e = 0;
-    RowBuf ring[E];
-    {
-        XStage<1> st;  // 4G <= 256 <= blockDim: one block per thread
-        xstage_issue<1>(x, G, st);
-#pragma unroll
-        for (int d = 0; d < D; ++d) load(row0 + d * stride, ring[d]);
-        publish_flag(xstage_convert<1>(st, G, smem), flags);
-        __syncthreads();
-        xstage_fetch(smem, G, gl, lane_on, xp, e);
-    }
-    const bool fix = __builtin_amdgcn_readfirstlane(any_flag(flags) ? 1 : 0) != 0;  // the guard, workgroup-uniform
-    const uint32_t magic = magic_vgpr();
-
-    for (int64_t row = row0; row < N; row += E * stride) {
-#pragma unroll
-        for (int i = 0; i < E; ++i) {
-            const int64_t r = row + i * stride;
-            load(r + D * stride, ring[(i + D) % E]);
-            __builtin_amdgcn_sched_barrier(0);
-            const float part = row_partial(ring[i], xp, e, magic);
-            const float tot = segment_sum<T>(part);
-            if (gl == T - 1 && r < N) y[r] = tot;
-        }
-    }
-    if (fix) {  // rare
-        __syncthreads();
-        group_errors(x, G, xd);
-        const int nnz = build_nz(0, G, [&](int g) { return xd[g] != 0.f; }, nz);
-        fixup_outputs<1>(x, 0, 1, packed, scales, G, 0, G, BlockRows{blk, nblk, R, N},
-                         [&](int, int g) { return xd[g]; }, nz, nnz, false, y, 0, threadIdx.x, blockDim.x);
-    }
-}
-
-// Workgroup barrier for LDS hand-offs: waits for this wave's LDS operations
-// only, so its global loads stay in flight across the barrier, and the
-// "memory" clobber keeps the compiler from moving memory accesses across it.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// Teams of T > 64 lanes, T a multiple of 32 (>= G): each half-wave sums its 32
-// lanes with DPP, the half sums go through LDS, and lane 0 of the team adds
-// its T/32 halves in order.  One barrier per D + 1 rows.  1024-thread
-// workgroups (K > 65536) keep a single row in flight to stay within 128 VGPRs.  The LDS holds the
-// converted activations first, then (after a barrier) the half sums.
-// LDS_X: the converted activations fit in LDS (K <= 32768); otherwise each
-// lane converts its own group.  A template parameter, so that one prologue
-// reaches the loop and the loop's waits are exact.
-// The batch-1 fixup out of line, for kernels held to 128 VGPRs (1024-thread
-// workgroups), where the inlined pass would crowd the main loop's registers.
-__device__ __noinline__ void fixup_m1_call(const uint16_t *x, const uint32_t *packed, const uint16_t *scales, float *y,
-                                           int G, BlockRows rows, const float *xd, const int *nz, int nnz, int tid,
-                                           int nthr) {
-    fixup_outputs<1>(x, 0, 1, packed, scales, G, 0, G, rows, [&](int, int g) { return xd[g]; }, nz, nnz, false, y, 0,
-                     tid, nthr);
-}
-
-constexpr int kBigRedWords = 256;  // half-sum slots of qgemv_big_kernel: 2 (E <= 4) x E x (<= 32 halves)
-// LDS words of qgemv_big_kernel: the staging (LDS_X) or the half sums, then
-// xd [G], 16 wave flags and the fixup's group list.
-__host__ __device__ constexpr size_t big_xd_at(int G, bool lds_x) { return lds_x ? (size_t)G * 65 : kBigRedWords; }
-__host__ __device__ constexpr size_t big_words(int G, bool lds_x) { return big_xd_at(G, lds_x) + G + 16 + kNzCap + 1; }
-
-template <int MAXWGS, int D, bool LDS_X>
-__global__ __launch_bounds__(MAXWGS) void qgemv_big_kernel(const uint16_t *__restrict__ x,
-                                                         const uint32_t *__restrict__ packed,
-                                                         const uint16_t *__restrict__ scales,
-                                                         float *__restrict__ y, int64_t N, int G, int T) {
-    extern __shared__ uint32_t smem[];
-    x += (int64_t)blockIdx.y * G * kGroup;  // token blockIdx.y (one token unless batch-invariant)
-    y += (int64_t)blockIdx.y * N;
-    float *xd = reinterpret_cast<float *>(smem + big_xd_at(G, LDS_X));
-    uint32_t *flags = smem + big_xd_at(G, LDS_X) + G;
-    int *nz = reinterpret_cast<int *>(flags + 16);
-    const int tid = threadIdx.x;
-    const int wgs = blockDim.x;
-    const int R = wgs / T;
-    const int gl = tid % T;
-    const int team = tid / T;
-    const int halves = T / 32;
-    const bool lane_on = gl < G;
-    const int g_load = lane_on ? gl : G - 1;
-    const int64_t W = (int64_t)G * kWordsPerGroup;
-    const int64_t stride = (int64_t)gridDim.x * R;
-    const int64_t row0 = (int64_t)blockIdx.x * R + team;
-
-    // Issue-first ring of E = D + 1 row buffers, as in qgemv_small_kernel.
-    constexpr int E = D + 1;
-    static_assert(2 * E * 32 <= kBigRedWords, "half-sum slots");
-    uint32_t xp[64];
-    int e = 0;
-    RowBuf ring[E];
-    bool fix = false;
-    if constexpr (LDS_X) {
-        XStage<4> st;  // 4G <= 4 * blockDim (T >= G, blockDim >= T)
-        xstage_issue<4>(x, G, st);
-#pragma unroll
-        for (int d = 0; d < D; ++d) {
-            __builtin_amdgcn_sched_barrier(0);  // rows issued in ring order
-            load_row(packed, scales, row0 + d * stride, N, W, G, g_load, ring[d]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        publish_flag(xstage_convert<4>(st, G, smem), flags);
-        __syncthreads();
-        xstage_fetch(smem, G, gl, lane_on, xp, e);
-        fix = __builtin_amdgcn_readfirstlane(any_flag(flags) ? 1 : 0) != 0;  // the guard, workgroup-uniform
-        __syncthreads();  // LDS is reused for the half sums below
-    } else {
-#pragma unroll
-        for (int d = 0; d < D; ++d) {
-            __builtin_amdgcn_sched_barrier(0);
-            load_row(packed, scales, row0 + d * stride, N, W, G, g_load, ring[d]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        publish_flag(xstage_lane(x, gl, lane_on, xp, e), flags);  // read after the loop's barriers
-    }
-    const uint32_t magic = magic_vgpr();
-
-    float *red = reinterpret_cast<float *>(smem);  // [2][E][wgs/32]
-    int parity = 0;
-    for (int64_t base = (int64_t)blockIdx.x * R; base < N; base += E * stride) {  // WG-uniform
-        const int64_t row = base + team;
-        float *slot = red + parity * E * (wgs / 32);
-#pragma unroll
-        for (int i = 0; i < E; ++i) {
-            const int64_t r = row + i * stride;
-            load_row(packed, scales, r + D * stride, N, W, G, g_load, ring[(i + D) % E]);
-            __builtin_amdgcn_sched_barrier(0);
-            const float part = row_partial(ring[i], xp, e, magic);
-            const float hs = segment_sum<32>(part);
-            if ((tid & 31) == 31) slot[i * (wgs / 32) + (tid >> 5)] = hs;
-        }
-        // Half sums written (lgkmcnt) before the barrier; global loads stay in
-        // flight (a __syncthreads fence would wait for them too).
-        lds_barrier();
-        if (gl == 0) {
-#pragma unroll
-            for (int i = 0; i < E; ++i) {
-                const int64_t r = row + i * stride;
-                if (r < N) {
-                    float tot = 0.f;
-                    for (int h = 0; h < halves; ++h) tot += slot[i * (wgs / 32) + team * halves + h];
-                    y[r] = tot;
-                }
-            }
-        }
-        parity ^= 1;
-    }
-    if (!LDS_X) fix = any_flag(flags);  // published before the loop's barriers
-    if (fix) {  // workgroup-uniform, rare
-        __syncthreads();
-        group_errors(x, G, xd);
-        const int nnz = build_nz(0, G, [&](int g) { return xd[g] != 0.f; }, nz);
-        const BlockRows rows{(int64_t)blockIdx.x, (int64_t)gridDim.x, R, N};
-        if constexpr (MAXWGS > 512)
-            fixup_m1_call(x, packed, scales, y, G, rows, xd, nz, nnz, tid, wgs);
-        else
-            fixup_outputs<1>(x, 0, 1, packed, scales, G, 0, G, rows, [&](int, int g) { return xd[g]; }, nz, nnz, false,
-                             y, 0, tid, wgs);
-    }
-}
-
-// Calls f(std::integral_constant<int, i>{}) for i = 0 .. C - 1, each index a
-// compile-time constant (register-ring slots must be static).
-template <int I, int C, typename F>
-__device__ __forceinline__ void static_for_from(F &&f) {
-    if constexpr (I < C) {
-        f(std::integral_constant<int, I>{});
-        static_for_from<I + 1, C>(f);
-    }
-}
-template <int C, typename F>
-__device__ __forceinline__ void static_for(F &&f) {
-    static_for_from<0, C>(f);
-}
-
-// ------------------------------------- batch 1, K = 8192, on the matrix cores --
-// The same fused GEMV with the dot products on v_mfma_f32_16x16x32_f16, which
-// leaves two VALU ops per weight pair (the exact decode) instead of three.
-// Workgroups of four waves walk 16-row tiles; wave w owns the 16 groups
-// 16q + 4w + j (q, j = 0..3) of every row of a tile, so the four waves together
-// cover K = 8192 and a tile's super-step q reads bytes [768q, 768q + 768) of
-// each of its rows.  In super-step q, lane (n, j) (n = lane % 16, j = lane / 16)
-// decodes group 16q + 4w + j of row n straight into the B operand (k chunk j
-// of 8 weights, 4 MFMAs per 32-code block).  The A operand is x' and stays in
-// 64 VGPRs for the whole kernel: row m = 4q' + j' of A carries the activations
-// of group 16q' + 4w + j' in k chunk j' and zero elsewhere.  So output row
-// 4q' + j' only ever sums products of group 16q' + 4w + j' activations; in
-// super-step q the rows 4q..4q+3 hold the partial sums of groups 16q + 4w + r
-// (r = 0..3) exactly apart, in lane row q, and the other 12 rows are discarded.
-// Those four partials are multiplied by their group scale (and the
-// activation exponent) and accumulated in fp32.  The wave's per-row partials
-// are summed across lane rows with permlane swaps and across the four waves
-// through LDS, in a fixed order, once per batch of tiles.  Loads run three
-// super-steps ahead in a register ring, as in qgemv_small_kernel.
-constexpr int kMfBatch = 8;  // tiles per cross-wave reduction
-constexpr int kMfRing = 4;   // register ring slots (one super-step each)
-constexpr int kMfAhead = 3;  // super-steps loaded ahead of the one decoded
-// LDS: the converted activations (xs4, xe), the partial sums
-// [2][kMfBatch][WAVES][16], then xd [G], 16 wave flags and the fixup's list.
-template <int WAVES>
-constexpr size_t mf_red_words() { return (size_t)2 * kMfBatch * WAVES * 16; }
-template <int GPW, int WAVES>
-constexpr size_t mf_lds() {
-    return ((size_t)GPW * WAVES * 66 + mf_red_words<WAVES>() + 16 + kNzCap + 1) * 4;
-}
-typedef unsigned u32x2v_t __attribute__((ext_vector_type(2)));
-struct MfSlot {
-    u32x4v_t a, b, c;  // the lane's 12 words of one group of one row
-    u32x2v_t s;        // (super-steps 0 and 4) the bf16 scales of lane row j's four groups
-};
-
-// First of the four groups that wave w (of WAVES, GPW groups each) handles in
-// super-step q.
-template <int GPW, int WAVES>
-__device__ __forceinline__ int mf_group(int w, int q) {
-    return 4 * WAVES * q + 4 * w;
-}
-
-// GPW groups per wave: 16 (K = 8192, 4 waves) or 32 (K = 28672, 7 waves).  A
-// wave then walks GPW / 4 super-steps per tile, and its activations are GPW /
-// 16 A-operand sets: set a serves super-steps 4a .. 4a + 3 with rows
-// m = 4(q mod 4) + j' as above.
-template <int GPW, int WAVES, bool MULTI>
-__global__ __launch_bounds__(64 * WAVES) void qgemv_mfma_kernel(const uint16_t *__restrict__ x, const GemvSegs sg) {
-    constexpr int G = GPW * WAVES;
-    constexpr int NS = GPW / 4;   // super-steps per tile
-    constexpr int AS = GPW / 16;  // A-operand sets
-    constexpr int XU = (4 * G + 64 * WAVES - 1) / (64 * WAVES);  // activation blocks per thread
-    constexpr int64_t W = (int64_t)G * kWordsPerGroup;
-    static_assert(NS % 4 == 0, "whole A-operand sets");
-    extern __shared__ uint32_t smem[];
-    float *red = reinterpret_cast<float *>(smem + G * 64 + G);  // [2][kMfBatch][WAVES][16 rows]
-    float *xd = reinterpret_cast<float *>(smem + G * 65 + mf_red_words<WAVES>());
-    uint32_t *flags = smem + G * 66 + mf_red_words<WAVES>();
-    int *nz = reinterpret_cast<int *>(flags + 16);
-    int kseg = 0, blk = blockIdx.x, nblk = gridDim.x;
-    if constexpr (MULTI) {
-        kseg = ((int)blockIdx.x >= sg.blk_end[0]) + ((int)blockIdx.x >= sg.blk_end[1]) +
-               ((int)blockIdx.x >= sg.blk_end[2]);
-        const int b0 = kseg == 0 ? 0 : seg_pick(sg.blk_end, kseg - 1);
-        blk = blockIdx.x - b0;
-        nblk = seg_pick(sg.blk_end, kseg) - b0;
-    }
-    const uint32_t *__restrict__ packed = MULTI ? seg_pick(sg.packed, kseg) : sg.packed[0];
-    const uint16_t *__restrict__ scales = MULTI ? seg_pick(sg.scales, kseg) : sg.scales[0];
-    const int64_t N = MULTI ? seg_pick(sg.rows, kseg) : sg.rows[0];
-    // token blockIdx.y (one token unless batch-invariant)
-    float *__restrict__ y = (MULTI ? seg_pick(sg.y, kseg) : sg.y[0]) + (int64_t)blockIdx.y * N;
-    x += (int64_t)blockIdx.y * G * kGroup;
-    const int lane = threadIdx.x & 63;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int n = lane & 15, lj = lane >> 4;
-    const int64_t my_tiles = (((N + 15) >> 4) - blk + nblk - 1) / nblk;  // >= 1: at most one workgroup per tile
-    // Unconditional loads (see load_row): tiles past the last re-read it, rows past N read row N - 1.
-    auto load = [&](int64_t it, int q, MfSlot &sl) {
-        it = it < my_tiles ? it : my_tiles - 1;
-        int64_t r = (blk + it * nblk) * 16 + n;
-        r = r < N ? r : N - 1;
-        const u32x4v_t *p =
-            reinterpret_cast<const u32x4v_t *>(packed + r * W + (mf_group<GPW, WAVES>(w, q) + lj) * kWordsPerGroup);
-        sl.a = p[0];
-        sl.b = p[1];
-        sl.c = p[2];
-        if (q % 4 == 0)
-            sl.s = *reinterpret_cast<const u32x2v_t *>(scales + r * G + mf_group<GPW, WAVES>(w, q + lj));
-    };
-    // Steps are numbered s = NS * tile + q; step s lives in ring slot s % RS.
-    // The body covers UT tiles, a whole number of ring cycles, so every slot
-    // index is static.
-    constexpr int RS = kMfRing, AH = kMfAhead;
-    constexpr int UT = RS > NS ? RS / NS : 1;
-    static_assert(AH < RS && (RS % NS == 0 || NS % RS == 0), "ring cycles must tile the super-steps");
-    MfSlot ring[RS];
-    XStage<XU> st;
-    xstage_issue<XU>(x, G, st);
-    // Issued strictly in ring order: the waits in the loop count on it.
-#pragma unroll
-    for (int s = 0; s < AH; ++s) {
-        load(s / NS, s % NS, ring[s % RS]);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    publish_flag(xstage_convert<XU>(st, G, smem), flags);
-    __syncthreads();
-    const bool fix = __builtin_amdgcn_readfirstlane(any_flag(flags) ? 1 : 0) != 0;  // the guard, workgroup-uniform
-    h8_t xa[AS][16];  // step t = 4 * block + u: pairs 4u .. 4u + 3 of 32-code block `block`
-    float fe[AS][4];  // 2^e of the groups whose partials this lane scales (lane row lj of each set)
-    {
-        const bool on = (n & 3) == lj;
-        const uint4 *xs4 = reinterpret_cast<const uint4 *>(smem);
-        const int *xe = reinterpret_cast<const int *>(smem + G * 64);
-#pragma unroll
-        for (int a = 0; a < AS; ++a) {
-            const int ga = mf_group<GPW, WAVES>(w, 4 * a + (n >> 2)) + lj;
-#pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                const uint4 v = xs4[t * G + ga];
-                xa[a][t] = on ? __builtin_bit_cast(h8_t, v) : h8_t{0, 0, 0, 0, 0, 0, 0, 0};
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) fe[a][r] = ldexpf(1.0f, xe[mf_group<GPW, WAVES>(w, 4 * a + lj) + r]);
-        }
-    }
-    const uint32_t magic = magic_vgpr();
-    // Tile it0 + h, whose super-steps are ring steps h * NS + q.
-    auto tile = [&](int64_t it0, auto hc) __attribute__((always_inline)) {
-        constexpr int h = decltype(hc)::value;
-        const int64_t it = it0 + h;
-        float acc[4] = {0.f, 0.f, 0.f, 0.f}, sc[AS][4];
-#pragma unroll
-        for (int q = 0; q < NS; ++q) {
-            // refill the slot freed by the previous step with the step AH ahead
-            const int u = h * NS + q;
-            load(it0 + (u + AH) / NS, (u + AH) % NS, ring[(u + AH) % RS]);
-            __builtin_amdgcn_sched_barrier(0);
-            const MfSlot &sl = ring[u % RS];
-            const int a = q / 4;
-            if (q % 4 == 0) {
-                sc[a][0] = bf16_to_f32(sl.s.x & 0xFFFFu) * fe[a][0];
-                sc[a][1] = __uint_as_float(sl.s.x & 0xFFFF0000u) * fe[a][1];
-                sc[a][2] = bf16_to_f32(sl.s.y & 0xFFFFu) * fe[a][2];
-                sc[a][3] = __uint_as_float(sl.s.y & 0xFFFF0000u) * fe[a][3];
-            }
-            const uint32_t wd[12] = {sl.a.x, sl.a.y, sl.a.z, sl.a.w, sl.b.x, sl.b.y,
-                                     sl.b.z, sl.b.w, sl.c.x, sl.c.y, sl.c.z, sl.c.w};
-            f4_t d = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                h2_t qd[16];
-                decode_block(wd[3 * b], wd[3 * b + 1], wd[3 * b + 2], magic, qd);
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const h8_t bop = {qd[4 * v].x,     qd[4 * v].y,     qd[4 * v + 1].x, qd[4 * v + 1].y,
-                                      qd[4 * v + 2].x, qd[4 * v + 2].y, qd[4 * v + 3].x, qd[4 * v + 3].y};
-                    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[a][4 * b + v], bop, d, 0, 0, 0);
-                }
-            }
-            if (lj == q % 4) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) acc[r] = fmaf(d[r], sc[a][r], acc[r]);
-            }
-        }
-        // Row n's partial over the wave's groups: the four lane rows, then LDS.
-        float part = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-        const auto s32 =
-            __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
-        part = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
-        const auto s16 =
-            __builtin_amdgcn_permlane16_swap(__float_as_uint(part), __float_as_uint(part), false, false);
-        part = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
-        const int bt = (int)(it % kMfBatch);
-        float *rb = red + ((it / kMfBatch) & 1) * (kMfBatch * WAVES * 16);
-        if (lj == 0) rb[(bt * WAVES + w) * 16 + n] = part;
-        if (bt == kMfBatch - 1 || it == my_tiles - 1) {
-            // The batch's partials are in LDS (lgkmcnt) before the barrier; the
-            // loads of the next tiles stay in flight.  The other half of `red`
-            // is written next, so one barrier per batch suffices.
-            lds_barrier();
-            const int i = threadIdx.x;
-            if (i < (bt + 1) * 16) {
-                const float *rr = rb + (i >> 4) * WAVES * 16 + (i & 15);
-                float tot = rr[0];
-#pragma unroll
-                for (int v = 1; v < WAVES; ++v) tot += rr[16 * v];
-                const int64_t row = (blk + (it - bt + (i >> 4)) * nblk) * 16 + (i & 15);
-                if (row < N) y[row] = tot;
-            }
-        }
-    };
-    // Whole ring cycles in the loop, so its back edge always carries the same
-    // pending loads (exact waits); a ragged last cycle follows it.
-    int64_t it0 = 0;
-    for (; it0 + UT <= my_tiles; it0 += UT)
-        static_for<UT>([&](auto hc) __attribute__((always_inline)) { tile(it0, hc); });
-    static_for<UT - 1>([&](auto hc) __attribute__((always_inline)) {
-        if (it0 + decltype(hc)::value < my_tiles) tile(it0, hc);
-    });
-    // Slots whose loads (past the last tile) are still in flight at the loop's
-    // exit and that the ragged cycle does not read: held until here, so their
-    // registers are not reused -- which would first wait for those loads.
-    if constexpr (UT > 1)
-        static_for<RS>([&ring](auto ic) __attribute__((always_inline)) {
-            constexpr int i = decltype(ic)::value;
-            if constexpr (i >= NS * (UT - 1) && i < AH)
-                asm volatile("" ::"v"(ring[i].a), "v"(ring[i].b), "v"(ring[i].c), "v"(ring[i].s));
-        });
-    if (fix) {  // rare
-        __syncthreads();
-        group_errors(x, G, xd);
-        const int nnz = build_nz(0, G, [&](int g) { return xd[g] != 0.f; }, nz);
-        fixup_outputs<1>(x, 0, 1, packed, scales, G, 0, G, BlockRows{blk, nblk, 16, N},
-                         [&](int, int g) { return xd[g]; }, nz, nnz, false, y, 0, threadIdx.x, blockDim.x);
-    }
 }
 
 // ----------------------------------------------- small-M matrix cores -----
@@ -2636,46 +1519,6 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float *__restrict__ y, i
 }
 
 // ------------------------------------------------------------ host side ---
-thread_local char g_hip_error[256] = "no HIP error";
-
-qw3_status hip_fail(hipError_t err) {
-    snprintf(g_hip_error, sizeof g_hip_error, "%s (%d)", hipGetErrorString(err), (int)err);
-    return QW3_ERR_HIP;
-}
-
-qw3_status check_launch() {
-    const hipError_t err = hipGetLastError();
-    return err == hipSuccess ? QW3_OK : hip_fail(err);
-}
-
-bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
-
-qw3_status check_shape(int64_t N, int64_t K) {
-    if (N < 0 || K < 0 || K % kGroup != 0 || K > QW3_MAX_K || N > (int64_t(1) << 40)) return QW3_ERR_SHAPE;
-    return QW3_OK;
-}
-
-std::mutex g_dev_mutex;
-int g_cu_count[64];
-
-qw3_status cu_count(int *out) {
-    int dev = 0;
-    hipError_t err = hipGetDevice(&dev);
-    if (err != hipSuccess) return hip_fail(err);
-    std::lock_guard<std::mutex> lock(g_dev_mutex);
-    if (dev < 0 || dev >= 64) return hip_fail(hipErrorInvalidDevice);
-    if (g_cu_count[dev] == 0) {
-        int cus = 0;
-        err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        if (err != hipSuccess) return hip_fail(err);
-        g_cu_count[dev] = cus > 0 ? cus : 1;
-    }
-    *out = g_cu_count[dev];
-    return QW3_OK;
-}
-
-int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
-
 // Device scratch of the batched-decode and prefill paths: converted
 // activations, the guard's error masses and K-chunk partial sums.
 //
@@ -2792,203 +1635,6 @@ qw3_status fill_zero(float *y, int64_t n, hipStream_t stream) {
     return check_launch();
 }
 
-// Workgroups of `kernel` that fit on one CU at `wgs` threads and `lds` bytes.
-qw3_status blocks_per_cu(const void *kernel, int wgs, size_t lds, int *out) {
-    int nb = 0;
-    const hipError_t err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, wgs, lds);
-    if (err != hipSuccess) return hip_fail(err);
-    *out = nb > 0 ? nb : 1;
-    return QW3_OK;
-}
-
-template <int T, bool MULTI>
-qw3_status launch_gemv_small(const uint16_t *x, GemvSegs sg, int count, int G, hipStream_t stream, int M) {
-    constexpr int R = kGemvWGS / T;
-    const size_t lds = stage_words(G) * 4;
-    const void *kern = reinterpret_cast<const void *>(&qgemv_small_kernel<T, MULTI, kGemvDepth>);
-    int cus = 0, per_cu = 0;
-    qw3_status st = cu_count(&cus);
-    if (st == QW3_OK) st = blocks_per_cu(kern, kGemvWGS, lds, &per_cu);
-    if (st != QW3_OK) return st;
-    if (per_cu > 1) per_cu = 1;  // one workgroup per CU: more bytes in flight measured slower
-    const int64_t budget = (int64_t)cus * per_cu;
-    int64_t tot = 0;
-    for (int i = 0; i < count; ++i) tot += sg.rows[i];
-    // Workgroups per matrix: in proportion to its rows (rounded down, so the
-    // total stays within one workgroup per CU), at least one for a non-empty
-    // matrix, at most one per R rows.
-    int64_t blocks = 0;
-    for (int i = 0; i < kMaxSegs; ++i) {
-        int64_t b = 0;
-        if (i < count && sg.rows[i] > 0) {
-            b = budget * sg.rows[i] / tot;
-            const int64_t cap = ceil_div(sg.rows[i], R);
-            b = b < 1 ? 1 : (b > cap ? cap : b);
-        }
-        blocks += b;
-        sg.blk_end[i] = (int)blocks;
-    }
-    // Waves with at most two rows each keep one row in flight instead of
-    // kGemvDepth (deeper rings would only re-read the last row).
-    const int64_t rows_per_wave = ceil_div(tot, blocks * R);
-    if (rows_per_wave <= 2)
-        hipLaunchKernelGGL((qgemv_small_kernel<T, MULTI, 1>), dim3((unsigned)blocks, (unsigned)M), dim3(kGemvWGS),
-                           lds, stream, x, sg, G);
-    else
-        hipLaunchKernelGGL((qgemv_small_kernel<T, MULTI, kGemvDepth>), dim3((unsigned)blocks, (unsigned)M),
-                           dim3(kGemvWGS), lds, stream, x, sg, G);
-    return check_launch();
-}
-
-template <bool MULTI>
-qw3_status launch_gemv_small_any(const uint16_t *x, const GemvSegs &sg, int count, int G, hipStream_t stream,
-                                 int M = 1) {
-    if (G <= 1) return launch_gemv_small<1, MULTI>(x, sg, count, G, stream, M);
-    if (G <= 2) return launch_gemv_small<2, MULTI>(x, sg, count, G, stream, M);
-    if (G <= 4) return launch_gemv_small<4, MULTI>(x, sg, count, G, stream, M);
-    if (G <= 8) return launch_gemv_small<8, MULTI>(x, sg, count, G, stream, M);
-    if (G <= 16) return launch_gemv_small<16, MULTI>(x, sg, count, G, stream, M);
-    if (G <= 32) return launch_gemv_small<32, MULTI>(x, sg, count, G, stream, M);
-    return launch_gemv_small<64, MULTI>(x, sg, count, G, stream, M);
-}
-
-qw3_status launch_gemv_big(const uint16_t *x, const uint32_t *packed, const uint16_t *scales, float *y,
-                           int64_t N, int G, hipStream_t stream, int M) {
-    // Team of T >= G lanes, T a multiple of 32; the workgroup holds whole
-    // waves and at most 1024 threads (T <= 1024 since K <= QW3_MAX_K).
-    int T = 32 * ((G + 31) / 32);
-    int R = T >= 512 ? 1 : 512 / T;
-    int wgs = T * R;
-    if (wgs % 64 != 0) {
-        if (2 * wgs <= 1024) {
-            R *= 2;
-            wgs *= 2;
-        } else {
-            T = 64 * ((G + 63) / 64);
-            R = 1;
-            wgs = T;
-        }
-    }
-    const bool lds_x = (size_t)G * 65 * 4 <= kMaxLdsX;
-    constexpr int kBigD = kGemvDepth, kHugeD = 1;
-    const size_t lds = big_words(G, lds_x) * 4;
-    const void *kern =
-        wgs <= 512 ? (lds_x ? reinterpret_cast<const void *>(&qgemv_big_kernel<512, kBigD, true>)
-                            : reinterpret_cast<const void *>(&qgemv_big_kernel<512, kBigD, false>))
-                   : (lds_x ? reinterpret_cast<const void *>(&qgemv_big_kernel<1024, kHugeD, true>)
-                            : reinterpret_cast<const void *>(&qgemv_big_kernel<1024, kHugeD, false>));
-    int cus = 0, per_cu = 0;
-    qw3_status st = cu_count(&cus);
-    if (st == QW3_OK) st = blocks_per_cu(kern, wgs, lds, &per_cu);
-    if (st != QW3_OK) return st;
-    int64_t blocks = ceil_div(N, R);
-    if (blocks > (int64_t)cus * per_cu) blocks = (int64_t)cus * per_cu;
-    hipLaunchKernelGGL(reinterpret_cast<void (*)(const uint16_t *, const uint32_t *, const uint16_t *, float *,
-                                                 int64_t, int, int)>(const_cast<void *>(kern)),
-                       dim3((unsigned)blocks, (unsigned)M), dim3(wgs), lds, stream, x, packed, scales, y, N, G, T);
-    return check_launch();
-}
-
-// The matrix-core GEMV: one workgroup per CU, workgroups dealt to the
-// matrices in proportion to their 16-row tiles, at least one and at most one
-// per tile each (4 waves x 16 groups at K = 8192).
-template <int GPW, int WAVES, bool MULTI>
-qw3_status launch_gemv_mfma(const uint16_t *x, GemvSegs sg, int count, hipStream_t stream, int M = 1) {
-    int cus = 0;
-    const qw3_status st = cu_count(&cus);
-    if (st != QW3_OK) return st;
-    int64_t tiles[kMaxSegs], tot = 0;
-    for (int i = 0; i < kMaxSegs; ++i) {
-        tiles[i] = i < count ? ceil_div(sg.rows[i], 16) : 0;
-        tot += tiles[i];
-    }
-    int64_t blocks = 0;
-    for (int i = 0; i < kMaxSegs; ++i) {
-        int64_t b = 0;
-        if (tiles[i] > 0) {
-            b = (int64_t)cus * tiles[i] / tot;
-            b = b < 1 ? 1 : (b > tiles[i] ? tiles[i] : b);
-        }
-        blocks += b;
-        sg.blk_end[i] = (int)blocks;
-    }
-    const size_t lds = mf_lds<GPW, WAVES>();
-    hipLaunchKernelGGL((qgemv_mfma_kernel<GPW, WAVES, MULTI>), dim3((unsigned)blocks, (unsigned)M), dim3(64 * WAVES),
-                       lds, stream, x, sg);
-    return check_launch();
-}
-
-// Whether the matrix-core GEMV takes a matrix: K = 8192, scale rows 8-byte
-// aligned (8-byte scale loads) and at least four 16-row tiles per CU (with
-// fewer it is no faster than the lane-per-group kernel).  At K = 28672
-// (7 waves x 32 groups) it measured no faster than qgemv_big_kernel on the
-// 8192-row down projection, two tiles per CU, so it is not used there.  The
-// choice depends on the matrix alone, so a matrix gets the same kernel -- and
-// the same bits -- from qgemv_w3g128 and from qgemv_w3g128_multi.
-bool gemv_mfma_takes(int G, const uint16_t *scales, int64_t N) {
-    if (G != 64 || N == 0 || !aligned(scales, 8)) return false;
-    int cus = 0;
-    if (cu_count(&cus) != QW3_OK) return false;
-    return ceil_div(N, 16) >= 4 * (int64_t)cus;
-}
-
-// M > 1 (the batch-invariant product): the same launch with a token grid
-// dimension, token m reading x + m K and writing y + m N.
-qw3_status launch_gemv(const uint16_t *x, const uint32_t *packed, const uint16_t *scales, float *y,
-                       int64_t N, int64_t K, hipStream_t stream, int M = 1) {
-    const int G = (int)(K / kGroup);
-    if (G <= 64) {
-        GemvSegs sg = {};
-        sg.packed[0] = packed;
-        sg.scales[0] = scales;
-        sg.y[0] = y;
-        sg.rows[0] = N;
-        if (gemv_mfma_takes(G, scales, N)) return launch_gemv_mfma<16, 4, false>(x, sg, 1, stream, M);
-        return launch_gemv_small_any<false>(x, sg, 1, G, stream, M);
-    }
-    return launch_gemv_big(x, packed, scales, y, N, G, stream, M);
-}
-
-// Several matrices sharing x: one launch when rows fit one wave (K <= 8192),
-// else one launch per matrix.
-qw3_status launch_gemv_multi(const uint16_t *x, int count, const uint32_t *const *packed,
-                             const uint16_t *const *scales, float *const *y, const int64_t *N, int64_t K,
-                             hipStream_t stream) {
-    const int G = (int)(K / kGroup);
-    if (G > 64) {
-        for (int i = 0; i < count; ++i) {
-            if (N[i] == 0) continue;
-            const qw3_status st = launch_gemv(x, packed[i], scales[i], y[i], N[i], K, stream);
-            if (st != QW3_OK) return st;
-        }
-        return QW3_OK;
-    }
-    // The matrices the matrix-core kernel takes go in one launch, the others
-    // in one launch of the lane-per-group kernel.
-    for (int pass = 0; pass < 2; ++pass) {
-        GemvSegs sg = {};
-        int cnt = 0;
-        for (int i = 0; i < count; ++i) {
-            if (N[i] == 0 || gemv_mfma_takes(G, scales[i], N[i]) != (pass == 0)) continue;
-            sg.packed[cnt] = packed[i];
-            sg.scales[cnt] = scales[i];
-            sg.y[cnt] = y[i];
-            sg.rows[cnt] = N[i];
-            ++cnt;
-        }
-        if (cnt == 0) continue;
-        for (int i = cnt; i < kMaxSegs; ++i) {
-            sg.packed[i] = sg.packed[cnt - 1];
-            sg.scales[i] = sg.scales[cnt - 1];
-            sg.y[i] = sg.y[cnt - 1];
-            sg.rows[i] = 0;
-        }
-        const qw3_status st = pass == 0 ? launch_gemv_mfma<16, 4, true>(x, sg, cnt, stream)
-                                        : launch_gemv_small_any<true>(x, sg, cnt, G, stream);
-        if (st != QW3_OK) return st;
-    }
-    return QW3_OK;
-}
 
 // Scratch of the per-token conversion of Mp tokens: x' [Mp][K] fp16, the
 // exponents [Mp], the token error masses [Mp] and the group masses [Mp][G].
