@@ -105,3 +105,25 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_source_hash_covers_every_library_source_and_the_build_flags(tmp_path, monkeypatch):
+    src, build = tmp_path / "csrc", tmp_path / "_build.py"
+    src.mkdir()
+    for name in ("qw3.hip", "qw3_gemv.hip", "qw3_common.h"):
+        (src / name).write_text("// %s\n" % name)
+    (src / "notes.txt").write_text("not a source")
+    build.write_text("UNITS = []\n")
+    monkeypatch.setattr(bench, "KERNEL_SRC_DIR", str(src))
+    monkeypatch.setattr(bench, "KERNEL_BUILD", str(build))
+    h0 = bench.kernel_source_hash()
+    (src / "notes.txt").write_text("still not a source")
+    assert bench.kernel_source_hash() == h0
+    for path in (src / "qw3_gemv.hip", src / "qw3_common.h", build):
+        old = path.read_text()
+        path.write_text(old + "// edited\n")
+        assert bench.kernel_source_hash() != h0, path.name
+        path.write_text(old)
+        assert bench.kernel_source_hash() == h0
+    (src / "qw3_extra.hip").write_text("// a new unit\n")
+    assert bench.kernel_source_hash() != h0
