@@ -219,7 +219,8 @@ def workload_summary(torch, q, steps):
     q/k/v and gate/up each fused into one launch), batched decode M = 4..32
     and prefill M = 512 on gate_proj and down_proj.  Device time per call
     from a replayed HIP graph (host launch cost excluded), and the time of
-    back-to-back stream launches beside it."""
+    back-to-back stream launches beside it.  Returns the same figures in
+    compact form for the main JSON line (compact_summary)."""
     import synth
     kept = {}
     layer = {}
@@ -272,6 +273,29 @@ def workload_summary(torch, q, steps):
     torch.cuda.empty_cache()
     for rec in lines:
         print(json.dumps(rec), file=sys.stderr, flush=True)
+    return compact_summary(layer, layer_ms, fused_ms, total_bytes, lines)
+
+
+def compact_summary(layer, layer_ms, fused_ms, layer_bytes, lines):
+    """The summary's figures as one small object: per workload, µs per call
+    (graph replay) and the fraction of the roofline that bounds it -- of
+    8 TB/s for the batch-1 and batched-decode calls (algorithmic bytes), of
+    the 2.5 PFLOP/s fp16 matrix peak for prefill (M = 512)."""
+    out = {"unit": "us per call, graph replay; frac of 8 TB/s HBM (M < 512) or of 2.5 PFLOP/s fp16 "
+                   "MFMA (M = 512)"}
+    for name, rec in layer.items():
+        out["%s_M1" % name] = {"us": rec["us"], "frac": round(rec["GB/s"] / HBM_PEAK_GBS, 4)}
+    out["layer_70b_M1"] = {"us": round(layer_ms * 1e3, 3),
+                           "frac": round(layer_bytes / layer_ms / 1e6 / HBM_PEAK_GBS, 4)}
+    out["layer_70b_M1_fused"] = {"us": round(fused_ms * 1e3, 3),
+                                 "frac": round(layer_bytes / fused_ms / 1e6 / HBM_PEAK_GBS, 4)}
+    for rec in lines:
+        if "layer_us" in rec:  # the layer's own line, already above
+            continue
+        name, m = rec["workload"].split(" ")[0], int(rec["workload"].rsplit("M=", 1)[1])
+        frac = rec["MFMA_frac"] if m == 512 else rec["HBM_frac"]
+        out["%s_M%d" % (name, m)] = {"us": rec["us"], "frac": frac}
+    return out
 
 
 def bench_extra(torch, q, steps, warmup):
@@ -723,7 +747,7 @@ def main():
     rot = packed = scales = None  # free the rotated copies before the other workloads
     torch.cuda.empty_cache()
     if not args.no_summary:
-        workload_summary(torch, q, max(200, args.steps))
+        line["other_configs"] = workload_summary(torch, q, max(200, args.steps))
     if args.extra:
         bench_extra(torch, q, max(50, args.steps // 4), max(10, args.warmup // 4))
     print(json.dumps(line), flush=True)

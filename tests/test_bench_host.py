@@ -127,3 +127,27 @@ def test_source_hash_covers_every_library_source_and_the_build_flags(tmp_path, m
         assert bench.kernel_source_hash() == h0
     (src / "qw3_extra.hip").write_text("// a new unit\n")
     assert bench.kernel_source_hash() != h0
+
+
+def test_compact_summary_of_the_other_workloads():
+    layer = {"gate_proj": {"us": 18.4, "GB/s": 4992.3, "bytes": 91881472, "us_stream_launches": 18.5},
+             "k_proj": {"us": 4.56, "GB/s": 722.5, "bytes": 3297280, "us_stream_launches": 11.8}}
+    lines = [{"workload": "Llama-3.1-70B decoder layer at B=1: q/o [8192, 8192], k/v [1024, 8192], gate/up "
+                          "[28672, 8192], down [8192, 28672] (device time, graph replay)",
+              "layer_bytes": 334725120, "layer_us": 84.528, "per_projection": {}},
+             {"workload": "gate_proj [28672, 8192] M=16", "us": 27.708, "HBM_frac": 0.4234, "MFMA_frac": 0.1085},
+             {"workload": "down_proj [8192, 28672] M=512", "us": 260.04, "HBM_frac": 0.0663, "MFMA_frac": 0.37}]
+    layer_bytes, layer_ms, fused_ms = 334725120, 0.084528, 0.077332
+    out = bench.compact_summary(layer, layer_ms, fused_ms, layer_bytes, lines)
+    assert out["gate_proj_M1"] == {"us": 18.4, "frac": round(4992.3 / 8000, 4)}
+    assert out["k_proj_M1"]["frac"] == round(722.5 / 8000, 4)
+    assert out["layer_70b_M1"] == {"us": 84.528, "frac": round(layer_bytes / layer_ms / 1e6 / 8000, 4)}
+    assert out["layer_70b_M1_fused"]["us"] == 77.332
+    assert out["gate_proj_M16"] == {"us": 27.708, "frac": 0.4234}     # decode: the HBM fraction
+    assert out["down_proj_M512"] == {"us": 260.04, "frac": 0.37}      # prefill: the MFMA fraction
+    assert len(out) == 1 + 2 + 2 + 2  # unit, two projections, two layer figures, two calls
+    # the full summary (7 projections, 2 layers, 10 batched/prefill calls) keeps the line short
+    full = dict(out, **{"%s_M%d" % (nm, m): {"us": 123.456, "frac": 0.1234}
+                        for nm in ("gate_proj", "down_proj") for m in (4, 8, 16, 32, 512)})
+    full.update({"%s_M1" % nm: {"us": 12.345, "frac": 0.1234} for nm in bench.LAYER_ORDER})
+    assert len(json.dumps(full)) < 1500
