@@ -10,8 +10,10 @@ decode, multiply-accumulate, reduction, store) in a single kernel.
 Inputs are seeded synthetic tensors (`synth`), resident in device memory
 before timing starts.  Weight/scale copies are rotated so the bytes of all
 copies exceed twice the 256 MB Infinity Cache; each step reads a copy that
-is not cache resident.  Steps are timed with HIP events recorded on the stream
-the kernels are launched on.
+is not cache resident.  The K timed steps are captured in one HIP graph and
+replayed once between two HIP events recorded on the stream the kernels run
+on (a decode loop replays its launches the same way); the time of K
+back-to-back stream launches is reported beside it.
 
 Prints ONE JSON line on stdout.  Unless --no-summary, the other workloads
 follow on stderr, one JSON line each: the full 70B decoder layer at batch 1
@@ -183,6 +185,33 @@ def graph_time(torch, fn, reps: int, replays: int, warmup: int):
             fn(i)
     torch.cuda.synchronize()
     return time_steps(torch, lambda i: graph.replay(), replays, warmup) / reps
+
+
+def graph_steps(torch, fn, steps: int, warmup: int):
+    """ms per step of fn(0) .. fn(steps - 1) captured in one HIP graph and
+    replayed once between two events on the launch stream: exactly `steps`
+    steps are timed, with no host launch between them.  Untimed before it:
+    `warmup` stream launches and one replay of the same graph."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        fn(0)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=side):
+        for i in range(steps):
+            fn(i)
+    torch.cuda.synchronize()
+    for i in range(warmup):
+        fn(i)
+    graph.replay()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    graph.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps
 
 
 LAYER_ORDER = ("q_proj", "k_proj", "v_proj", "o_proj", "gate_proj", "up_proj", "down_proj")
@@ -714,7 +743,9 @@ def main():
     rot = Rotation(torch, packed, scales)
     y = torch.empty(n, dtype=torch.float32, device="cuda")
 
-    ms = time_steps(torch, lambda i: q.qgemv_w3g128(xd, rot[i][0], rot[i][1], out=y), args.steps, args.warmup)
+    step = lambda i: q.qgemv_w3g128(xd, rot[i][0], rot[i][1], out=y)  # noqa: E731
+    ms_launch = time_steps(torch, step, args.steps, args.warmup)
+    ms = graph_steps(torch, step, args.steps, args.warmup)
     nbytes = gemv_bytes(n, k)
     gbs = nbytes / ms / 1e6
     if ceiling is not None:
@@ -738,7 +769,9 @@ def main():
         "config": {"workload": "gate_proj W3G128 GEMV, W [28672, 8192] -> int32 [28672, 768] + bf16 "
                                "[28672, 64], x bf16 [1, 8192], y fp32 [28672]",
                    "N": n, "K": k, "M": 1, "bytes_per_step": nbytes,
-                   "weight_copies_rotated": rot.copies, "us_per_step": round(ms * 1e3, 3)},
+                   "weight_copies_rotated": rot.copies, "us_per_step": round(ms * 1e3, 3),
+                   "timing": "the K steps captured in one HIP graph, replayed once between events",
+                   "us_per_step_stream_launches": round(ms_launch * 1e3, 3)},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic()},
     }
