@@ -506,19 +506,18 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_mt_kernel(const uint4 *__res
 constexpr int kMrBatch = 4;  // tiles per cross-wave reduction
 // TS sets of 16 tokens share each decoded block (TS = 2: 17..32 tokens in one
 // pass over the weights); a wave then owns 8 / TS groups.
-// LDS: the partial sums [2][kMrBatch][WAVES][TS][64 lanes] x f4, then the
-// guard's error masses of in-kernel conversion [8 tokens][WAVES * 8 groups],
-// 16 wave flags and the fixup's group list.
+// LDS: the partial sums [2][kMrBatch][WAVES][TS][64 lanes] x f4, then 16
+// wave flags and the fixup's group list.
 template <int WAVES, int TS>
 constexpr size_t mr_red_bytes() { return (size_t)2 * kMrBatch * WAVES * TS * 64 * 16; }
 template <int WAVES, int TS>
-constexpr size_t mr_lds() { return mr_red_bytes<WAVES, TS>() + ((size_t)8 * WAVES * 8 + 16 + kNzCap + 1) * 4; }
+constexpr size_t mr_lds() { return mr_red_bytes<WAVES, TS>() + ((size_t)16 + kNzCap + 1) * 4; }
 struct MrSlot {
     u32x4v_t w[3];  // group g0 + 4q + j of row n: 12 words
     u32x2v_t s;     // bf16 scales of groups g0 + 4q .. g0 + 4q + 3 of row n
 };
 
-template <int WAVES, int TS, bool XH>
+template <int WAVES, int TS>
 __global__ __launch_bounds__(64 * WAVES) void qgemm_mr_kernel(const uint4 *__restrict__ xq,
                                                             const int16_t *__restrict__ xe,
                                                             const float *__restrict__ xd,
@@ -533,8 +532,7 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_mr_kernel(const uint4 *__res
     constexpr int UT = 4 / NS;   // tiles per ring cycle (4 slots)
     extern __shared__ __align__(16) unsigned char lds[];  // mr_lds()
     f4_t *red = reinterpret_cast<f4_t *>(lds);
-    float *xdl = reinterpret_cast<float *>(lds + mr_red_bytes<WAVES, TS>());  // [8][WAVES * 8]
-    uint32_t *flags = reinterpret_cast<uint32_t *>(xdl + 8 * WAVES * 8);
+    uint32_t *flags = reinterpret_cast<uint32_t *>(lds + mr_red_bytes<WAVES, TS>());
     int *nz = reinterpret_cast<int *>(flags + 16);
     int small = 0;  // some error mass of this lane's tokens and groups is non-zero
     const int lane = threadIdx.x & 63;
@@ -550,52 +548,38 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_mr_kernel(const uint4 *__res
 
     int et[TS][4];
     h8_t xa[GW][TS][4];
-    [[maybe_unused]] uint4 xh[4][4];
-    if constexpr (XH) {
-        // Up to 8 tokens (TS = 1): the activations straight from x.  Lane
-        // (n, j) reads block j of groups g0 + 4(n / 8) .. + 3 of token n % 8
-        // (tokens past M read token M - 1; rows 8..15 of D are never stored),
-        // so lanes n and n + 8 share the wave's 8 groups of one token.
-        static_assert(!XH || TS == 1, "in-kernel conversion for one token set");
-        const int64_t K = (int64_t)G * kGroup;
-        const int t = (n & 7) < M ? (n & 7) : M - 1;
+    // The slice's activation exponents (one per token; the wave's groups lie
+    // in one 8-group slice) through the scalar unit: they stay out of the
+    // vector memory counter, whose waits in the loop count the ring's loads
+    // exactly.  Lane row j scales tokens 16 ts + 4j .. 16 ts + 4j + 3.
+    {
+        const int *xs = reinterpret_cast<const int *>(xe + (int64_t)(g0 / 8) * Mp);
+        int ew[8 * TS];
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-            load_x32(x + t * K + (int64_t)(g0 + 4 * (n >> 3) + k) * kGroup + 32 * j, xh[k]);
-    } else {
-        // The slice's activation exponents (one per token; the wave's groups lie
-        // in one 8-group slice) through the scalar unit: they stay out of the
-        // vector memory counter, whose waits in the loop count the ring's loads
-        // exactly.  Lane row j scales tokens 16 ts + 4j .. 16 ts + 4j + 3.
-        {
-            const int *xs = reinterpret_cast<const int *>(xe + (int64_t)(g0 / 8) * Mp);
-            int ew[8 * TS];
+        for (int i = 0; i < 8 * TS; ++i) ew[i] = xs[i];
 #pragma unroll
-            for (int i = 0; i < 8 * TS; ++i) ew[i] = xs[i];
+        for (int ts = 0; ts < TS; ++ts)
 #pragma unroll
-            for (int ts = 0; ts < TS; ++ts)
+            for (int r = 0; r < 4; ++r) {
+                const int b = 8 * ts + r / 2;
+                const int w0 = j == 0 ? ew[b] : j == 1 ? ew[b + 2] : j == 2 ? ew[b + 4] : ew[b + 6];
+                const int v = (r & 1) ? (w0 >> 16) : (int)(int16_t)(w0 & 0xFFFF);
+                small |= v & 1;  // the low bit flags a non-zero error mass
+                et[ts][r] = v >> 1;
+            }
+    }
+    // Activations first (L2-resident), then the ring: the loop's waits for
+    // the ring count exactly.  Token slots past M read slot M - 1 again (their
+    // rows of D are never stored), so a load touches only the lines of the M
+    // real tokens.
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int b = 8 * ts + r / 2;
-                    const int w0 = j == 0 ? ew[b] : j == 1 ? ew[b + 2] : j == 2 ? ew[b + 4] : ew[b + 6];
-                    const int v = (r & 1) ? (w0 >> 16) : (int)(int16_t)(w0 & 0xFFFF);
-                    small |= v & 1;  // the low bit flags a non-zero error mass
-                    et[ts][r] = v >> 1;
-                }
-        }
-        // Activations first (L2-resident), then the ring: the loop's waits for
-        // the ring count exactly.  Token slots past M read slot M - 1 again (their
-        // rows of D are never stored), so a load touches only the lines of the M
-        // real tokens.
+    for (int ts = 0; ts < TS; ++ts) {
+        const int m = 16 * ts + n < M ? 16 * ts + n : M - 1;
 #pragma unroll
-        for (int ts = 0; ts < TS; ++ts) {
-            const int m = 16 * ts + n < M ? 16 * ts + n : M - 1;
+        for (int gi = 0; gi < GW; ++gi)
 #pragma unroll
-            for (int gi = 0; gi < GW; ++gi)
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    xa[gi][ts][u] = __builtin_bit_cast(h8_t, xq[(((int64_t)(g0 + gi) * 4 + u) * 4 + j) * Mp + m]);
-        }
+            for (int u = 0; u < 4; ++u)
+                xa[gi][ts][u] = __builtin_bit_cast(h8_t, xq[(((int64_t)(g0 + gi) * 4 + u) * 4 + j) * Mp + m]);
     }
     // Unconditional loads: tiles past the last re-read it, rows past N read row N - 1.
     auto load = [&](int64_t t, int q, MrSlot &sl) {
@@ -614,42 +598,6 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_mr_kernel(const uint4 *__res
     __builtin_amdgcn_sched_barrier(0);
     load(1 / NS, 1 % NS, ring[1]);
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (XH) {
-        // One exponent per token over the slice (the largest |x| over lanes
-        // n, n + 8 and the four lane rows).  Each lane converts its 4 groups;
-        // a DPP row rotation by 8 brings the other 4 from lane n ^ 8, so
-        // every lane holds all 8 groups of token n % 8.
-        uint32_t mx = 0, mnk[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            uint32_t bm;
-            block_stats(xh[k], bm, mnk[k]);
-            mx = max(mx, bm);
-        }
-        mx = max(mx, dpp_u32<0x128>(mx));
-        mx = max(mx, (uint32_t)__shfl_xor((int)mx, 16));
-        mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32));
-        const int e = group_exponent(mx);
-        // The guard's cheap test (a value below the slice's exact range).
-#pragma unroll
-        for (int k = 0; k < 4; ++k) small |= mnk[k] < exact_floor_bits(e);
-        const bool lo = n < 8;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            uint32_t o[16];
-            convert_block(xh[k], e, o);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const uint4 own = make_uint4(o[4 * u], o[4 * u + 1], o[4 * u + 2], o[4 * u + 3]);
-                const uint4 oth = make_uint4(dpp_u32<0x128>(o[4 * u]), dpp_u32<0x128>(o[4 * u + 1]),
-                                             dpp_u32<0x128>(o[4 * u + 2]), dpp_u32<0x128>(o[4 * u + 3]));
-                xa[k][0][u] = __builtin_bit_cast(h8_t, lo ? own : oth);
-                xa[4 + k][0][u] = __builtin_bit_cast(h8_t, lo ? oth : own);
-            }
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) et[0][r] = __shfl(e, 4 * j + r);
-    }
 
     const uint32_t magic = magic_vgpr();
     f4_t acc[TS];
@@ -745,10 +693,7 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_mr_kernel(const uint4 *__res
     if (any_flag(flags)) {  // workgroup-uniform, rare
         __syncthreads();
         const int gc0 = chunk * WAVES * GW, gc1 = gc0 + WAVES * GW;
-        if constexpr (XH) slice_errors(x, (int64_t)G * kGroup, M, gc0, WAVES, xdl);
-        auto d_at = [&](int m, int g) {
-            return XH ? xdl[m * (WAVES * 8) + (g - gc0)] : xd[(int64_t)g * Mp + m];
-        };
+        auto d_at = [&](int m, int g) { return xd[(int64_t)g * Mp + m]; };
         const int nnz = build_nz(gc0, gc1, [&](int g) {
             bool f = false;
             for (int m = 0; m < M; ++m) f |= d_at(m, g) != 0.f;
@@ -759,30 +704,43 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_mr_kernel(const uint4 *__res
     }
 }
 
-// ------------------------------------- batched decode, up to four tokens ----
-// The batch-1 matrix-core layout with the four tokens in place of its four
-// super-step slots.  In super-step q lane (n, j) decodes group g0 + 4q + j of
-// row n straight into the B operand (k chunk j), as in qgemv_mfma_kernel, so
-// no transpose across lanes is needed.  A-operand set q has row m = 4t + j'
-// carrying token t's activations of group g0 + 4q + j' in k chunk j' and zero
-// elsewhere, so after the super-step's 16 MFMAs rows 4t .. 4t + 3 -- lane row
-// t's registers -- hold token t's partial sums of the four groups, exactly
-// apart.  A wave owns the 8 groups of one activation slice (two sets, 128
-// VGPRs) and walks 16-row tiles through the ring of qgemm_mr_kernel; the
+// ------------------------------------- batched decode, up to eight tokens ---
+// The batch-1 matrix-core layout with the tokens in place of its four
+// super-step slots.  In super-step q lane (n, j) loads group g0 + 4q + j of
+// row n (48 bytes), as in qgemv_mfma_kernel.
+// TOK = 4: the lane decodes that group straight into the B operand (k chunk
+// j), so no exchange across lanes is needed.  A-operand set q has row
+// m = 4t + j' carrying token t's activations of group g0 + 4q + j' in k chunk
+// j' and zero elsewhere, so after the super-step's 16 MFMAs rows 4t .. 4t + 3
+// -- lane row t's registers -- hold token t's partial sums of the four groups,
+// exactly apart.
+// TOK = 8: one v_permlane32_swap per word pairs half-groups across lane rows:
+// afterwards lane rows 0 and 2 hold the two halves (blocks 2-3 and 0-1) of
+// group 4q and rows 1 and 3 those of group 4q + 1 (set 0), and a second
+// register set holds groups 4q + 2 and 4q + 3 the same way (set 1).  Each set
+// takes 8 MFMAs whose A row m = 2t + g' carries token t's activations in the
+// k chunks j' with j' % 2 == g' (group 4q + 2 set + g') and zero in the
+// others, so D rows 2t, 2t + 1 hold token t's partials of the set's two
+// groups, and lane row j' accumulates tokens 2j' and 2j' + 1.  The same 16
+// MFMAs and the same decode per super-step as TOK = 4, twice the tokens.
+// A wave owns the 8 groups of one activation slice (128 VGPRs of A operands
+// either way) and walks 16-row tiles through the ring of qgemm_mr_kernel; the
 // waves' partials meet in LDS every kMrBatch tiles and are added in wave
 // order.  The kernel converts the activations itself, with one exponent per
 // token over the wave's slice (a conversion launch in front measured slower).
-template <int WAVES>
+template <int WAVES, int TOK>
 __global__ __launch_bounds__(64 * WAVES) void qgemm_m4_kernel(const uint16_t *__restrict__ x,
                                                             const uint32_t *__restrict__ packed,
                                                             const uint16_t *__restrict__ scales,
                                                             float *__restrict__ out, int M, int64_t N, int G, int C,
                                                             int64_t out_chunk) {
+    static_assert(TOK == 4 || TOK == 8, "four or eight token slots");
     constexpr int GW = 8, NS = 2, UT = 2;
-    extern __shared__ __align__(16) unsigned char lds[];  // [2][kMrBatch][WAVES][64 lanes] floats, then the guard's
+    constexpr int R2 = TOK / 4;  // tokens per lane row and lane
+    extern __shared__ __align__(16) unsigned char lds[];  // [2][kMrBatch][WAVES][R2][64 lanes] floats, then the guard's
     float *red = reinterpret_cast<float *>(lds);
-    float *xdl = red + 2 * kMrBatch * WAVES * 64;                            // D [4 tokens][WAVES * GW groups]
-    uint32_t *flags = reinterpret_cast<uint32_t *>(xdl + 4 * WAVES * GW);  // per wave
+    float *xdl = red + 2 * kMrBatch * WAVES * 64 * R2;                         // D [TOK tokens][WAVES * GW groups]
+    uint32_t *flags = reinterpret_cast<uint32_t *>(xdl + TOK * WAVES * GW);  // per wave
     int *nz = reinterpret_cast<int *>(flags + 16);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -795,18 +753,35 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_m4_kernel(const uint16_t *__
     const int64_t W = (int64_t)G * kWordsPerGroup;
     float *y = out + (int64_t)chunk * out_chunk;
 
-    // The bf16 activations straight from x, before the ring's loads: the
-    // four lanes n = 4t .. 4t + 3 of lane row j share token t and group
-    // g0 + 4q + j, and lane n reads block n % 4 of it (tokens past M read
-    // token M - 1, whose rows of D are not stored).
-    int et;
+    // The bf16 activations straight from x, before the ring's loads (tokens
+    // past M read token M - 1, whose rows of D are not stored).
+    // TOK = 4: the four lanes n = 4t .. 4t + 3 of lane row j share token t
+    // and group g0 + 4q + j, and lane n reads block n % 4 of it.
+    // TOK = 8: lanes n = 2t, 2t + 1 of lane row j share token t; the one with
+    // n % 2 == j % 2 (whose A rows take lane row j's k chunk) reads blocks
+    // bb + (2 if j < 2 else 0) of group g0 + 4q + j % 2 (set 0), its
+    // neighbour the same blocks of group g0 + 4q + 2 + j % 2 (set 1).
+    constexpr int XB = TOK == 4 ? NS : 2 * NS;  // blocks per lane
+    int et[R2];
     h8_t xa[NS][16];
-    uint4 xb[NS][4];
+    uint4 xb[XB][4];
     {
         const int64_t K = (int64_t)G * kGroup;
-        const int t = (n >> 2) < M ? (n >> 2) : M - 1;
+        if constexpr (TOK == 4) {
+            const int t = (n >> 2) < M ? (n >> 2) : M - 1;
 #pragma unroll
-        for (int q = 0; q < NS; ++q) load_x32(x + t * K + (int64_t)(g0 + 4 * q + j) * kGroup + 32 * (n & 3), xb[q]);
+            for (int q = 0; q < NS; ++q)
+                load_x32(x + t * K + (int64_t)(g0 + 4 * q + j) * kGroup + 32 * (n & 3), xb[q]);
+        } else {
+            const int t = (n >> 1) < M ? (n >> 1) : M - 1;
+            const int gs = ((n & 1) == (j & 1) ? 0 : 2) + (j & 1);
+            const int b0 = j < 2 ? 2 : 0;
+#pragma unroll
+            for (int q = 0; q < NS; ++q)
+#pragma unroll
+                for (int bb = 0; bb < 2; ++bb)
+                    load_x32(x + t * K + (int64_t)(g0 + 4 * q + gs) * kGroup + 32 * (b0 + bb), xb[2 * q + bb]);
+        }
     }
     // Unconditional loads: tiles past the last re-read it, rows past N read row N - 1.
     auto load = [&](int64_t t, int q, MrSlot &sl) {
@@ -827,49 +802,78 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_m4_kernel(const uint16_t *__
     __builtin_amdgcn_sched_barrier(0);
     {
         // One exponent per token over the wave's slice: the largest |x| over
-        // the token's 4 x 4 lanes (the quad: the group's blocks; lane ^ 16
-        // and lane ^ 32: its groups) maps to [2^14, 2^15).  Each lane
-        // converts its block; the quad then hands all four blocks to its lane
-        // n % 4 = j (a DPP broadcast per dword), the only one whose row takes
-        // k chunk j: the other rows are zero.  Lane row j accumulates token
-        // j, held by lane 4j.
-        uint32_t mx = 0, mnq[NS];
+        // the token's lanes (TOK = 4: the quad -- the group's blocks -- and
+        // lane ^ 16, lane ^ 32 -- its groups; TOK = 8: lane ^ 1 and the lane
+        // rows) maps to [2^14, 2^15).
+        uint32_t mx = 0, mnq[XB];
 #pragma unroll
-        for (int q = 0; q < NS; ++q) {
+        for (int i = 0; i < XB; ++i) {
             uint32_t bm;
-            block_stats(xb[q], bm, mnq[q]);
+            block_stats(xb[i], bm, mnq[i]);
             mx = max(mx, bm);
         }
         mx = max(mx, dpp_u32<kDppQuadXor1>(mx));
-        mx = max(mx, dpp_u32<kDppQuadXor2>(mx));
+        if constexpr (TOK == 4) mx = max(mx, dpp_u32<kDppQuadXor2>(mx));
         mx = max(mx, (uint32_t)__shfl_xor((int)mx, 16));
         mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32));
         const int e = group_exponent(mx);
         // The guard's cheap test (a value below the slice's exact range).
         bool small = false;
 #pragma unroll
-        for (int q = 0; q < NS; ++q) small |= mnq[q] < exact_floor_bits(e);
+        for (int i = 0; i < XB; ++i) small |= mnq[i] < exact_floor_bits(e);
         publish_flag(small, flags);
-        const bool on = (n & 3) == j;
+        if constexpr (TOK == 4) {
+            // Each lane converts its block; the quad then hands all four
+            // blocks to its lane n % 4 = j (a DPP broadcast per dword), the
+            // only one whose row takes k chunk j: the other rows are zero.
+            // Lane row j accumulates token j, held by lane 4j.
+            const bool on = (n & 3) == j;
 #pragma unroll
-        for (int q = 0; q < NS; ++q) {
-            uint32_t o[16];
-            convert_block(xb[q], e, o);
-            static_for<4>([&](auto bc) __attribute__((always_inline)) {
-                constexpr int b = decltype(bc)::value;
+            for (int q = 0; q < NS; ++q) {
+                uint32_t o[16];
+                convert_block(xb[q], e, o);
+                static_for<4>([&](auto bc) __attribute__((always_inline)) {
+                    constexpr int b = decltype(bc)::value;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const uint4 f = make_uint4(dpp_u32<0x55 * b>(o[4 * v]), dpp_u32<0x55 * b>(o[4 * v + 1]),
+                                                   dpp_u32<0x55 * b>(o[4 * v + 2]), dpp_u32<0x55 * b>(o[4 * v + 3]));
+                        xa[q][4 * b + v] = on ? __builtin_bit_cast(h8_t, f) : h8_t{0, 0, 0, 0, 0, 0, 0, 0};
+                    }
+                });
+            }
+            et[0] = __shfl(e, 4 * j);
+        } else {
+            // Each lane converts its four blocks; the lane with n % 2 == j % 2
+            // keeps its own (set 0) and takes its neighbour's (set 1, a DPP
+            // swap of adjacent lanes); the other lane's rows are zero.
+            // xa[q][8 set + 4 bb + v]; lane row j accumulates tokens 2j and
+            // 2j + 1, held by lanes 4j and 4j + 2.
+            const bool on = (n & 1) == (j & 1);
+#pragma unroll
+            for (int i = 0; i < XB; ++i) {
+                const int q = i >> 1, bb = i & 1;
+                uint32_t o[16];
+                convert_block(xb[i], e, o);
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    const uint4 f = make_uint4(dpp_u32<0x55 * b>(o[4 * v]), dpp_u32<0x55 * b>(o[4 * v + 1]),
-                                               dpp_u32<0x55 * b>(o[4 * v + 2]), dpp_u32<0x55 * b>(o[4 * v + 3]));
-                    xa[q][4 * b + v] = on ? __builtin_bit_cast(h8_t, f) : h8_t{0, 0, 0, 0, 0, 0, 0, 0};
+                    const uint4 own = make_uint4(o[4 * v], o[4 * v + 1], o[4 * v + 2], o[4 * v + 3]);
+                    const uint4 nb = make_uint4(dpp_u32<kDppQuadXor1>(o[4 * v]), dpp_u32<kDppQuadXor1>(o[4 * v + 1]),
+                                                dpp_u32<kDppQuadXor1>(o[4 * v + 2]),
+                                                dpp_u32<kDppQuadXor1>(o[4 * v + 3]));
+                    xa[q][4 * bb + v] = on ? __builtin_bit_cast(h8_t, own) : h8_t{0, 0, 0, 0, 0, 0, 0, 0};
+                    xa[q][8 + 4 * bb + v] = on ? __builtin_bit_cast(h8_t, nb) : h8_t{0, 0, 0, 0, 0, 0, 0, 0};
                 }
-            });
+            }
+            et[0] = __shfl(e, 4 * j);
+            et[1] = __shfl(e, 4 * j + 2);
         }
-        et = __shfl(e, 4 * j);
     }
 
     const uint32_t magic = magic_vgpr();
-    float acc = 0.f;
+    float acc[R2];
+#pragma unroll
+    for (int r = 0; r < R2; ++r) acc[r] = 0.f;
     // Tile c0 + h: ring steps u = 2h + q (UT tiles are one ring cycle).
     auto tile = [&](int64_t c0, auto hc) __attribute__((always_inline)) {
         constexpr int h = decltype(hc)::value;
@@ -882,44 +886,82 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_m4_kernel(const uint16_t *__
             const MrSlot &sl = ring[u];
             const uint32_t wd[12] = {sl.w[0].x, sl.w[0].y, sl.w[0].z, sl.w[0].w, sl.w[1].x, sl.w[1].y,
                                      sl.w[1].z, sl.w[1].w, sl.w[2].x, sl.w[2].y, sl.w[2].z, sl.w[2].w};
-            f4_t d = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (TOK == 4) {
+                f4_t d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                h2_t qd[16];
-                decode_block(wd[3 * b], wd[3 * b + 1], wd[3 * b + 2], magic, qd);
+                for (int b = 0; b < 4; ++b) {
+                    h2_t qd[16];
+                    decode_block(wd[3 * b], wd[3 * b + 1], wd[3 * b + 2], magic, qd);
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const h8_t bop = {qd[4 * v].x,     qd[4 * v].y,     qd[4 * v + 1].x, qd[4 * v + 1].y,
-                                      qd[4 * v + 2].x, qd[4 * v + 2].y, qd[4 * v + 3].x, qd[4 * v + 3].y};
-                    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[q][4 * b + v], bop, d, 0, 0, 0);
+                    for (int v = 0; v < 4; ++v) {
+                        const h8_t bop = {qd[4 * v].x,     qd[4 * v].y,     qd[4 * v + 1].x, qd[4 * v + 1].y,
+                                          qd[4 * v + 2].x, qd[4 * v + 2].y, qd[4 * v + 3].x, qd[4 * v + 3].y};
+                        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[q][4 * b + v], bop, d, 0, 0, 0);
+                    }
+                }
+                // d[r]: token j, group g0 + 4q + r of row n
+                acc[0] = fmaf(d[0], bf16_to_f32(sl.s.x & 0xFFFFu), acc[0]);
+                acc[0] = fmaf(d[1], __uint_as_float(sl.s.x & 0xFFFF0000u), acc[0]);
+                acc[0] = fmaf(d[2], bf16_to_f32(sl.s.y & 0xFFFFu), acc[0]);
+                acc[0] = fmaf(d[3], __uint_as_float(sl.s.y & 0xFFFF0000u), acc[0]);
+            } else {
+                // hw[0] (set 0): rows 0, 2 hold group 4q, rows 1, 3 group
+                // 4q + 1; hw[1] (set 1): groups 4q + 2 and 4q + 3.  Rows 0, 1
+                // hold blocks 2-3 of their group, rows 2, 3 blocks 0-1.
+                uint32_t hw[2][6];
+#pragma unroll
+                for (int w = 0; w < 6; ++w) {
+                    const auto r = __builtin_amdgcn_permlane32_swap(wd[6 + w], wd[w], false, false);
+                    hw[0][w] = r[0];
+                    hw[1][w] = r[1];
+                }
+#pragma unroll
+                for (int st = 0; st < 2; ++st) {
+                    f4_t d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int bb = 0; bb < 2; ++bb) {
+                        h2_t qd[16];
+                        decode_block(hw[st][3 * bb], hw[st][3 * bb + 1], hw[st][3 * bb + 2], magic, qd);
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            const h8_t bop = {qd[4 * v].x,     qd[4 * v].y,     qd[4 * v + 1].x, qd[4 * v + 1].y,
+                                              qd[4 * v + 2].x, qd[4 * v + 2].y, qd[4 * v + 3].x, qd[4 * v + 3].y};
+                            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[q][8 * st + 4 * bb + v], bop, d, 0, 0, 0);
+                        }
+                    }
+                    // d[2r + g]: token 2j + r, group g0 + 4q + 2 st + g of row n
+                    const uint32_t sw = st ? sl.s.y : sl.s.x;
+                    const float s_lo = bf16_to_f32(sw & 0xFFFFu), s_hi = __uint_as_float(sw & 0xFFFF0000u);
+                    acc[0] = fmaf(d[0], s_lo, acc[0]);
+                    acc[0] = fmaf(d[1], s_hi, acc[0]);
+                    acc[1] = fmaf(d[2], s_lo, acc[1]);
+                    acc[1] = fmaf(d[3], s_hi, acc[1]);
                 }
             }
-            // d[r]: token j, group g0 + 4q + r of row n
-            acc = fmaf(d[0], bf16_to_f32(sl.s.x & 0xFFFFu), acc);
-            acc = fmaf(d[1], __uint_as_float(sl.s.x & 0xFFFF0000u), acc);
-            acc = fmaf(d[2], bf16_to_f32(sl.s.y & 0xFFFFu), acc);
-            acc = fmaf(d[3], __uint_as_float(sl.s.y & 0xFFFF0000u), acc);
             if (q == NS - 1) {
                 const int bt = (int)(t % kMrBatch);
-                float *rb = red + ((t / kMrBatch) & 1) * (kMrBatch * WAVES * 64);
-                rb[(bt * WAVES + wave) * 64 + lane] = ldexpf(acc, et);
-                acc = 0.f;
+                float *rb = red + ((t / kMrBatch) & 1) * (kMrBatch * WAVES * 64 * R2);
+#pragma unroll
+                for (int r = 0; r < R2; ++r) {
+                    rb[((bt * WAVES + wave) * R2 + r) * 64 + lane] = ldexpf(acc[r], et[r]);
+                    acc[r] = 0.f;
+                }
                 if (bt == kMrBatch - 1 || t == my_tiles - 1) {
                     lds_barrier();
-                    // (tile, lane) outputs in a fixed number of passes
-                    const int outs = (bt + 1) * 64;
-                    constexpr int kPasses = (kMrBatch * 64 + 64 * WAVES - 1) / (64 * WAVES);
+                    // (tile, token of the lane, lane) outputs in a fixed number of passes
+                    const int outs = (bt + 1) * 64 * R2;
+                    constexpr int kPasses = (kMrBatch * 64 * R2 + 64 * WAVES - 1) / (64 * WAVES);
 #pragma unroll
                     for (int ps = 0; ps < kPasses; ++ps) {
                         const int i = threadIdx.x + ps * 64 * WAVES;
-                        const int tt = i >> 6, l = i & 63;
-                        const int tok = l >> 4;
+                        const int tt = i / (64 * R2), r = (i >> 6) % R2, l = i & 63;
+                        const int tok = R2 * (l >> 4) + r;
                         const int64_t row = (tb + (t - bt + tt) * TB) * 16 + (l & 15);
                         if (i < outs && tok < M && row < N) {
-                            const float *src = rb + tt * WAVES * 64 + l;
+                            const float *src = rb + (tt * WAVES * R2 + r) * 64 + l;
                             float tot = src[0];
 #pragma unroll
-                            for (int w = 1; w < WAVES; ++w) tot += src[w * 64];
+                            for (int w = 1; w < WAVES; ++w) tot += src[w * R2 * 64];
                             y[(int64_t)tok * N + row] = tot;
                         }
                     }
@@ -944,9 +986,9 @@ __global__ __launch_bounds__(64 * WAVES) void qgemm_m4_kernel(const uint16_t *__
                          nnz, false, y, N, threadIdx.x, blockDim.x);
     }
 }
-template <int WAVES>
+template <int WAVES, int TOK>
 constexpr size_t m4_lds() {
-    return (size_t)2 * kMrBatch * WAVES * 64 * sizeof(float) + ((size_t)4 * WAVES * 8 + 16 + kNzCap + 1) * 4;
+    return (size_t)2 * kMrBatch * WAVES * 64 * (TOK / 4) * sizeof(float) + ((size_t)TOK * WAVES * 8 + 16 + kNzCap + 1) * 4;
 }
 
 // --------------------------------------------------- prefill (large M) tiles --
@@ -1735,28 +1777,21 @@ qw3_status launch_gemm_mt(const uint16_t *x, const uint32_t *packed, const uint1
     const bool ring = TS == 2 || aligned(scales, 8);
     constexpr int Mp = 16 * TS;
     const int C = G / ((8 / TS) * WAVES);
-    // Up to 8 tokens the ring kernel converts the activations itself (at 8,
-    // about 1 us faster than the conversion launch in front of it; at 16
-    // tokens, with one token per lane, about 1.5 us slower).
-    const bool xh = ring && TS == 1 && M <= 8;
     Carve cv;
-    const size_t xq_at = cv.take(xh ? 0 : (size_t)Mp * (size_t)K * 2);
-    const size_t xe_at = cv.take(xh ? 0 : (size_t)(G / 8) * Mp * sizeof(int16_t));
-    const size_t xd_at = cv.take(xh ? 0 : (size_t)G * Mp * sizeof(float));
+    const size_t xq_at = cv.take((size_t)Mp * (size_t)K * 2);
+    const size_t xe_at = cv.take((size_t)(G / 8) * Mp * sizeof(int16_t));
+    const size_t xd_at = cv.take((size_t)G * Mp * sizeof(float));
     const size_t part_at = cv.take(C > 1 ? (size_t)C * Mp * (size_t)N * sizeof(float) : 0);
-    const void *kern = xh     ? reinterpret_cast<const void *>(&qgemm_mr_kernel<WAVES, TS, TS == 1>)
-                       : ring ? reinterpret_cast<const void *>(&qgemm_mr_kernel<WAVES, TS, false>)
-                              : reinterpret_cast<const void *>(&qgemm_mt_kernel<WAVES>);
+    const void *kern = ring ? reinterpret_cast<const void *>(&qgemm_mr_kernel<WAVES, TS>)
+                            : reinterpret_cast<const void *>(&qgemm_mt_kernel<WAVES>);
     const size_t lds = ring ? mr_lds<WAVES, TS>() : 0;
     int cus = 0, per_cu = 0;
     qw3_status st = cu_count(&cus);
     if (st == QW3_OK) st = blocks_per_cu(kern, 64 * WAVES, lds, &per_cu);
     if (st != QW3_OK) return st;
     void *base = nullptr;
-    if (cv.off > 0) {
-        st = src.get(cv.off, &base);
-        if (st != QW3_OK) return st;
-    }
+    st = src.get(cv.off, &base);
+    if (st != QW3_OK) return st;
     char *b = static_cast<char *>(base);
     uint4 *xq = reinterpret_cast<uint4 *>(b + xq_at);
     int16_t *xe = reinterpret_cast<int16_t *>(b + xe_at);
@@ -1769,19 +1804,14 @@ qw3_status launch_gemm_mt(const uint16_t *x, const uint32_t *packed, const uint1
     const hipStream_t stream = src.stream;
     for (int64_t m0 = 0; m0 < M && st == QW3_OK; m0 += Mp) {
         const int mc = (int)(M - m0 < Mp ? M - m0 : Mp);
-        if (!xh) {
-            const int64_t units = (int64_t)(G / 8) * Mp * 32;
-            hipLaunchKernelGGL(prep_x_slice_kernel, dim3((unsigned)ceil_div(units, 256)), dim3(256), 0, stream,
-                               x + m0 * K, xq, xe, xd, mc, Mp, K, G / 8);
-            st = check_launch();
-            if (st != QW3_OK) break;
-        }
+        const int64_t units = (int64_t)(G / 8) * Mp * 32;
+        hipLaunchKernelGGL(prep_x_slice_kernel, dim3((unsigned)ceil_div(units, 256)), dim3(256), 0, stream,
+                           x + m0 * K, xq, xe, xd, mc, Mp, K, G / 8);
+        st = check_launch();
+        if (st != QW3_OK) break;
         float *dst = C > 1 ? part : y + m0 * N;
-        if (xh)
-            hipLaunchKernelGGL((qgemm_mr_kernel<WAVES, TS, TS == 1>), dim3((unsigned)(tb * C)), dim3(64 * WAVES), lds,
-                               stream, xq, xe, xd, x + m0 * K, packed, scales, dst, mc, N, G, C, (int64_t)Mp * N);
-        else if (ring)
-            hipLaunchKernelGGL((qgemm_mr_kernel<WAVES, TS, false>), dim3((unsigned)(tb * C)), dim3(64 * WAVES), lds,
+        if (ring)
+            hipLaunchKernelGGL((qgemm_mr_kernel<WAVES, TS>), dim3((unsigned)(tb * C)), dim3(64 * WAVES), lds,
                                stream, xq, xe, xd, x + m0 * K, packed, scales, dst, mc, N, G, C, (int64_t)Mp * N);
         else
             hipLaunchKernelGGL(qgemm_mt_kernel<WAVES>, dim3((unsigned)(tb * C)), dim3(64 * WAVES), 0, stream, xq, xe,
@@ -1796,20 +1826,20 @@ qw3_status launch_gemm_mt(const uint16_t *x, const uint32_t *packed, const uint1
     return st;
 }
 
-// Up to four tokens: qgemm_m4_kernel, WAVES x 8 groups per K chunk (scale
-// rows 8-byte aligned).
-template <int WAVES>
+// Up to TOK (4 or 8) tokens: qgemm_m4_kernel, WAVES x 8 groups per K chunk
+// (scale rows 8-byte aligned).
+template <int WAVES, int TOK>
 qw3_status launch_gemm_m4(const uint16_t *x, const uint32_t *packed, const uint16_t *scales, float *y, int64_t M,
                           int64_t N, int64_t K, const ScratchSrc &src) {
-    constexpr int Mp = 4;  // token slots of the partial sums
+    constexpr int Mp = TOK;  // token slots of the partial sums
     const int G = (int)(K / kGroup);
     const int C = G / (8 * WAVES);
     const size_t part_bytes = C > 1 ? (size_t)C * Mp * (size_t)N * sizeof(float) : 0;
-    const size_t lds = m4_lds<WAVES>();
+    const size_t lds = m4_lds<WAVES, TOK>();
     int cus = 0, per_cu = 0;
     qw3_status st = cu_count(&cus);
     if (st == QW3_OK)
-        st = blocks_per_cu(reinterpret_cast<const void *>(&qgemm_m4_kernel<WAVES>), 64 * WAVES, lds, &per_cu);
+        st = blocks_per_cu(reinterpret_cast<const void *>(&qgemm_m4_kernel<WAVES, TOK>), 64 * WAVES, lds, &per_cu);
     if (st != QW3_OK) return st;
     float *part = nullptr;
     if (part_bytes > 0) {
@@ -1822,8 +1852,8 @@ qw3_status launch_gemm_m4(const uint16_t *x, const uint32_t *packed, const uint1
     int64_t tb = (int64_t)cus * per_cu / C;
     if (tb < 1) tb = 1;
     if (tb > tiles) tb = tiles;
-    hipLaunchKernelGGL(qgemm_m4_kernel<WAVES>, dim3((unsigned)(tb * C)), dim3(64 * WAVES), lds, src.stream, x, packed,
-                       scales, C > 1 ? part : y, (int)M, N, G, C, (int64_t)Mp * N);
+    hipLaunchKernelGGL((qgemm_m4_kernel<WAVES, TOK>), dim3((unsigned)(tb * C)), dim3(64 * WAVES), lds, src.stream, x,
+                       packed, scales, C > 1 ? part : y, (int)M, N, G, C, (int64_t)Mp * N);
     st = check_launch();
     if (st != QW3_OK || C == 1) return st;
     const int64_t count = M * N;
@@ -1841,12 +1871,19 @@ qw3_status launch_gemm_small(const uint16_t *x, const uint32_t *packed, const ui
         if (M >= kPfMinM) return launch_gemm_pf(x, packed, scales, y, M, N, K, src);
         return launch_gemm_tile(x, packed, scales, y, M, N, K, src);
     }
-    // Batched decode: 17..32 tokens in one pass when the scale rows allow the
-    // ring kernel (chunks of 8 waves x 4 groups); otherwise passes of up to
-    // 16 tokens in chunks of 8 waves x 8 groups (or 7 x 8 when K = 28672).
+    // Batched decode.  With 8-byte aligned scale rows: up to 4 and up to 8
+    // tokens in the batch-1 layout, converting the activations in the kernel
+    // (8 tokens: about 1 us faster than the ring kernel with its conversion
+    // launch on both MLP shapes); 17..32 tokens in one pass of the ring kernel
+    // (chunks of 8 waves x 4 groups).  Otherwise passes of up to 16 tokens in
+    // chunks of 8 waves x 8 groups (or 7 x 8 when K = 28672).
     if (M <= 4 && aligned(scales, 8)) {
-        if (G % 64 == 0) return launch_gemm_m4<8>(x, packed, scales, y, M, N, K, src);
-        if (G % 56 == 0) return launch_gemm_m4<7>(x, packed, scales, y, M, N, K, src);
+        if (G % 64 == 0) return launch_gemm_m4<8, 4>(x, packed, scales, y, M, N, K, src);
+        if (G % 56 == 0) return launch_gemm_m4<7, 4>(x, packed, scales, y, M, N, K, src);
+    }
+    if (M <= 8 && aligned(scales, 8)) {
+        if (G % 64 == 0) return launch_gemm_m4<8, 8>(x, packed, scales, y, M, N, K, src);
+        if (G % 56 == 0) return launch_gemm_m4<7, 8>(x, packed, scales, y, M, N, K, src);
     }
     if (M > 16 && aligned(scales, 8) && G % 32 == 0) return launch_gemm_mt<8, 2>(x, packed, scales, y, M, N, K, src);
     if (G % 64 == 0) return launch_gemm_mt<8, 1>(x, packed, scales, y, M, N, K, src);

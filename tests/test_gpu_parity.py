@@ -611,8 +611,8 @@ def test_layer_projection_b1_full_size(name):
 
 @pytest.mark.parametrize("name", ["gate_proj", "down_proj"])
 def test_gate_down_b1_and_batched_full_size(name):
-    """Batch 1 and batched decode M = 4, 8, 16, 32, every output."""
-    check_layer_full(name, [1, 4, 8, 16, 32])
+    """Batch 1 and batched decode M = 4, 6, 8, 16, 32, every output."""
+    check_layer_full(name, [1, 4, 6, 8, 16, 32])
 
 
 @pytest.mark.parametrize("name", ["gate_proj", "down_proj"])
