@@ -127,6 +127,13 @@ def test_guard_batched(kind, m, n, k):
     run_and_check(kind, m, n, k, 200 + m + k)
 
 
+# batched decode on a matrix of 26000 rows (7 tiles of 16 rows per CU)
+@pytest.mark.parametrize("kind", ["x", "s"])
+@pytest.mark.parametrize("m", [9, 16])
+def test_guard_many_tiles(kind, m):
+    run_and_check(kind, m, 26000, 2048, 700 + m)
+
+
 # 2-byte aligned scale rows (the 16-token pass reading two bytes at a time)
 # and 8-byte aligned but not 16 (the ring and four-token kernels)
 @pytest.mark.parametrize("m", [3, 8, 24])

@@ -468,6 +468,24 @@ def test_qgemm_chunked_k(m, n, k):
     assert_close(y, yr, a, "qgemm chunked M=%d %dx%d" % (m, n, k))
 
 
+@pytest.mark.parametrize("m,n,k,off", [(9, 28672, 8192, 0), (16, 26000, 2048, 0), (12, 30001, 4096, 1),
+                                       (3, 28672, 2048, 1), (13, 32768, 2048, 4), (16, 25000, 28672, 0)])
+def test_qgemm_many_tiles_per_cu(m, n, k, off):
+    """Batched decode on matrices of 25000..32768 rows (7 or 8 tiles of 16
+    rows per CU), every output compared: ragged N, 2- and 8-byte aligned
+    scale views (offset by 1 or 4 elements), K = 2048 .. 28672."""
+    say("qgemm many tiles per CU", m, n, k, "scale offset", off)
+    c = synth.codes_all8(5000 + m + n, n, k)
+    s = synth.scales(5001 + k, n, k // 128, sigma=0.02, eps=1e-3)
+    x = synth.activations(5002 + m, m, k)
+    big = torch.zeros(s.size + 8, dtype=torch.int16, device="cuda")
+    big[off:off + s.size] = torch.from_numpy(s.reshape(-1).view(np.int16)).cuda()
+    sv = big[off:off + s.size].view(n, k // 128)
+    y = host(q().qgemm_w3g128_smallM(dev(x), gpu_pack(c), sv))
+    yr, a = oracle.gemm(x, oracle.pack(c), s, k)
+    assert_close(y, yr, a, "qgemm many tiles M=%d %dx%d" % (m, n, k))
+
+
 @pytest.mark.parametrize("m,n,k", [(300, 72, 1024), (129, 300, 2048), (520, 260, 4096)])
 def test_qgemm_large_m_tiles(m, n, k):
     # ragged 256-token and 256-row tiles, K split into chunks
