@@ -610,12 +610,11 @@ def traffic_from_counters(fetch_csv: str, write_csv: str, out_path: str = TRAFFI
            "hbm_read_bytes_per_launch": rd, "hbm_write_bytes_per_launch": wr, "hbm_bytes_per_launch": rd + wr,
            "algorithmic_bytes_per_launch": alg, "traffic_over_algorithmic": round((rd + wr) / alg, 4),
            "dispatches_averaged": nd,
-           "commands": ["rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- "
-                        "python3 bench.py --steps 10 --warmup 2 --no-cpu-baseline --no-summary --calibrate",
-                        "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- "
-                        "python3 bench.py --steps 10 --warmup 2 --no-cpu-baseline --no-summary --calibrate",
-                        "python3 bench.py --traffic-from gpurun_out/pmc_fetch/run_counter_collection.csv "
-                        "gpurun_out/pmc_write/run_counter_collection.csv"]}
+           "commands": ["cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc %s --output-format csv -d %s -o run -- "
+                        "python3 /root/repo/bench.py --steps 10 --warmup 2 --no-cpu-baseline --no-summary --calibrate"
+                        % (counter, os.path.dirname(path)) for counter, path in
+                        (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv))]
+                       + ["python3 bench.py --traffic-from %s %s" % (fetch_csv, write_csv)]}
     with open(out_path, "w") as fh:
         json.dump(rec, fh, indent=1)
         fh.write("\n")
