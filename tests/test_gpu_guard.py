@@ -142,10 +142,11 @@ def test_guard_scale_views(m, off):
     run_and_check("x", m, 40, 8192, 300 + m + off, scale_offset=off)
 
 
-# 128-token tiles (33..128 tokens) and 256-token prefill tiles (K split)
+# 33..128 tokens in passes of 32 (K / 128 a multiple of 32) and on the
+# 128-token tiles (K / 128 = 8 or 24), 256-token prefill tiles (K split)
 @pytest.mark.parametrize("kind", ["x", "s"])
-@pytest.mark.parametrize("m,n,k", [(33, 64, 8192), (100, 130, 4096), (129, 72, 4096), (512, 64, 2048),
-                                   (300, 260, 1024)])
+@pytest.mark.parametrize("m,n,k", [(33, 64, 8192), (100, 130, 4096), (48, 96, 1024), (100, 130, 3072),
+                                   (129, 72, 4096), (512, 64, 2048), (300, 260, 1024)])
 def test_guard_tiles(kind, m, n, k):
     run_and_check(kind, m, n, k, 400 + m + n)
 
