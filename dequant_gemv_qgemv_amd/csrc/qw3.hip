@@ -1864,17 +1864,48 @@ qw3_status launch_gemm_m4(const uint16_t *x, const uint32_t *packed, const uint1
     return check_launch();
 }
 
+// Waves per workgroup of the batched-decode kernels, whose waves own 8 groups
+// (one activation slice) each: the largest w <= 8 with G a multiple of 8 w,
+// so that a workgroup's w slices tile K exactly (K = 8192: 8, 28672: 7,
+// 4096: 4, 53248: 4); 0 when G is not a multiple of 8.
+int slice_waves(int G) {
+    if (G % 8 != 0) return 0;
+    for (int w = 8; w > 1; --w)
+        if ((G / 8) % w == 0) return w;
+    return 1;
+}
+
+// f(std::integral_constant<int, w>{}) for w = 1..8.
+template <class F>
+qw3_status with_waves(int w, F &&f) {
+    switch (w) {
+        case 8: return f(std::integral_constant<int, 8>{});
+        case 7: return f(std::integral_constant<int, 7>{});
+        case 6: return f(std::integral_constant<int, 6>{});
+        case 5: return f(std::integral_constant<int, 5>{});
+        case 4: return f(std::integral_constant<int, 4>{});
+        case 3: return f(std::integral_constant<int, 3>{});
+        case 2: return f(std::integral_constant<int, 2>{});
+        case 1: return f(std::integral_constant<int, 1>{});
+        default: return QW3_ERR_SHAPE;
+    }
+}
+
 // Small-M path: convert x once into scratch, then one streaming pass over W
 // per chunk of up to 32 tokens.
 qw3_status launch_gemm_small(const uint16_t *x, const uint32_t *packed, const uint16_t *scales, float *y,
                              int64_t M, int64_t N, int64_t K, const ScratchSrc &src) {
     const int G = (int)(K / kGroup);
+    const int w = slice_waves(G);
     if (M > 32) {
         if (M >= kPfMinM) return launch_gemm_pf(x, packed, scales, y, M, N, K, src);
         // 33..128 tokens: passes of 32 through the ring kernel (weights read
         // once per pass) when it applies -- gate_proj M = 64 in 66 us, down_proj
-        // 68, q_proj 37, against 140, 458 and 139 on the 128-token tiles.
+        // 68, q_proj 37, against 140, 458 and 139 on the 128-token tiles --
+        // else passes of 16 when K / 1024 is whole.
         if (aligned(scales, 8) && G % 32 == 0) return launch_gemm_mt<8, 2>(x, packed, scales, y, M, N, K, src);
+        if (w > 0)
+            return with_waves(w, [&](auto wc) { return launch_gemm_mt<decltype(wc)::value, 1>(x, packed, scales, y, M, N, K, src); });
         return launch_gemm_tile(x, packed, scales, y, M, N, K, src);
     }
     // Batched decode.  With 8-byte aligned scale rows: up to 4 and up to 8
@@ -1882,18 +1913,16 @@ qw3_status launch_gemm_small(const uint16_t *x, const uint32_t *packed, const ui
     // (8 tokens: about 1 us faster than the ring kernel with its conversion
     // launch on both MLP shapes); 17..32 tokens in one pass of the ring kernel
     // (chunks of 8 waves x 4 groups).  Otherwise passes of up to 16 tokens in
-    // chunks of 8 waves x 8 groups (or 7 x 8 when K = 28672).
-    if (M <= 4 && aligned(scales, 8)) {
-        if (G % 64 == 0) return launch_gemm_m4<8, 4>(x, packed, scales, y, M, N, K, src);
-        if (G % 56 == 0) return launch_gemm_m4<7, 4>(x, packed, scales, y, M, N, K, src);
-    }
-    if (M <= 8 && aligned(scales, 8)) {
-        if (G % 64 == 0) return launch_gemm_m4<8, 8>(x, packed, scales, y, M, N, K, src);
-        if (G % 56 == 0) return launch_gemm_m4<7, 8>(x, packed, scales, y, M, N, K, src);
+    // chunks of w waves x 8 groups (slice_waves: 8 at K = 8192, 7 at 28672).
+    // The 4- and 8-token kernels and the 16-token passes need K / 1024 whole.
+    if (w > 0 && M <= 8 && aligned(scales, 8)) {
+        if (M <= 4)
+            return with_waves(w, [&](auto wc) { return launch_gemm_m4<decltype(wc)::value, 4>(x, packed, scales, y, M, N, K, src); });
+        return with_waves(w, [&](auto wc) { return launch_gemm_m4<decltype(wc)::value, 8>(x, packed, scales, y, M, N, K, src); });
     }
     if (M > 16 && aligned(scales, 8) && G % 32 == 0) return launch_gemm_mt<8, 2>(x, packed, scales, y, M, N, K, src);
-    if (G % 64 == 0) return launch_gemm_mt<8, 1>(x, packed, scales, y, M, N, K, src);
-    if (G % 56 == 0) return launch_gemm_mt<7, 1>(x, packed, scales, y, M, N, K, src);
+    if (w > 0)
+        return with_waves(w, [&](auto wc) { return launch_gemm_mt<decltype(wc)::value, 1>(x, packed, scales, y, M, N, K, src); });
     const int mchunk = M > 16 ? 32 : 16;
     Carve cv;
     const size_t xq_at = cv.take((size_t)mchunk * (size_t)K * 2);

@@ -134,6 +134,14 @@ def test_guard_many_tiles(kind, m):
     run_and_check(kind, m, 26000, 2048, 700 + m)
 
 
+# batched kernels with 5 and 4 waves per workgroup (K = 5120, 4096)
+@pytest.mark.parametrize("kind", ["x", "s"])
+@pytest.mark.parametrize("m", [4, 8, 16, 48])
+@pytest.mark.parametrize("n,k", [(72, 5120), (40, 4096)])
+def test_guard_slice_waves(kind, m, n, k):
+    run_and_check(kind, m, n, k, 800 + m + k)
+
+
 # 2-byte aligned scale rows (the 16-token pass reading two bytes at a time)
 # and 8-byte aligned but not 16 (the ring and four-token kernels)
 @pytest.mark.parametrize("m", [3, 8, 24])

@@ -486,6 +486,22 @@ def test_qgemm_many_tiles_per_cu(m, n, k, off):
     assert_close(y, yr, a, "qgemm many tiles M=%d %dx%d" % (m, n, k))
 
 
+@pytest.mark.parametrize("m", [3, 8, 16, 40])
+@pytest.mark.parametrize("n,k", [(50, 2048), (40, 3072), (300, 4096), (36, 5120), (64, 6144), (20, 53248)])
+def test_qgemm_slice_waves(m, n, k):
+    """The batched kernels with 2..6 waves per workgroup (K / 1024 = 2, 3, 4, 5,
+    6 and 52: one 8-group slice per wave, the largest wave count up to 8 that
+    tiles K; K = 53248 in 13 K chunks), up to 8 tokens in the batch-1 layout,
+    16-token passes, and 40 tokens in passes of 32 or 16."""
+    say("qgemm slice waves", m, n, k)
+    c = synth.codes_all8(5100 + n + k, n, k)
+    s = synth.scales(5101 + k, n, k // 128, sigma=0.02, eps=1e-3)
+    x = synth.activations(5102 + m, m, k)
+    y = host(q().qgemm_w3g128_smallM(dev(x), gpu_pack(c), dev(s)))
+    yr, a = oracle.gemm(x, oracle.pack(c), s, k)
+    assert_close(y, yr, a, "qgemm slice waves M=%d %dx%d" % (m, n, k))
+
+
 @pytest.mark.parametrize("m,n,k", [(300, 72, 1024), (129, 300, 2048), (520, 260, 4096)])
 def test_qgemm_large_m_tiles(m, n, k):
     # ragged 256-token and 256-row tiles, K split into chunks
