@@ -169,15 +169,28 @@ __global__ __launch_bounds__(256) void prep_x_kernel(const uint16_t *__restrict_
     }
 }
 
-// Streaming small-M product on v_mfma_f32_16x16x32_f16.  One wave owns 16
-// output rows and walks all groups.  Lane l works on row n0 + l%16 and block
-// j = l/16 of each group: it decodes 32 codes (3 words) into the B operand
-// (8 fp16 per MFMA, 4 MFMAs per group) while the A operand holds the same
-// k-slots of x' for token l%16.  D[m][n] of one group is scaled by
-// s[n][g] * 2^e[g][m] and added to the fp32 accumulator.  MT tiles of 16
-// tokens share each decoded B operand, so the weights are read once.
+// Batched decode for any K (the path of K / 128 not a multiple of 8, where no
+// whole 8-group activation slices exist), on v_mfma_f32_16x16x32_f16.  One
+// workgroup of 8 waves per 16-row tile; wave w takes groups w, w + 8, ... of
+// the tile.  Lane l works on row n0 + l%16 and block j = l/16 of each group:
+// it decodes 32 codes (3 words) into the B operand (8 fp16 per MFMA, 4 MFMAs
+// per group) while the A operand holds the same k-slots of x' for token l%16.
+// D[m][n] of one group is scaled by s[n][g] * 2^e[g][m] and added to the fp32
+// accumulator.  MT sets of 16 tokens share each decoded B operand, so the
+// weights are read once.  Each wave keeps its next groups' words, scale, A
+// operands and exponents in a 3-slot register ring, loaded two groups ahead
+// (loads past its last group re-read that group, so the waits stay exact);
+// the 8 waves' accumulators meet in LDS and are added in wave order.
+typedef unsigned u32x3g_t __attribute__((ext_vector_type(3)));
 template <int MT>
-__global__ __launch_bounds__(256) void qgemm_mfma_kernel(const uint4 *__restrict__ xq,
+struct MfSlotG {
+    u32x3g_t w;        // block j of the group of row n
+    uint32_t s;        // its bf16 scale (low half)
+    h8_t a[MT][4];     // A operands: x' of token 16 mt + n, block j
+    uint32_t e[MT][2]; // exponents (2 e + flag) of tokens 16 mt + 4 j .. + 3
+};
+template <int MT>
+__global__ __launch_bounds__(512) void qgemm_mfma_kernel(const uint4 *__restrict__ xq,
                                                          const int16_t *__restrict__ xe,
                                                          const float *__restrict__ xd,
                                                          const uint16_t *__restrict__ x,
@@ -185,10 +198,13 @@ __global__ __launch_bounds__(256) void qgemm_mfma_kernel(const uint4 *__restrict
                                                          const uint16_t *__restrict__ scales,
                                                          float *__restrict__ y, int M, int Mp,
                                                          int64_t N, int G, int64_t y_ld) {
+    constexpr int WAVES = 8;
+    __shared__ __align__(16) f4_t red[WAVES][MT][64];
+    __shared__ uint32_t flags[16];
     const int lane = threadIdx.x & 63;
-    const int64_t wblk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int64_t n0 = wblk * 16;
-    if (n0 >= N) return;  // whole wave
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t wblk = blockIdx.x;
+    const int64_t n0 = wblk * 16;  // the grid has ceil(N / 16) workgroups
     const int nl = lane & 15;
     const int jq = lane >> 4;
     const int64_t n = n0 + nl;
@@ -196,61 +212,93 @@ __global__ __launch_bounds__(256) void qgemm_mfma_kernel(const uint4 *__restrict
     const int64_t W = (int64_t)G * kWordsPerGroup;
     const uint32_t *wrow = packed + nrow * W + jq * 3;
     const uint16_t *srow = scales + nrow * G;
+    const int steps = (G - wave + WAVES - 1) / WAVES;  // this wave's groups (0 when wave >= G)
 
+    auto load = [&](int i, MfSlotG<MT> &sl) {
+        int g = wave + WAVES * i;
+        g = g < G ? g : G - 1;
+        sl.w = *reinterpret_cast<const u32x3g_t *>(wrow + (int64_t)g * kWordsPerGroup);
+        sl.s = srow[g];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const uint4 *ap = xq + (((int64_t)g * Mp + mt * 16 + nl) * 4 + jq) * 4;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) sl.a[mt][t] = __builtin_bit_cast(h8_t, ap[t]);
+            const uint2 ev = *reinterpret_cast<const uint2 *>(xe + (int64_t)g * Mp + mt * 16 + 4 * jq);
+            sl.e[mt][0] = ev.x;
+            sl.e[mt][1] = ev.y;
+        }
+    };
     f4_t acc[MT];
 #pragma unroll
     for (int t = 0; t < MT; ++t) acc[t] = f4_t{0.f, 0.f, 0.f, 0.f};
     const uint32_t magic = magic_vgpr();
     int small = 0;
-
-    for (int g = 0; g < G; ++g) {
-        const uint32_t *wp = wrow + (int64_t)g * kWordsPerGroup;
-        const uint32_t w0 = wp[0], w1 = wp[1], w2 = wp[2];
-        const float s = bf16_to_f32(srow[g]);
+    auto step = [&](const MfSlotG<MT> &sl) __attribute__((always_inline)) {
         h2_t q[16];
-        decode_block(w0, w1, w2, magic, q);
-        h8_t bop[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-            bop[t] = h8_t{q[4 * t].x, q[4 * t].y, q[4 * t + 1].x, q[4 * t + 1].y,
-                          q[4 * t + 2].x, q[4 * t + 2].y, q[4 * t + 3].x, q[4 * t + 3].y};
+        decode_block(sl.w.x, sl.w.y, sl.w.z, magic, q);
+        const float s = bf16_to_f32(sl.s & 0xFFFFu);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-            h8_t aop[4];
-            if (mt * 16 + nl < M) {
-                const uint4 *ap = xq + (((int64_t)g * Mp + mt * 16 + nl) * 4 + jq) * 4;
-#pragma unroll
-                for (int t = 0; t < 4; ++t) aop[t] = __builtin_bit_cast(h8_t, ap[t]);
-            } else {
-#pragma unroll
-                for (int t = 0; t < 4; ++t) aop[t] = h8_t{0, 0, 0, 0, 0, 0, 0, 0};
-            }
             f4_t d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int t = 0; t < 4; ++t) d = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop[t], bop[t], d, 0, 0, 0);
-            const int16_t *ep = xe + (int64_t)g * Mp + mt * 16 + 4 * jq;
+            for (int t = 0; t < 4; ++t) {
+                const h8_t bop = {q[4 * t].x,     q[4 * t].y,     q[4 * t + 1].x, q[4 * t + 1].y,
+                                  q[4 * t + 2].x, q[4 * t + 2].y, q[4 * t + 3].x, q[4 * t + 3].y};
+                d = __builtin_amdgcn_mfma_f32_16x16x32_f16(sl.a[mt][t], bop, d, 0, 0, 0);
+            }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int ev = ep[r];
+                const uint32_t ew = sl.e[mt][r >> 1];
+                const int ev = (r & 1) ? (int)ew >> 16 : (int)(int16_t)(ew & 0xFFFFu);
                 small |= ev & 1;
                 acc[mt][r] += ldexpf(d[r], ev >> 1) * s;
             }
         }
+    };
+    MfSlotG<MT> ring[3];
+    __builtin_amdgcn_sched_barrier(0);
+    load(0, ring[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    load(1, ring[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    int i = 0;
+    for (; i + 3 <= steps; i += 3) {  // wave-uniform
+        load(i + 2, ring[2]);
+        __builtin_amdgcn_sched_barrier(0);
+        step(ring[0]);
+        load(i + 3, ring[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        step(ring[1]);
+        load(i + 4, ring[1]);
+        __builtin_amdgcn_sched_barrier(0);
+        step(ring[2]);
     }
-    const bool fix = __ballot(small != 0) != 0;  // wave-uniform, rare
-    if (n < N) {
+    if (i < steps) step(ring[0]);
+    if (i + 1 < steps) step(ring[1]);
+
+    publish_flag(small != 0, flags);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+    for (int mt = 0; mt < MT; ++mt) red[wave][mt][lane] = acc[mt];
+    __syncthreads();
+    // (set, lane row, r, row) outputs, rows fastest; waves added in order.
+    for (int o = threadIdx.x; o < 256 * MT; o += 512) {
+        const int row16 = o & 15, r = (o >> 4) & 3, jj = (o >> 6) & 3, mt = o >> 8;
+        const int tok = mt * 16 + 4 * jj + r;
+        const int64_t row = n0 + row16;
+        if (tok < M && row < N) {
+            const float *src = reinterpret_cast<const float *>(&red[0][mt][16 * jj + row16]) + r;
+            float tot = src[0];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = mt * 16 + 4 * jq + r;
-                if (m < M) y[(int64_t)m * y_ld + n] = acc[mt][r];
-            }
+            for (int w = 1; w < WAVES; ++w) tot += src[w * MT * 64 * 4];
+            y[(int64_t)tok * y_ld + row] = tot;
+        }
     }
-    if (fix) {
-        __threadfence_block();  // this wave's stores above land before the fixup's
-        fixup_outputs<4>(x, (int64_t)G * kGroup, M, packed, scales, G, 0, G, BlockRows{wblk, (N + 15) / 16, 16, N},
-                         [&](int m, int g) { return xd[(int64_t)g * Mp + m]; }, nullptr, 0, false, y, y_ld, lane, 64);
+    if (any_flag(flags)) {  // workgroup-uniform (published before the barrier), rare
+        __syncthreads();
+        fixup_outputs<4>(x, (int64_t)G * kGroup, M, packed, scales, G, 0, G, BlockRows{wblk, (int64_t)gridDim.x, 16, N},
+                         [&](int m, int g) { return xd[(int64_t)g * Mp + m]; }, nullptr, 0, false, y, y_ld,
+                         threadIdx.x, blockDim.x);
     }
 }
 
@@ -1000,8 +1048,7 @@ constexpr size_t m4_lds() {
 // [8, 16).  A = x * 2^-(E[m] + p) in fp16 with one exponent per token (largest
 // |x| of the token maps to [2^14, 2^15); exact down to 2^-28 of it).  The
 // accumulators then hold sum_k x w * 2^-(E[m] + E[n]), rescaled once at the
-// end.  Tiles are 128 tokens x 128 rows x one group (128 k) per step, double
-// buffered in LDS; each wave owns 64 x 64 of the output (16 MFMA tiles).
+// end.  The activation tiles go through LDS one group (128 k) at a time;
 // LDS rows (256 bytes = 16 chunks of 16 bytes) are stored with chunk index
 // XOR (row & 15) so that the 16 lanes of a quarter-wave reading one chunk of
 // 16 consecutive rows hit 16 different bank groups.
@@ -1069,7 +1116,7 @@ __global__ __launch_bounds__(256) void prep_tile_x_kernel(const uint16_t *__rest
     }
 }
 
-// The fixup pass of one tile-kernel workgroup, out of line so that the main
+// The fixup pass of one prefill workgroup, out of line so that the main
 // kernel's registers stay with its MFMA loop: tokens [0, mt) of the tile (x,
 // xd and y already offset to its first token), rows of `rows`, groups
 // [g0, g1), every row's fold checked.  All threads call it.
@@ -1085,7 +1132,7 @@ __device__ __noinline__ void fixup_tile_call(const uint16_t *x, int64_t K, int m
     fixup_outputs<8>(x, K, mt, packed, scales, G, g0, g1, rows, d_at, nz, nnz, true, y, ldo, threadIdx.x, blockDim.x);
 }
 
-// Whether the tile kernels' fast result may be outside the accuracy bound
+// Whether the prefill kernel's fast result may be outside the accuracy bound
 // for an output of row set / token set whose largest row exponent is en_max
 // (largest scale below 2^(en_max + 4)) and whose largest token error mass is
 // dmax: 4 s D > budget.
@@ -1093,233 +1140,10 @@ __device__ __forceinline__ bool tile_coarse_flag(int en_max, float dmax) {
     return dmax > 0.f && !(4.0f * ldexpf(dmax, en_max + 4) <= kFixBudget);
 }
 
-constexpr int kTileBM = 128;
-constexpr int kTileBN = 128;
-constexpr int kTileRow = 256;  // bytes of one row of one group (128 fp16)
-constexpr size_t kTileStage = (size_t)(kTileBM + kTileBN) * kTileRow;
-// LDS: two stages, the row exponents [kTileBN], 16 wave flags, the fixup's list.
-constexpr size_t kTileLds = 2 * kTileStage + ((size_t)kTileBN + 16 + kNzCap + 1) * 4;
+constexpr int kTileRow = 256;  // bytes of one LDS row: one token's group (128 fp16)
 
 __device__ __forceinline__ int tile_off(int row, int chunk) { return row * kTileRow + ((chunk ^ (row & 15)) << 4); }
 
-// One pipeline stage of the tile GEMM held in registers: this thread's share
-// of a group's activations (8 x 16 B) and of its packed words and scales
-// (two 12-byte blocks).
-typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
-
-struct TileStage {
-    u32x4_t a[8];  // native vector type: stays in registers (HIP's uint4 struct copies did not)
-    uint32_t w[6];
-    uint32_t s[2];
-};
-
-__device__ __forceinline__ void tile_load(TileStage &st, const uint32_t *a_src, const uint32_t *const (&b_w)[2],
-                                          const uint16_t *const (&b_s)[2], int g) {
-    const u32x4_t *ap = reinterpret_cast<const u32x4_t *>(a_src + (int64_t)g * 64);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) st.a[i] = ap[i];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const uint32_t *wp = b_w[h] + (int64_t)g * kWordsPerGroup;
-        st.w[3 * h] = wp[0];
-        st.w[3 * h + 1] = wp[1];
-        st.w[3 * h + 2] = wp[2];
-        st.s[h] = b_s[h][g];
-    }
-}
-
-// Activations as they are; weights decoded to (c-4) * 2^p * s * 2^-E[row].
-__device__ __forceinline__ void tile_store(const TileStage &st, unsigned char *sa, int a_row, int a_half, int tid,
-                                           int b_blk, const int (&b_e)[2], uint32_t magic) {
-    unsigned char *sb = sa + (size_t)kTileBM * kTileRow;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4_t *>(sa + tile_off(a_row, a_half * 8 + i)) = st.a[i];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        h2_t q[16];
-        decode_block(st.w[3 * h], st.w[3 * h + 1], st.w[3 * h + 2], magic, q);
-        const _Float16 sv = (_Float16)ldexpf(bf16_to_f32(st.s[h]), -b_e[h]);
-        const h2_t s2 = {sv, sv};
-        const int rl = h * 64 + (tid >> 2);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const uint4 v = make_uint4(__builtin_bit_cast(uint32_t, q[4 * c] * s2),
-                                       __builtin_bit_cast(uint32_t, q[4 * c + 1] * s2),
-                                       __builtin_bit_cast(uint32_t, q[4 * c + 2] * s2),
-                                       __builtin_bit_cast(uint32_t, q[4 * c + 3] * s2));
-            *reinterpret_cast<uint4 *>(sb + tile_off(rl, 4 * b_blk + c)) = v;
-        }
-    }
-}
-
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void qgemm_tile_kernel(
-    const uint32_t *__restrict__ xq, const int *__restrict__ xe, const float *__restrict__ xd,
-    const float *__restrict__ dtot, const uint16_t *__restrict__ x, const uint32_t *__restrict__ packed,
-    const uint16_t *__restrict__ scales, float *__restrict__ y, int M, int MT, int64_t N, int G) {
-    extern __shared__ __align__(16) unsigned char lds[];
-    int *En = reinterpret_cast<int *>(lds + 2 * kTileStage);
-    uint32_t *flags = reinterpret_cast<uint32_t *>(En + kTileBN);
-    int *nz = reinterpret_cast<int *>(flags + 16);
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave & 1, wn = wave >> 1;
-    // Token-tile major: the workgroups in flight together share one token
-    // tile, which then stays in each XCD's L2 while the weight tiles stream.
-    const int64_t NT = (N + kTileBN - 1) / kTileBN;
-    const int m_tile = (int)(blockIdx.x / NT);
-    const int64_t n_tile = blockIdx.x - (int64_t)m_tile * NT;
-    const int64_t n0 = n_tile * kTileBN;
-    const int m0 = m_tile * kTileBM;
-    const int64_t K = (int64_t)G * kGroup;
-    const int64_t W = (int64_t)G * kWordsPerGroup;
-
-    // Row exponents: the largest scale of each row maps to [8, 16).  A row
-    // whose smallest non-zero scale lies below 2^(E - 17) does not fold
-    // exactly (fold_inexact): its outputs are recomputed after the loop.
-    bool need = false;
-    if (tid < kTileBN) {
-        int64_t r = n0 + tid;
-        r = r < N ? r : N - 1;
-        uint32_t mx = 0, mn = 0x10000u;
-        for (int g = 0; g < G; ++g) {
-            const uint32_t b = (uint32_t)scales[r * G + g] & 0x7FFFu;
-            mx = max(mx, b);
-            if (b) mn = min(mn, b);
-        }
-        const int E = __builtin_amdgcn_frexp_expf(bf16_to_f32(mx)) - 4;
-        En[tid] = E;
-        need = mx != 0 && bf16_to_f32(mn) < ldexpf(1.0f, E - 17);
-    }
-    __syncthreads();
-    // The guard, decided before the loop: a row that does not fold exactly,
-    // or a token error mass large enough to matter against this lane's rows.
-    {
-        float dmax = 0.f;
-        int en_max = -1000;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int tok = m0 + (wave & 1) * 64 + 16 * i + 4 * ((tid & 63) >> 4) + r;
-                dmax = fmaxf(dmax, dtot[tok < M ? tok : M - 1]);
-            }
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) en_max = max(en_max, En[(wave >> 1) * 64 + 16 * jj + (tid & 15)]);
-        publish_flag(need || tile_coarse_flag(en_max, dmax), flags);
-    }
-    __syncthreads();
-    const bool fix = __builtin_amdgcn_readfirstlane(any_flag(flags) ? 1 : 0) != 0;
-
-    // Loader roles.  A: token tid/2, 64 fp16 (half a group row) = 8 x 16 B.
-    // B: rows tid/4 and 64 + tid/4, block tid%4 (12 bytes each).
-    const int a_row = tid >> 1, a_half = tid & 1;
-    const uint32_t *a_src = xq + (int64_t)(m0 + a_row) * (K / 2) + a_half * 32;
-    const int b_blk = tid & 3;
-    int64_t b_r[2];
-    int b_e[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int rl = h * 64 + (tid >> 2);
-        int64_t r = n0 + rl;
-        b_r[h] = r < N ? r : N - 1;
-        b_e[h] = En[rl];
-    }
-    // Register ring of 3 stages: the operands of group g + 2 are loaded while
-    // group g is multiplied and group g + 1 is decoded into LDS, so two steps
-    // of latency are hidden.  Loads are unconditional (clamped to the last
-    // group) and the barrier waits for LDS only, so the loads stay in flight.
-    TileStage ring0, ring1, ring2;
-    const uint32_t *b_w[2] = {packed + b_r[0] * W + 3 * b_blk, packed + b_r[1] * W + 3 * b_blk};
-    const uint16_t *b_s[2] = {scales + b_r[0] * G, scales + b_r[1] * G};
-    const uint32_t magic = magic_vgpr();
-#define QW3_RING(k_) ((k_) == 0 ? ring0 : ((k_) == 1 ? ring1 : ring2))
-#define QW3_TILE_LOAD(k_, g_) tile_load(QW3_RING(k_), a_src, b_w, b_s, (g_))
-#define QW3_TILE_STORE(k_, buf_) \
-    tile_store(QW3_RING(k_), lds + (size_t)(buf_) * kTileStage, a_row, a_half, tid, b_blk, b_e, magic)
-
-    f4_t acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) acc[i][jj] = f4_t{0.f, 0.f, 0.f, 0.f};
-
-    const int lr = lane & 15, lc = lane >> 4;
-    auto mfma_group = [&](int buf) {
-        const unsigned char *sa = lds + (size_t)buf * kTileStage;
-        const unsigned char *sb = sa + (size_t)kTileBM * kTileRow;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            h8_t av[4], bv[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                av[i] = *reinterpret_cast<const h8_t *>(sa + tile_off(wm * 64 + 16 * i + lr, 4 * ks + lc));
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
-                bv[jj] = *reinterpret_cast<const h8_t *>(sb + tile_off(wn * 64 + 16 * jj + lr, 4 * ks + lc));
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj)
-                    acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[i], bv[jj], acc[i][jj], 0, 0, 0);
-        }
-    };
-
-    QW3_TILE_LOAD(0, 0);
-    QW3_TILE_LOAD(1, (1 < G ? 1 : G - 1));
-    QW3_TILE_STORE(0, 0);
-    lds_barrier();
-    // Step g: load g + 2 into slot (g + 2) % 3, multiply buffer g % 2, decode
-    // slot (g + 1) % 3 into buffer (g + 1) % 2, barrier.  Unrolled by 3 so the
-    // slots are static; steps past the last group only keep the pipeline shape.
-#define QW3_TILE_STEP(u_)                                                                       \
-    do {                                                                                        \
-        const int g_ = g + (u_);                                                                \
-        const int gl_ = g_ + 2 < G ? g_ + 2 : G - 1;                                            \
-        QW3_TILE_LOAD(((u_) + 2) % 3, gl_);                                                     \
-        if (g_ < G) mfma_group(g_ & 1);                                                         \
-        QW3_TILE_STORE(((u_) + 1) % 3, (g_ + 1) & 1);                                           \
-        lds_barrier();                                                                          \
-    } while (0)
-    for (int g = 0; g < G; g += 3) {
-        QW3_TILE_STEP(0);
-        QW3_TILE_STEP(1);
-        QW3_TILE_STEP(2);
-    }
-#undef QW3_TILE_STEP
-
-    // the exponents of the lane's 16 tokens, loaded together (past M: the last)
-    int xt[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int tok = m0 + wm * 64 + 16 * i + 4 * lc + r;
-            xt[i][r] = xe[tok < M ? tok : M - 1];
-        }
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-        const int nl = wn * 64 + 16 * jj + lr;
-        const int64_t row = n0 + nl;
-        const int en = En[nl];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int tok = m0 + wm * 64 + 16 * i + 4 * lc + r;
-                if (tok < M && row < N) y[(int64_t)tok * N + row] = ldexpf(acc[i][jj][r], en + xt[i][r]);
-            }
-        }
-    }
-    if (fix) {  // workgroup-uniform, rare
-        __syncthreads();  // orders the stores above before the fixup's
-        fixup_tile_call(x + (int64_t)m0 * K, K, M - m0 < kTileBM ? M - m0 : kTileBM, packed, scales, G, 0, G,
-                        BlockRows{n_tile, NT, kTileBN, N}, xd + (int64_t)m0 * G, nz, y + (int64_t)m0 * N, N);
-    }
-}
-#undef QW3_TILE_LOAD
-#undef QW3_TILE_STORE
-#undef QW3_RING
 
 // ------------------------------------------ prefill, 256 x 256 output tiles --
 // Larger tiles for the MFMA-bound case.  Eight waves, two per SIMD, each
@@ -1698,32 +1522,6 @@ TileX tile_x_at(void *base, const size_t (&at)[4]) {
                  reinterpret_cast<float *>(b + at[2]), reinterpret_cast<float *>(b + at[3])};
 }
 
-// 33..128 tokens when the ring kernel does not apply (scale rows not 8-byte
-// aligned, or K / 128 not a multiple of 32): convert x once (per-token
-// exponent), then one tile GEMM launch.
-qw3_status launch_gemm_tile(const uint16_t *x, const uint32_t *packed, const uint16_t *scales, float *y,
-                            int64_t M, int64_t N, int64_t K, const ScratchSrc &src) {
-    const int G = (int)(K / kGroup);
-    const int MT = (int)ceil_div(M, kTileBM);
-    const int64_t Mp = (int64_t)MT * kTileBM;
-    Carve cv;
-    size_t at[4];
-    void *base = nullptr;
-    qw3_status st = src.get(tile_x_layout(Mp, K, cv, at), &base);
-    if (st != QW3_OK) return st;
-    const TileX tx = tile_x_at(base, at);
-    hipLaunchKernelGGL(prep_tile_x_kernel, dim3((unsigned)Mp), dim3(256), 0, src.stream, x, tx.xq, tx.xe, tx.xd,
-                       tx.dtot, (int)M, K);
-    st = check_launch();
-    if (st == QW3_OK) {
-        const int64_t blocks = ceil_div(N, kTileBN) * MT;
-        hipLaunchKernelGGL(qgemm_tile_kernel, dim3((unsigned)blocks), dim3(256), kTileLds, src.stream, tx.xq, tx.xe,
-                           tx.xd, tx.dtot, x, packed, scales, y, (int)M, MT, N, G);
-        st = check_launch();
-    }
-    return st;
-}
-
 // Prefill on 256 x 256 tiles: convert x once (per-token exponent), one tile
 // launch (K split into C chunks when the tiles alone would not fill the
 // GPU), and a chunk sum.
@@ -1897,24 +1695,18 @@ qw3_status launch_gemm_small(const uint16_t *x, const uint32_t *packed, const ui
                              int64_t M, int64_t N, int64_t K, const ScratchSrc &src) {
     const int G = (int)(K / kGroup);
     const int w = slice_waves(G);
-    if (M > 32) {
-        if (M >= kPfMinM) return launch_gemm_pf(x, packed, scales, y, M, N, K, src);
-        // 33..128 tokens: passes of 32 through the ring kernel (weights read
-        // once per pass) when it applies -- gate_proj M = 64 in 66 us, down_proj
-        // 68, q_proj 37, against 140, 458 and 139 on the 128-token tiles --
-        // else passes of 16 when K / 1024 is whole.
-        if (aligned(scales, 8) && G % 32 == 0) return launch_gemm_mt<8, 2>(x, packed, scales, y, M, N, K, src);
-        if (w > 0)
-            return with_waves(w, [&](auto wc) { return launch_gemm_mt<decltype(wc)::value, 1>(x, packed, scales, y, M, N, K, src); });
-        return launch_gemm_tile(x, packed, scales, y, M, N, K, src);
-    }
-    // Batched decode.  With 8-byte aligned scale rows: up to 4 and up to 8
-    // tokens in the batch-1 layout, converting the activations in the kernel
-    // (8 tokens: about 1 us faster than the ring kernel with its conversion
-    // launch on both MLP shapes); 17..32 tokens in one pass of the ring kernel
-    // (chunks of 8 waves x 4 groups).  Otherwise passes of up to 16 tokens in
-    // chunks of w waves x 8 groups (slice_waves: 8 at K = 8192, 7 at 28672).
-    // The 4- and 8-token kernels and the 16-token passes need K / 1024 whole.
+    if (M >= kPfMinM) return launch_gemm_pf(x, packed, scales, y, M, N, K, src);
+    // Batched decode, and 33..128 tokens in passes over the weights (against
+    // one 128-token tile GEMM, since removed: gate_proj M = 64 66 us against
+    // 140, down_proj 68 against 458, q_proj 37 against 139).  With 8-byte aligned scale rows:
+    // up to 4 and up to 8 tokens in the batch-1 layout, converting the
+    // activations in the kernel (8 tokens: about 1 us faster than the ring
+    // kernel with its conversion launch on both MLP shapes); 17 and more
+    // tokens in passes of 32 through the ring kernel (chunks of 8 waves x 4
+    // groups).  Otherwise passes of up to 16 tokens in chunks of w waves x 8
+    // groups (slice_waves: 8 at K = 8192, 7 at 28672).  The 4- and 8-token
+    // kernels and the 16-token passes need K / 1024 whole; other K take
+    // qgemm_mfma_kernel in passes of 16 or 32.
     if (w > 0 && M <= 8 && aligned(scales, 8)) {
         if (M <= 4)
             return with_waves(w, [&](auto wc) { return launch_gemm_m4<decltype(wc)::value, 4>(x, packed, scales, y, M, N, K, src); });
@@ -1942,12 +1734,12 @@ qw3_status launch_gemm_small(const uint16_t *x, const uint32_t *packed, const ui
                            x + m0 * K, xq, xe, xd, mc, mchunk, K, G);
         st = check_launch();
         if (st != QW3_OK) break;
-        const unsigned blocks = (unsigned)ceil_div(N, 64);
+        const unsigned blocks = (unsigned)ceil_div(N, 16);
         if (mchunk == 16)
-            hipLaunchKernelGGL(qgemm_mfma_kernel<1>, dim3(blocks), dim3(256), 0, src.stream, xq, xe, xd, x + m0 * K,
+            hipLaunchKernelGGL(qgemm_mfma_kernel<1>, dim3(blocks), dim3(512), 0, src.stream, xq, xe, xd, x + m0 * K,
                                packed, scales, y + m0 * N, mc, mchunk, N, G, N);
         else
-            hipLaunchKernelGGL(qgemm_mfma_kernel<2>, dim3(blocks), dim3(256), 0, src.stream, xq, xe, xd, x + m0 * K,
+            hipLaunchKernelGGL(qgemm_mfma_kernel<2>, dim3(blocks), dim3(512), 0, src.stream, xq, xe, xd, x + m0 * K,
                                packed, scales, y + m0 * N, mc, mchunk, N, G, N);
         st = check_launch();
     }

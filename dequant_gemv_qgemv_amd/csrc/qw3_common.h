@@ -28,7 +28,7 @@
 //
 // Activations.  x is bf16; the products use fp16 operands, so each exponent
 // set (a group of 128 activations at batch 1, an 8-group slice of a token in
-// batched decode, a whole token in the tile kernels) is scaled by a power of
+// batched decode, a whole token in the prefill kernel) is scaled by a power of
 // two 2^-e that brings its largest magnitude into [2^14, 2^15), each element
 // by its slot's 2^-p (p <= 7), and rounded to fp16.  bf16 has 8 significant
 // bits and fp16 11, so every element of magnitude at least 2^(e-7) lands in
@@ -43,7 +43,7 @@
 // pass after the fast loop (fixup_outputs) evaluates that bound for every
 // output the workgroup wrote and recomputes in fp32 the ones above 2^-21, so
 // each output meets |y - y_exact| <= 1e-4 sum_k |w_k x_k| + 1e-6 whatever the
-// spread of x.  The tile kernels also fold the group scale into the fp16
+// spread of x.  The prefill kernel also folds the group scale into the fp16
 // weight, exact while every scale of the row lies within 2^21 of its largest;
 // other rows are recomputed by the same pass.  The fast loops are unchanged:
 // the pass costs nothing when every D is zero and every row folds exactly.

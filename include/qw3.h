@@ -156,7 +156,7 @@ qw3_status qgemv_w3g128_multi(const uint16_t *x, int32_t count, const int32_t *c
  * Workspace.  The call uses device scratch owned by the library, one buffer
  * per (device, stream handle): the
  * activations converted to fp16 (2 bytes per element, M rounded up to 16 or
- * 32 per pass, or to whole 128- or 256-token tiles), per-group error masses
+ * 32 per pass, or to whole 256-token tiles), per-group error masses
  * (4 bytes per token and group) and, when K is split across workgroups, fp32
  * partial sums (4 bytes per output element and K chunk).  Exceptions: M == 1
  * uses none; 2 <= M <= 8 with 8-byte aligned scale rows and K / 128 a
@@ -222,7 +222,7 @@ qw3_status qgemm_w3g128_batch_invariant(const uint16_t *x, const int32_t *packed
  *   ends; the call itself never allocates, frees or synchronizes.  A call
  *   that needs more scratch returns QW3_ERR_SCRATCH and enqueues nothing.
  *   Needs, in bytes (Mp = M rounded up to 16 or 32 per batched pass, or to
- *   whole 128- or 256-token tiles; G = K / 128; C = K chunks):
+ *   whole 256-token tiles; G = K / 128; C = K chunks):
  *     batched decode  2 Mp K + 5 G Mp + 4 C Mp N   (about 9 MiB for 32 tokens
  *                     against either MLP matrix of a 70B layer);
  *     prefill         2 Mp K + 4 Mp (G + 2) + 4 C M N  (about 97 MiB for 512

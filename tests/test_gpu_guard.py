@@ -5,7 +5,7 @@ Each case is compared with the oracle, element by element, within
 fixes), through the C ABI, on every dispatch path: batch 1 (lane-per-group,
 long-row and matrix-core kernels), up to four tokens, the in-kernel and
 launched activation conversions of batched decode, 2-byte and 8-byte aligned
-scale rows, K split into chunks, the 128-token tiles and the 256-token
+scale rows, K split into chunks, K / 128 not a multiple of 8, and the 256-token
 prefill tiles.
 
 Two adversarial families (seeded):
@@ -142,6 +142,14 @@ def test_guard_slice_waves(kind, m, n, k):
     run_and_check(kind, m, n, k, 800 + m + k)
 
 
+# K / 128 not a multiple of 8 (86 and 5 groups)
+@pytest.mark.parametrize("kind", ["x", "s"])
+@pytest.mark.parametrize("m", [4, 20])
+@pytest.mark.parametrize("n,k", [(40, 11008), (33, 640)])
+def test_guard_any_k(kind, m, n, k):
+    run_and_check(kind, m, n, k, 900 + m + k)
+
+
 # 2-byte aligned scale rows (the 16-token pass reading two bytes at a time)
 # and 8-byte aligned but not 16 (the ring and four-token kernels)
 @pytest.mark.parametrize("m", [3, 8, 24])
@@ -151,7 +159,8 @@ def test_guard_scale_views(m, off):
 
 
 # 33..128 tokens in passes of 32 (K / 128 a multiple of 32) and on the
-# 128-token tiles (K / 128 = 8 or 24), 256-token prefill tiles (K split)
+# 33..128 tokens in passes of 32 or 16 (K / 128 = 64, 32, 8, 24), 256-token
+# prefill tiles (K split)
 @pytest.mark.parametrize("kind", ["x", "s"])
 @pytest.mark.parametrize("m,n,k", [(33, 64, 8192), (100, 130, 4096), (48, 96, 1024), (100, 130, 3072),
                                    (129, 72, 4096), (512, 64, 2048), (300, 260, 1024)])

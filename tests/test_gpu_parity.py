@@ -486,6 +486,21 @@ def test_qgemm_many_tiles_per_cu(m, n, k, off):
     assert_close(y, yr, a, "qgemm many tiles M=%d %dx%d" % (m, n, k))
 
 
+@pytest.mark.parametrize("m", [2, 7, 16, 17, 32])
+@pytest.mark.parametrize("n,k", [(2048, 11008), (45, 384), (300, 640), (37, 2944)])
+def test_qgemm_any_k(m, n, k):
+    """K / 128 not a multiple of 8 (SmolLM3-3B's down_proj K = 11008 is 86
+    groups): the workgroup-per-tile kernel with 8 waves over the groups, fewer
+    groups than waves included (K = 384, 640), every output."""
+    say("qgemm any K", m, n, k)
+    c = synth.codes_all8(5200 + n + k, n, k)
+    s = synth.scales(5201 + k, n, k // 128, sigma=0.02, eps=1e-3)
+    x = synth.activations(5202 + m, m, k)
+    y = host(q().qgemm_w3g128_smallM(dev(x), gpu_pack(c), dev(s)))
+    yr, a = oracle.gemm(x, oracle.pack(c), s, k)
+    assert_close(y, yr, a, "qgemm any K M=%d %dx%d" % (m, n, k))
+
+
 @pytest.mark.parametrize("m", [3, 8, 16, 40])
 @pytest.mark.parametrize("n,k", [(50, 2048), (40, 3072), (300, 4096), (36, 5120), (64, 6144), (20, 53248)])
 def test_qgemm_slice_waves(m, n, k):
