@@ -159,10 +159,11 @@ qw3_status qgemv_w3g128_multi(const uint16_t *x, int32_t count, const int32_t *c
  * 32 per pass, or to whole 256-token tiles), per-group error masses
  * (4 bytes per token and group) and, when K is split across workgroups, fp32
  * partial sums (4 bytes per output element and K chunk).  Exceptions: M == 1
- * uses none; 2 <= M <= 8 with 8-byte aligned scale rows and K / 128 a
- * multiple of 64 or 56 converts the activations inside the kernel and uses
- * only the partial sums, and only when K is split (K / 128 above 64 or 56,
- * e.g. K = 28672).
+ * uses none; 2 <= M <= 8 with 8-byte aligned scale rows and K a multiple of
+ * 1024 converts the activations inside the kernel and uses only the partial
+ * sums, and only when K is split: into K / (1024 w) chunks, w the largest of
+ * 1..8 dividing K / 1024 (K = 8192 or 4096: one chunk, no workspace;
+ * K = 28672: w = 7, four chunks).
  *   - The first call on a stream allocates its buffer (hipMalloc).  A later
  *     call that needs more allocates a buffer at least twice as large; the
  *     superseded one is never freed or reused while the process runs, so work
