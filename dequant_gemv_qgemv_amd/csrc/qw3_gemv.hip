@@ -733,15 +733,16 @@ qw3_status launch_gemv_mfma(const uint16_t *x, GemvSegs sg, int count, hipStream
     return check_launch();
 }
 
-// Whether the matrix-core GEMV takes a matrix: K = 8192, scale rows 8-byte
-// aligned (8-byte scale loads) and at least four 16-row tiles per CU (with
-// fewer it is no faster than the lane-per-group kernel).  At K = 28672
+// Whether the matrix-core GEMV takes a matrix: K = 8192 (4 waves x 16 groups)
+// or 16384 (4 waves x 32 groups), scale rows 8-byte aligned (8-byte scale
+// loads) and at least four 16-row tiles per CU (with fewer it is no faster
+// than the lane-per-group kernel).  At K = 28672
 // (7 waves x 32 groups) it measured no faster than qgemv_big_kernel on the
 // 8192-row down projection, two tiles per CU, so it is not used there.  The
 // choice depends on the matrix alone, so a matrix gets the same kernel -- and
 // the same bits -- from qgemv_w3g128 and from qgemv_w3g128_multi.
 bool gemv_mfma_takes(int G, const uint16_t *scales, int64_t N) {
-    if (G != 64 || N == 0 || !aligned(scales, 8)) return false;
+    if ((G != 64 && G != 128) || N == 0 || !aligned(scales, 8)) return false;
     int cus = 0;
     if (cu_count(&cus) != QW3_OK) return false;
     return ceil_div(N, 16) >= 4 * (int64_t)cus;
@@ -754,13 +755,21 @@ bool gemv_mfma_takes(int G, const uint16_t *scales, int64_t N) {
 qw3_status qw3_shared::launch_gemv(const uint16_t *x, const uint32_t *packed, const uint16_t *scales, float *y,
                                    int64_t N, int64_t K, hipStream_t stream, int M) {
     const int G = (int)(K / kGroup);
+    if (gemv_mfma_takes(G, scales, N)) {
+        GemvSegs sg = {};
+        sg.packed[0] = packed;
+        sg.scales[0] = scales;
+        sg.y[0] = y;
+        sg.rows[0] = N;
+        return G == 64 ? launch_gemv_mfma<16, 4, false>(x, sg, 1, stream, M)
+                       : launch_gemv_mfma<32, 4, false>(x, sg, 1, stream, M);
+    }
     if (G <= 64) {
         GemvSegs sg = {};
         sg.packed[0] = packed;
         sg.scales[0] = scales;
         sg.y[0] = y;
         sg.rows[0] = N;
-        if (gemv_mfma_takes(G, scales, N)) return launch_gemv_mfma<16, 4, false>(x, sg, 1, stream, M);
         return launch_gemv_small_any<false>(x, sg, 1, G, stream, M);
     }
     return launch_gemv_big(x, packed, scales, y, N, G, stream, M);

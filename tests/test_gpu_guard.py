@@ -112,7 +112,8 @@ def run_and_check(kind, m, n, k, seed, scale_offset=0):
 # batch 1: lane-per-group (K <= 8192), long rows through LDS (K = 28672) and
 # per lane (K = 65536), and the matrix-core kernel (N >= 16384 at K = 8192)
 @pytest.mark.parametrize("kind", ["x", "s"])
-@pytest.mark.parametrize("n,k", [(300, 1024), (200, 8192), (96, 28672), (24, 65536), (16400, 8192)])
+@pytest.mark.parametrize("n,k", [(300, 1024), (200, 8192), (96, 28672), (24, 65536), (16400, 8192),
+                                 (16400, 16384)])
 def test_guard_batch1(kind, n, k):
     run_and_check(kind, 1, n, k, 100 + k + n)
 

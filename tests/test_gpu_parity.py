@@ -254,8 +254,10 @@ def test_binding_rejects_misaligned_view():
 MF_K = 8192
 
 
-# (the K = 28672 cases check the lane-per-group kernel at the same sizes)
-@pytest.mark.parametrize("n,k", [(16411, MF_K), (17000, MF_K), (8200, 28672), (8213, 28672)])
+# (K = 16384: 32 groups per wave; the K = 28672 cases check the lane-per-group
+# kernel at the same sizes; 16300 rows at K = 16384 stay below four tiles per CU)
+@pytest.mark.parametrize("n,k", [(16411, MF_K), (17000, MF_K), (16400, 16384), (16300, 16384), (8200, 28672),
+                                 (8213, 28672)])
 def test_qgemv_mfma_parity_all_codes(n, k):
     say("qgemv matrix cores", n, k)
     c = synth.codes_all8(7000 + n, n, k)
@@ -363,7 +365,7 @@ def test_qgemv_multi_matches_single(k, ns):
 # ----------------------------------------------- batch-invariant product --
 
 @pytest.mark.parametrize("m,n,k", [(1, 37, 256), (5, 300, 1024), (3, 130, 8192), (4, 16400, 8192),
-                                   (7, 200, 28672), (2, 9, 131072)])
+                                   (2, 16400, 16384), (7, 200, 28672), (2, 9, 131072)])
 def test_batch_invariant_rows_equal_gemv(m, n, k):
     """Every row of qgemm_w3g128_batch_invariant equals qgemv_w3g128 on that
     activation row bit for bit (the lane-per-group, matrix-core and long-row
